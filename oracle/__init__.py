@@ -1,0 +1,40 @@
+"""CPU oracle for paged decode attention and the paged KV cache operations.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the test suite, the smoke check
+in ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py``
+may import or run anything in this package.  The library under
+``paged_kv_cache_116_amd/`` never imports it, and this package imports nothing
+from the library: the two share no code, tables or helpers.
+
+Everything here is plain, slow and written to be checked by eye against the
+pages that define the method.  Floating point work is done in float64
+(widening float32 / bfloat16 / float16 inputs to float64 is exact).  Integer
+and byte work (block-table resolution, cache append, block copy, the block
+manager) is exact by construction.
+
+Sources, cited in the modules by tag and section:
+
+  [pofe]    "PagedAttention: paging the KV cache" (pofe.ai)
+  [lesson]  "PagedAttention" lesson in "How Text Is Generated"
+            (learn.pranaymahendrakar.com)
+  [note]    "PagedAttention: Manage the Cache Without Moving the Sequence"
+            (neelmishra.github.io)
+  [claims]  "Paged Attention" (firehose-demo claims page)
+  [arch]    "PagedAttention: Virtual-Memory KV Cache Management, Continuous
+            Batching, and PyTorch Architecture" (ailinkdeeptech.com)
+
+Modules:
+  paging        block-table resolution, explicit gather, slot accounting
+  attention     decode attention by explicit gather + two-pass softmax,
+                the block-wise online-softmax recurrence and the
+                log-sum-exp merge of partition states
+  cache_ops     cache append and block copy on pool copies
+  block_manager free list, reference counts, fork and copy-on-write
+  allocator_toy contiguous-reservation vs paged accounting of a toy workload
+
+Every function in this package is pinned by a ``-m "not gpu"`` test against
+values printed on the pages, closed forms, brute force or an independent
+library routine; none is "parity unpinned".
+"""
+
+from . import paging, attention, cache_ops, block_manager, allocator_toy  # noqa: F401

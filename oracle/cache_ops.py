@@ -1,0 +1,61 @@
+"""Cache append and block copy on copies of the pools (oracle).
+
+Test infrastructure only; see the package docstring for who may use it.
+Both operations are byte moves, so the result is exact and a GPU result must
+match it bit for bit.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .paging import resolve
+
+
+def append_token(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
+                 v_new: np.ndarray, tables: np.ndarray, lens_pre, block_size: int):
+    """Write each sequence's new token into its slot; return new pools.
+
+    [pofe] "How it works", decode step: the new token's k and v go to slot
+    len mod b of the last table entry, where len is the length before the
+    append ([pofe] "Minimal implementation", ``Sequence.append`` writes at
+    ``self.len % b`` and then increments ``len``).  Resolving position len
+    through the table names that same block (floor(len / b) is the last
+    entry once the host has allocated it).  A negative length marks a padding
+    row that writes nothing.  Every other byte of the pools is unchanged.
+
+    k_new, v_new: [S, H_kv, D]; pools: [N, B, H_kv, D]; lens_pre: [S].
+    """
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    num_blocks = k_pool.shape[0]
+    for s, length in enumerate(lens_pre):
+        length = int(length)
+        if length < 0:
+            continue
+        physical, offset = resolve(tables[s], block_size, length)
+        if not (0 <= physical < num_blocks):
+            raise IndexError(f"sequence {s}: block id {physical} outside the pool")
+        k_out[physical, offset] = k_new[s]
+        v_out[physical, offset] = v_new[s]
+    return k_out, v_out
+
+
+def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, src, dst):
+    """Copy whole blocks (all B slots, all heads) src[i] -> dst[i]; return new pools.
+
+    The copy-on-write step of [arch] 4. ("copy the B tokens from the shared
+    block to the new block") and [pofe] "Minimal implementation"
+    (``p.k[:, new] = p.k[:, old]``).  The destinations must be distinct and
+    must not also be sources, so the order of the copies does not matter.
+    """
+    src = [int(x) for x in src]
+    dst = [int(x) for x in dst]
+    if len(set(dst)) != len(dst) or set(dst) & set(src):
+        raise ValueError("destinations must be distinct and disjoint from sources")
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    for a, b in zip(src, dst):
+        k_out[b] = k_pool[a]
+        v_out[b] = v_pool[a]
+    return k_out, v_out

@@ -1,0 +1,227 @@
+"""Seeded synthetic decode workloads shared by the tests, the smoke check and
+the benchmark.
+
+This module only draws inputs: sequence lengths, block tables built from a
+shuffled list of physical ids, query / new-token / cache values, and NaN
+poison in every pool slot that holds no token.  It holds none of the
+attention or append arithmetic; both the oracle and the GPU library read the
+arrays it produces.
+
+Shapes follow the per-layer head shapes the pages use: a 13B-class model
+(40 heads of 128) from [pofe] "The problem: reservation and fragmentation"
+(OPT-13B), a 70B-class GQA model (8 KV heads of 128) from [arch] "KV Cache
+Memory Bottlenecks", and the 32 query / 8 KV heads of 128 of the [arch]
+"Production PyTorch Implementation" driver.  The pages measured on request
+traces that are not available here; these seeded draws stand in for them.
+
+Conventions
+-----------
+``lens[s]`` is the attention length L_s *after* the decode step's append.
+The pool holds positions 0 .. L_s-2 of every sequence; position L_s-1 is the
+token the step appends (from ``k_new`` / ``v_new``).  The table of sequence s
+already lists ceil(L_s / B) blocks (the host has allocated the slot), and the
+remaining entries are -1.  Every slot that holds no token before the append
+(unallocated blocks, the tail of each sequence's last block, including the
+append slot) is NaN when ``poison`` is set, so any read of it shows up in the
+result.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+CONFIG_NAMES = {
+    1: "tiny_fp32",
+    2: "mha13b_bf16",
+    3: "gqa70b_bf16",
+    4: "shared_prefix_gqa_fp16",
+    5: "long_context_gqa_bf16",
+}
+
+
+@dataclass
+class Workload:
+    name: str
+    dtype: str
+    block_size: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_blocks: int
+    lens: np.ndarray                 # int32 [S], attention length after append
+    tables: np.ndarray               # int32 [S, max_blocks], -1 padded
+    q: torch.Tensor                  # [S, H_q, D]
+    k_new: torch.Tensor              # [S, H_kv, D]
+    v_new: torch.Tensor
+    k_pool: torch.Tensor             # [N, B, H_kv, D], positions 0..L-2 filled
+    v_pool: torch.Tensor
+    partition_tokens: int = 512
+    shared_blocks: list = field(default_factory=list)
+    seed: int = 0
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.lens.shape[0])
+
+    @property
+    def lens_pre(self) -> np.ndarray:
+        return (self.lens - 1).astype(np.int32)
+
+    @property
+    def max_blocks(self) -> int:
+        return int(self.tables.shape[1])
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return DTYPES[self.dtype]
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def default_seed(config_id: int) -> int:
+    return 1000 + config_id
+
+
+def _draw_lengths(config_id: int, rng: np.random.Generator, batch: int, len_range):
+    lo, hi = len_range
+    if config_id == 1:
+        return np.array([10, 5, 13], dtype=np.int64)
+    if config_id in (2, 5):
+        return rng.integers(lo, hi + 1, size=batch)
+    if config_id == 3:
+        return np.rint(np.exp(rng.uniform(math.log(lo), math.log(hi), size=batch))).astype(np.int64)
+    raise ValueError(config_id)
+
+
+SPECS = {
+    # id: dtype, B, H_q, H_kv, D, batch, length range
+    1: ("f32", 4, 2, 1, 16, 3, (10, 13)),
+    2: ("bf16", 16, 40, 40, 128, 64, (64, 2048)),
+    3: ("bf16", 16, 64, 8, 128, 256, (512, 8192)),
+    4: ("f16", 16, 32, 8, 128, 128, (1, 512)),       # suffix range; prefix 1024
+    5: ("bf16", 16, 64, 8, 128, 8, (8192, 32768)),
+}
+
+
+def make_workload(config_id: int, seed: int | None = None, *, batch: int | None = None,
+                  len_range=None, block_size: int | None = None, prefix_tokens: int = 1024,
+                  device="cpu", poison: bool = True, dtype: str | None = None,
+                  num_q_heads: int | None = None, num_kv_heads: int | None = None,
+                  head_dim: int | None = None) -> Workload:
+    """Draw config ``config_id`` (1-5).  Keyword overrides shrink a config for
+    tests while keeping its structure (length law, sharing, shuffled ids)."""
+    if seed is None:
+        seed = default_seed(config_id)
+    spec_dtype, spec_b, spec_hq, spec_hkv, spec_d, spec_batch, spec_range = SPECS[config_id]
+    dtype = dtype or spec_dtype
+    B = block_size or spec_b
+    Hq = num_q_heads or spec_hq
+    Hkv = num_kv_heads or spec_hkv
+    D = head_dim or spec_d
+    full_size = batch is None and len_range is None
+    batch = batch or spec_batch
+    len_range = len_range or spec_range
+    rng = np.random.default_rng(seed)
+
+    shared: list[int] = []
+    if config_id == 4:
+        suffix = rng.integers(len_range[0], len_range[1] + 1, size=batch)
+        lens = prefix_tokens + suffix
+        prefix_blocks = -(-prefix_tokens // B)
+        if prefix_tokens % B != 0:
+            raise ValueError("the shared prefix must fill whole blocks")
+        private = [-(-int(L) // B) - prefix_blocks for L in lens]
+        needed = prefix_blocks + sum(private)
+        num_blocks = int(math.ceil(1.1 * needed)) + 128
+    else:
+        lens = _draw_lengths(config_id, rng, batch, len_range)
+        nb = [-(-int(L) // B) for L in lens]
+        if config_id == 1:
+            num_blocks = 16
+        elif config_id == 2 and full_size and B == 16:
+            num_blocks = 16384
+        else:
+            num_blocks = int(math.ceil(1.1 * sum(nb))) + 1
+
+    perm = rng.permutation(num_blocks)
+    nbs = [-(-int(L) // B) for L in lens]
+    max_blocks = max(nbs)
+    if config_id == 4 and full_size:
+        max_blocks = 96
+    elif config_id == 2 and full_size:
+        max_blocks = 128
+    elif config_id == 3 and full_size:
+        max_blocks = 512
+    elif config_id == 5 and full_size:
+        max_blocks = 32768 // B
+    elif config_id == 1:
+        max_blocks = 4
+    tables = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    pos = 0
+    if config_id == 4:
+        shared = [int(x) for x in perm[:prefix_blocks]]
+        pos = prefix_blocks
+        for s, n in enumerate(nbs):
+            tables[s, :prefix_blocks] = shared
+            k = n - prefix_blocks
+            tables[s, prefix_blocks:n] = perm[pos:pos + k]
+            pos += k
+    else:
+        for s, n in enumerate(nbs):
+            tables[s, :n] = perm[pos:pos + n]
+            pos += n
+    used_ids = perm[:pos]
+    unused_ids = perm[pos:]
+
+    tdtype = DTYPES[dtype]
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    S = len(lens)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(tdtype)
+
+    q = randn(S, Hq, D)
+    k_new = randn(S, Hkv, D)
+    v_new = randn(S, Hkv, D)
+    k_pool = randn(num_blocks, B, Hkv, D)
+    v_pool = randn(num_blocks, B, Hkv, D)
+    if poison:
+        nan = float("nan")
+        if len(unused_ids):
+            idx = torch.as_tensor(unused_ids, device=dev, dtype=torch.long)
+            k_pool[idx] = nan
+            v_pool[idx] = nan
+        # The tail of each sequence's last block, from the append slot on,
+        # holds no token yet.
+        blk_idx, off_idx = [], []
+        for s, (L, n) in enumerate(zip(lens, nbs)):
+            last = int(tables[s, n - 1])
+            first_empty = int(L) - 1 - (n - 1) * B
+            for o in range(first_empty, B):
+                blk_idx.append(last)
+                off_idx.append(o)
+        if blk_idx:
+            bi = torch.as_tensor(blk_idx, device=dev, dtype=torch.long)
+            oi = torch.as_tensor(off_idx, device=dev, dtype=torch.long)
+            k_pool[bi, oi] = nan
+            v_pool[bi, oi] = nan
+    del used_ids
+    return Workload(name=CONFIG_NAMES[config_id], dtype=dtype, block_size=B,
+                    num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, num_blocks=num_blocks,
+                    lens=lens.astype(np.int32), tables=tables, q=q, k_new=k_new, v_new=v_new,
+                    k_pool=k_pool, v_pool=v_pool, shared_blocks=shared, seed=seed)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of a float32 / float16 / bfloat16 tensor to numpy float64."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
