@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+A step is one pass of the whole decode hot path over one batch: the cache
+append of one new token per sequence (paged_kv_append), the per-partition
+attention kernel and the log-sum-exp merge (paged_decode_attention_partitions
++ paged_decode_attention_merge).  Host slot allocation is done once before
+timing (the tables already list the slot), and the append rewrites the same
+bytes every step, so the timed steps are identical.
+
+Default workload: the 70B-shaped GQA decode batch (64 query / 8 KV heads of
+128, bf16, B = 16, 256 sequences with log-uniform lengths in [512, 8192],
+pool of 1.1x the needed blocks with shuffled ids), drawn on the GPU.
+
+Prints one JSON line.  `value` is KV GB/s over the whole step: valid key and
+value bytes of every sequence, divided by the step time.  The `roofline`
+object prices the partition kernel (the dominant one) against the 8 TB/s HBM
+peak, timed with HIP events on the stream it runs on.  `cpu_baseline` is the
+float64 CPU oracle on a sample of the same batch, single threaded.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+WORKLOAD_DESC = {
+    1: "tiny fp32: 2 q / 1 kv heads, D 16, B 4, lengths 10/5/13, pool 16 blocks",
+    2: "13B-shaped MHA bf16: 40 q = 40 kv heads, D 128, B 16, batch 64, lengths U[64,2048], pool 16384 blocks",
+    3: "70B-shaped GQA bf16: 64 q / 8 kv heads, D 128, B 16, batch 256, lengths log-uniform [512,8192], pool 1.1x needed",
+    4: "shared-prefix GQA fp16: 32 q / 8 kv heads, D 128, B 16, batch 128, 1024-token shared prefix + U[1,512] private",
+    5: "long-context GQA bf16: 64 q / 8 kv heads, D 128, batch 8, lengths U[8192,32768], 512-token partitions",
+}
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--partition-tokens", type=int, default=512)
+    ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
+    ap.add_argument("--copy-gib", type=float, default=2.0,
+                    help="size of the device-to-device copy that measures practical bandwidth")
+    return ap.parse_args(argv)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("decode_attention.hip", "pkv_common.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_116_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per partition launch from committed rocprofv3 counter runs,
+    used only while the kernel source is the one that was profiled."""
+    path = os.path.join(ROOT, "profiles", "partition_kernel_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    entry = rec.get(workload, {}).get(kernel)
+    if not entry or entry.get("source_digest") != kernel_source_digest():
+        return None
+    return entry.get("traffic_bytes")
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this library has no "
+              "multi-GPU path; run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    sys.path.insert(0, ROOT)
+    import paged_kv_cache_116_amd as pkv
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    kw = {}
+    if args.block_size:
+        kw["block_size"] = args.block_size
+    t0 = time.time()
+    w = workloads.make_workload(args.config, device=dev, **kw)
+    torch.cuda.synchronize()
+    print(f"# workload {w.name}: {w.num_seqs} seqs, tokens={int(w.lens.sum())}, "
+          f"blocks={w.num_blocks}, drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    # Host copies for the oracle, taken before any library call touches the pools.
+    rng = np.random.default_rng(7)
+    check_seqs = sorted(set([int(np.argmax(w.lens))] +
+                            rng.choice(w.num_seqs, size=min(4, w.num_seqs), replace=False).tolist()))
+    cpu_sample = sorted(rng.choice(w.num_seqs, size=min(32, w.num_seqs), replace=False).tolist())
+    check_inputs = None if args.no_check else workloads.extract_sequences(w, check_seqs)
+    cpu_inputs = (workloads.extract_sequences(w, cpu_sample, dtype=np.float32)
+                  if args.cpu_seconds > 0 else None)
+
+    esize = w.k_pool.element_size()
+    S, Hq, Hkv, D, B = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    lens64 = w.lens.astype(np.int64)
+    kv_bytes = int(lens64.sum()) * Hkv * D * 2 * esize
+    table_bytes = int(sum(-(-int(L) // B) for L in lens64)) * 4
+    alg_bytes = kv_bytes + 2 * S * Hq * D * esize + table_bytes + S * 4
+
+    tables = torch.as_tensor(w.tables, device=dev)
+    lens = torch.as_tensor(w.lens, device=dev)
+    lens_pre = torch.as_tensor(w.lens_pre, device=dev)
+    out = torch.empty_like(w.q)
+    P = args.partition_tokens
+    ws = torch.empty(max(1, pkv.paged_decode_workspace_bytes(S, Hq, D, w.max_blocks * B, P)),
+                     dtype=torch.uint8, device=dev)
+    kernel = {"auto": pkv.PKV_ATTN_AUTO, "valu": pkv.PKV_ATTN_VALU, "mfma": pkv.PKV_ATTN_MFMA}[args.kernel]
+    stream = torch.cuda.current_stream()
+
+    def append():
+        pkv.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens_pre, stream=stream)
+
+    def partitions():
+        pkv.paged_decode_attention_partitions(kernel, out, w.q, w.k_pool, w.v_pool, tables, lens,
+                                              scale=w.scale, partition_tokens=P, workspace=ws,
+                                              stream=stream)
+
+    def merge():
+        pkv.paged_decode_attention_merge(out, w.q, w.k_pool, w.v_pool, tables, lens,
+                                         scale=w.scale, partition_tokens=P, workspace=ws,
+                                         stream=stream)
+
+    for _ in range(args.warmup):
+        append()
+        partitions()
+        merge()
+    torch.cuda.synchronize()
+    print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    start, end = ev(), ev()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for m in marks:
+        m[0].record(stream)
+        append()
+        m[1].record(stream)
+        partitions()
+        m[2].record(stream)
+        merge()
+        m[3].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    t_app = [m[0].elapsed_time(m[1]) for m in marks]
+    t_part = [m[1].elapsed_time(m[2]) for m in marks]
+    t_merge = [m[2].elapsed_time(m[3]) for m in marks]
+    part_ms = statistics.mean(t_part)
+    print(f"# timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, partition {part_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    # Practical ceiling: a large device-to-device copy, outside the timed region.
+    copy_gbps = None
+    if args.copy_gib > 0:
+        n = int(args.copy_gib * 2**30) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        for _ in range(5):
+            b.copy_(a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 5 * 2 * n * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        del a, b
+
+    parity = None
+    if check_inputs is not None:
+        from oracle import attention as o_attn
+        from oracle import cache_ops as o_cache
+        c = check_inputs
+        kp, vp = o_cache.append_token(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
+                                      c["tables"], c["lens_pre"], B)
+        ref = o_attn.decode_attention(c["q"], kp, vp, c["tables"], c["lens"], B, w.scale)
+        got = out[torch.as_tensor(check_seqs, device=dev)].double().cpu().numpy()
+        err = np.abs(got - ref)
+        if w.dtype == "f32":
+            ok = bool(err.max() <= 1e-5)
+        else:
+            ok = bool((err <= 2e-2 + 1e-2 * np.abs(ref)).all())
+        parity = {"sampled_seqs": check_seqs, "max_abs_err": float(err.max()), "ok": ok}
+        print(f"# parity on {check_seqs}: max_abs_err={err.max():.3e} ok={ok}", file=sys.stderr,
+              flush=True)
+
+    cpu = None
+    if cpu_inputs is not None:
+        import threadpoolctl
+        from oracle import attention as o_attn
+        from oracle import cache_ops as o_cache
+        c = cpu_inputs
+        sample_kv = int(c["lens"].astype(np.int64).sum()) * Hkv * D * 2 * esize
+        passes, spent = 0, 0.0
+        with threadpoolctl.threadpool_limits(1):
+            while spent < args.cpu_seconds:
+                t = time.perf_counter()
+                kp, vp = o_cache.append_token(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
+                                              c["tables"], c["lens_pre"], B)
+                o_attn.decode_attention(c["q"], kp, vp, c["tables"], c["lens"], B, w.scale)
+                spent += time.perf_counter() - t
+                passes += 1
+        cpu = {"value": passes * sample_kv / spent / 1e9, "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "seq_layer_steps_per_s": passes * len(cpu_sample) / spent,
+               "sample": f"{len(cpu_sample)} of the {S} sequences (seeded), "
+                         f"{int(c['lens'].sum())} tokens, {passes} pass(es) in {spent:.1f}s, "
+                         "append + float64 gather attention, BLAS limited to 1 thread"}
+        print(f"# cpu oracle: {cpu['value']:.4f} GB/s over {spent:.1f}s", file=sys.stderr, flush=True)
+
+    kv_gbps_step = kv_bytes / (ms_step * 1e-3) / 1e9
+    attn_ms = statistics.mean(t_part) + statistics.mean(t_merge)
+    achieved = alg_bytes / (part_ms * 1e-3) / 1e9
+    kname = {"auto": "mfma" if w.dtype != "f32" and D >= 32 else "valu"}.get(args.kernel, args.kernel)
+    traffic = measured_traffic(w.name + (f"_B{B}" if args.config == 5 else ""), kname)
+    result = {
+        "metric": "paged decode attention KV GB/s (% of HBM peak) + seq-layer steps/s",
+        "value": round(kv_gbps_step, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16"}[w.dtype],
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_DESC[args.config] + (f" (B={B})" if args.config == 5 else ""),
+                   "name": w.name, "batch": S, "block_size": B, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "tokens": int(lens64.sum()),
+                   "partition_tokens": P, "kernel": kname},
+        "pct_of_hbm_peak": round(100 * kv_gbps_step / HBM_PEAK_GBPS, 2),
+        "seq_layer_steps_per_s": round(S / (ms_step * 1e-3), 1),
+        "kv_bytes_per_step": kv_bytes,
+        "kv_gbps_attention": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 2),
+        "us": {"step": round(ms_step * 1e3, 2), "append": round(statistics.mean(t_app) * 1e3, 2),
+               "partitions": round(part_ms * 1e3, 2),
+               "partitions_p10": round(np.percentile(t_part, 10) * 1e3, 2),
+               "partitions_p90": round(np.percentile(t_part, 90) * 1e3, 2),
+               "merge": round(statistics.mean(t_merge) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": f"attn_partition_{kname}",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "copy_gbps": round(copy_gbps, 1) if copy_gbps else None,
+        "parity": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0 if (parity is None or parity["ok"]) else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

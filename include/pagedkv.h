@@ -1,0 +1,286 @@
+/*
+ * pagedkv.h - C ABI of libpagedkv, paged KV cache decode for AMD MI355X (gfx950).
+ *
+ * Sources cited below by tag and section:
+ *   [pofe]   "PagedAttention: paging the KV cache" (pofe.ai)
+ *   [lesson] "PagedAttention" lesson in "How Text Is Generated" (learn.pranaymahendrakar.com)
+ *   [note]   "PagedAttention: Manage the Cache Without Moving the Sequence" (neelmishra.github.io)
+ *   [arch]   "PagedAttention: Virtual-Memory KV Cache Management, Continuous Batching,
+ *            and PyTorch Architecture" (ailinkdeeptech.com)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every function returns an int status: PKV_OK (0) or a negative PKV_ERR_*.
+ *   No C++ exception crosses this boundary.  pkv_status_string() names a code.
+ * - Device pointers are owned by the caller and must stay valid until the work
+ *   queued on `stream` has finished.  `stream` is a hipStream_t passed as void*
+ *   (NULL = the null stream).  Device entry points only enqueue work; they do
+ *   not synchronise and they allocate no memory.
+ * - Arguments are validated on the host before anything is launched; an invalid
+ *   call launches nothing and leaves every buffer untouched.
+ * - Layouts are dense row-major.  KV pools are per layer:
+ *       k_pool, v_pool : [num_blocks, block_size, num_kv_heads, head_dim]
+ *   ([arch] "Production PyTorch Implementation", Step 2 cache tensors; one layer
+ *   of the [pofe] "Minimal implementation" pool).  Token t of a sequence lives in
+ *   physical block table[t / B] at offset t % B ([arch] "1. Paged Virtual Memory
+ *   Mapping"; [note] "Map a ten-token sequence into pages"), so its element
+ *   (head h, channel d) sits at ((block * B + t % B) * num_kv_heads + h) * head_dim + d.
+ * - block_tables : int32 [num_seqs, max_blocks_per_seq], row s lists the physical
+ *   block ids of sequence s in logical order.  Entries at or past ceil(L_s / B) are
+ *   never read and may hold anything (for example -1).
+ * - q, out : [num_seqs, num_q_heads, head_dim].  Query head h reads KV head
+ *   h / (num_q_heads / num_kv_heads) ([pofe] "Minimal implementation" repeats each
+ *   KV head over its group; [arch] Step 2 grouped-query ratio).
+ * - dtype: q, pools, new tokens and out share one element type (pkv_dtype).
+ *   Attention accumulates in fp32 and rounds the output to the element type
+ *   with round-to-nearest-even.
+ * - Supported shapes: block_size in {1, 2, 4, 8, 16, 32, 64, 128}; head_dim in
+ *   {16, 32, 64, 128, 256}.  Other shapes return PKV_ERR_UNSUPPORTED; there is no
+ *   slower fallback path.
+ * - Block ids are the caller's contract: entries a call reads must lie in
+ *   [0, num_blocks).  Kernels never touch memory outside the pools for a bad id:
+ *   append and copy skip the row, and attention writes NaN for every head of a
+ *   sequence whose table names an id outside the pool.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,   /* null pointer, negative size, H_q % H_kv != 0, ...      */
+  PKV_ERR_UNSUPPORTED = -2,   /* block size, head size or dtype outside the list above  */
+  PKV_ERR_NO_FREE_BLOCK = -3, /* host block manager: free list empty ([pofe] "Minimal
+                                 implementation" raises MemoryError for a preemption)   */
+  PKV_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required             */
+  PKV_ERR_HIP = -5            /* a HIP launch or runtime call failed                    */
+};
+
+/* Name of a status code; never NULL, static storage. */
+const char* pkv_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int pkv_version(void);
+
+/* ------------------------------------------------------------------------- */
+/* Device operations                                                         */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * paged_kv_append - write one new token per sequence into its cache slot.
+ *
+ * [pofe] "How it works", decode step: the new token's k and v go to slot
+ * len % B of the block the table lists at index len / B (the last entry, once
+ * the host has allocated it); [pofe] "Minimal implementation", Sequence.append.
+ *
+ *   k_new, v_new     : device, [num_seqs, num_kv_heads, head_dim], dtype
+ *   context_lens_pre : device int32 [num_seqs], length BEFORE the append; a
+ *                      negative value marks a padding row that writes nothing.
+ *   block_tables     : device int32 [num_seqs, max_blocks_per_seq]
+ * Writes exactly num_kv_heads*head_dim elements per sequence into each pool and
+ * nothing else (bit copy).  Two sequences must not name the same slot.
+ */
+int paged_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens_pre, int num_seqs, int num_blocks,
+                    int block_size, int num_kv_heads, int head_dim, int dtype, void* stream);
+
+/*
+ * paged_kv_copy_blocks - copy whole blocks src[i] -> dst[i] in both pools.
+ *
+ * The copy-on-write copy of [arch] "4. Automatic Prefix Caching (APC) and
+ * Copy-on-Write (CoW)" step 2 (all B token slots, all KV heads) and of [pofe]
+ * "Minimal implementation".  src, dst: device int32 [num_pairs].  The dst ids
+ * must be distinct and must not appear in src (not checked on the device: the
+ * ids live in device memory); bit copy.
+ */
+int paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src, const int32_t* dst,
+                         int num_pairs, int num_blocks, int block_size, int num_kv_heads,
+                         int head_dim, int dtype, void* stream);
+
+/*
+ * paged_kv_gather - materialise contiguous K and V histories (test / debug).
+ *
+ * k_out, v_out : device [num_seqs, max_len_out, num_kv_heads, head_dim]; row t of
+ * sequence s receives the pool row of token t for t < min(L_s, max_len_out);
+ * rows at or past that are left untouched.  Uses the same device index function
+ * as attention, so block-table resolution can be checked bit for bit against
+ * an explicit gather ([pofe] "Minimal implementation", paged_attention's gather).
+ */
+int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int num_seqs, int num_blocks, int block_size,
+                    int num_kv_heads, int head_dim, int max_len_out, int dtype, void* stream);
+
+/*
+ * paged_decode_workspace_bytes - scratch size paged_decode_attention needs.
+ *
+ * max_context_len bounds every L_s of the call (max_blocks_per_seq * block_size
+ * always does).  partition_tokens 0 selects the default of 512.  Returns 0 for
+ * invalid arguments.
+ */
+size_t paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                    int max_context_len, int partition_tokens);
+
+/*
+ * paged_decode_attention - one decode query token per sequence over its paged
+ * KV history.
+ *
+ * For each sequence s and query head h, with g = num_q_heads / num_kv_heads and
+ * L = context_lens[s] (length AFTER this step's append):
+ *     out[s,h] = sum_{t<L} softmax_t(scale * q[s,h] . K_s[t, h/g]) * V_s[t, h/g]
+ * where K_s[t] is the pool row of token t resolved through block_tables[s].
+ * This is the ordinary attention sum regrouped by block ([pofe] "How it works";
+ * [arch] "3. Non-Contiguous Online Softmax Attention Kernel": running maximum,
+ * normaliser and unnormalised accumulator per block, in fp32).  The history is
+ * cut into partitions of partition_tokens tokens (a multiple of block_size;
+ * 0 = 512) processed in parallel; their partial states are merged with the
+ * log-sum-exp rule O = sum_p e^(m_p-M) o_p / sum_p e^(m_p-M) l_p, M = max_p m_p.
+ * L = 0 yields zeros.  Slots at or past L are never read.
+ *
+ *   scale     : usually 1/sqrt(head_dim) ([arch] section 3)
+ *   workspace : device scratch of at least
+ *               paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ *                                            max_blocks_per_seq*block_size, partition_tokens)
+ *               bytes, 256-byte aligned; contents on entry do not matter.
+ */
+int paged_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int num_seqs, int num_blocks,
+                           int block_size, int num_q_heads, int num_kv_heads, int head_dim,
+                           float scale, int partition_tokens, void* workspace,
+                           size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * paged_decode_attention_with - paged_decode_attention with an explicit choice
+ * of partition kernel, for measuring one design against the other:
+ *   PKV_ATTN_AUTO  the default choice (MFMA for fp16/bf16 with head_dim >= 32,
+ *                  vector ALU otherwise);
+ *   PKV_ATTN_VALU  the vector-ALU kernel (every dtype and head size);
+ *   PKV_ATTN_MFMA  the matrix-core kernel (fp16/bf16, head_dim >= 32 only,
+ *                  else PKV_ERR_UNSUPPORTED).
+ * Results agree to fp32 rounding; other arguments as paged_decode_attention.
+ */
+enum pkv_attn_kernel { PKV_ATTN_AUTO = 0, PKV_ATTN_VALU = 1, PKV_ATTN_MFMA = 2 };
+
+int paged_decode_attention_with(int kernel, void* out, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_tables,
+                                int max_blocks_per_seq, const int32_t* context_lens,
+                                int num_seqs, int num_blocks, int block_size, int num_q_heads,
+                                int num_kv_heads, int head_dim, float scale,
+                                int partition_tokens, void* workspace, size_t workspace_bytes,
+                                int dtype, void* stream);
+
+/*
+ * paged_decode_attention_partitions / paged_decode_attention_merge - the two
+ * launches paged_decode_attention_with(kernel, ...) makes, exposed so a caller
+ * can time or schedule them separately.  Same arguments; call partitions then
+ * merge on the same stream with the same workspace.
+ *  - partitions: every (sequence, KV head, partition) workgroup runs the block
+ *    recurrence of [arch] section 3 over its tokens; a sequence with a single
+ *    partition gets its final output here, the others leave their partial
+ *    state (m, l, o) in the workspace;
+ *  - merge: for every sequence with more than one partition, combines the
+ *    partial states with O = sum_p e^(m_p-M) o_p / sum_p e^(m_p-M) l_p and
+ *    writes the output.  Does nothing when every L fits one partition.
+ */
+int paged_decode_attention_partitions(int kernel, void* out, const void* q, const void* k_pool,
+                                      const void* v_pool, const int32_t* block_tables,
+                                      int max_blocks_per_seq, const int32_t* context_lens,
+                                      int num_seqs, int num_blocks, int block_size,
+                                      int num_q_heads, int num_kv_heads, int head_dim,
+                                      float scale, int partition_tokens, void* workspace,
+                                      size_t workspace_bytes, int dtype, void* stream);
+int paged_decode_attention_merge(void* out, const void* q, const void* k_pool,
+                                 const void* v_pool, const int32_t* block_tables,
+                                 int max_blocks_per_seq, const int32_t* context_lens,
+                                 int num_seqs, int num_blocks, int block_size, int num_q_heads,
+                                 int num_kv_heads, int head_dim, float scale,
+                                 int partition_tokens, void* workspace, size_t workspace_bytes,
+                                 int dtype, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* Host block manager (CPU only; no device calls)                            */
+/* ------------------------------------------------------------------------- */
+/*
+ * Free list, reference counts and per-sequence block tables with fork and
+ * copy-on-write, as in [pofe] "Minimal implementation" (BlockPool, Sequence)
+ * and the decode-step pseudocode of [pofe] "How it works":
+ *  - the free list starts as 0..N-1 and hands out the id at its end (LIFO);
+ *  - alloc sets a block's count to 1, share adds 1, release subtracts 1 and
+ *    returns the block to the free list at 0 ([note] "Shared prefixes can share
+ *    physical storage");
+ *  - appending token `len`: if len % B == 0 a block is allocated and appended to
+ *    the table; else if the last block's count is > 1 a block is allocated, the
+ *    caller must copy old -> new (paged_kv_copy_blocks), the old block is
+ *    released and the last entry remapped ([arch] section 4, steps 1-4).
+ * Any call that returns PKV_ERR_NO_FREE_BLOCK leaves all state unchanged.
+ * A manager is not thread safe; use one per thread or lock around it.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+int pkv_bm_create(int num_blocks, int block_size, pkv_block_manager** out);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+int pkv_bm_num_free(const pkv_block_manager* bm);           /* >= 0, or error */
+int pkv_bm_refcount(const pkv_block_manager* bm, int block); /* >= 0, or error */
+int pkv_bm_alloc(pkv_block_manager* bm, int* block_out);
+int pkv_bm_share(pkv_block_manager* bm, int block);          /* block must be allocated */
+int pkv_bm_release(pkv_block_manager* bm, int block);        /* block must be allocated */
+
+/* Sequences are named by small non-negative ids the manager hands out. */
+int pkv_bm_seq_new(pkv_block_manager* bm, int* seq_out);
+/* Admission / prefill: allocate the blocks n_tokens more prompt tokens need
+ * ([pofe] "How it works", admit pseudocode).  The current last block must not
+ * be a shared partial block. */
+int pkv_bm_seq_extend(pkv_block_manager* bm, int seq, int n_tokens);
+/* Start an empty sequence on the first n_blocks full blocks of src, shared
+ * (a prefix hit: [arch] section 4). */
+int pkv_bm_seq_adopt_prefix(pkv_block_manager* bm, int seq, int src, int n_blocks);
+/* Parallel sampling: a new sequence sharing every block of parent ([pofe]
+ * "Sharing and copy-on-write"). */
+int pkv_bm_seq_fork(pkv_block_manager* bm, int parent, int* child_out);
+/* Decide the slot of the next token; *cow_src_out is the block to copy from
+ * (into *block_out) or -1 when no copy is needed.  len grows by one. */
+int pkv_bm_seq_append_slot(pkv_block_manager* bm, int seq, int* block_out, int* slot_out,
+                           int* cow_src_out);
+/* One decode step for a batch: append_slot for seqs[0..n), all or nothing
+ * (if the free list cannot cover every allocation nothing changes).
+ * block_out, slot_out: [n]; cow_src_out, cow_dst_out: [n] (first *num_cow used). */
+int pkv_bm_append_batch(pkv_block_manager* bm, const int* seqs, int n, int32_t* block_out,
+                        int32_t* slot_out, int32_t* cow_src_out, int32_t* cow_dst_out,
+                        int* num_cow_out);
+int pkv_bm_seq_free(pkv_block_manager* bm, int seq);        /* release all blocks; id retired */
+int pkv_bm_seq_len(const pkv_block_manager* bm, int seq);   /* >= 0, or error */
+int pkv_bm_seq_num_blocks(const pkv_block_manager* bm, int seq);
+/* Copy up to cap table entries of seq into out; returns the count copied. */
+int pkv_bm_seq_table(const pkv_block_manager* bm, int seq, int32_t* out, int cap);
+/* Host rows of block_tables for seqs[0..n): row i gets seqs[i]'s table padded
+ * with -1 to ld entries, lens_out[i] its length.  A table longer than ld is
+ * PKV_ERR_INVALID_ARG. */
+int pkv_bm_export_tables(const pkv_block_manager* bm, const int* seqs, int n, int32_t* out,
+                         int ld, int32_t* lens_out);
+
+/*
+ * pkv_validate_tables - host check of the block-id contract of a batch: every
+ * entry below ceil(lens[s] / block_size) lies in [0, num_blocks) and fits in the
+ * row.  Host pointers.  Returns PKV_OK, or PKV_ERR_INVALID_ARG and the first bad
+ * sequence in *bad_seq_out (may be NULL).
+ */
+int pkv_validate_tables(const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* context_lens, int num_seqs, int num_blocks,
+                        int block_size, int* bad_seq_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,373 @@
+"""Python binding of libpagedkv: paged KV cache decode for AMD MI355X (gfx950).
+
+Each function marshals torch tensors (device pointers, shapes, the current
+HIP stream) into the C ABI call of the same name declared in
+``include/pagedkv.h`` and raises :class:`PagedKVError` on a non-zero status.
+Every computation runs in the library's HIP kernels; this module does no
+arithmetic on the data and has no fallback path.  If ``libpagedkv.so`` has not
+been built (``python paged_kv_cache_116_amd/build.py``) importing the package
+fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python paged_kv_cache_116_amd/build.py` (hipcc, gfx950)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_NO_FREE_BLOCK = -3
+PKV_ERR_WORKSPACE = -4
+PKV_ERR_HIP = -5
+
+PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_ATTN_AUTO, PKV_ATTN_VALU, PKV_ATTN_MFMA = 0, 1, 2
+
+_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+_i32 = ctypes.c_int
+_p = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_intp = ctypes.POINTER(ctypes.c_int)
+
+
+def _sig(name, restype, argtypes):
+    fn = getattr(_lib, name)
+    fn.restype = restype
+    fn.argtypes = argtypes
+    return fn
+
+
+_sig("pkv_status_string", ctypes.c_char_p, [_i32])
+_sig("pkv_version", _i32, [])
+_sig("paged_kv_append", _i32, [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p])
+_sig("paged_kv_copy_blocks", _i32, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p])
+_sig("paged_kv_gather", _i32, [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+                               _i32, _p])
+_sig("paged_decode_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32])
+_ATTN_ARGS = [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
+              _i32, _p, _sz, _i32, _p]
+_sig("paged_decode_attention", _i32, _ATTN_ARGS)
+_sig("paged_decode_attention_with", _i32, [_i32] + _ATTN_ARGS)
+_sig("paged_decode_attention_partitions", _i32, [_i32] + _ATTN_ARGS)
+_sig("paged_decode_attention_merge", _i32, _ATTN_ARGS)
+_sig("pkv_validate_tables", _i32, [_p, _i32, _p, _i32, _i32, _i32, _intp])
+_sig("pkv_bm_create", _i32, [_i32, _i32, ctypes.POINTER(_p)])
+_sig("pkv_bm_destroy", None, [_p])
+_sig("pkv_bm_num_free", _i32, [_p])
+_sig("pkv_bm_refcount", _i32, [_p, _i32])
+_sig("pkv_bm_alloc", _i32, [_p, _intp])
+_sig("pkv_bm_share", _i32, [_p, _i32])
+_sig("pkv_bm_release", _i32, [_p, _i32])
+_sig("pkv_bm_seq_new", _i32, [_p, _intp])
+_sig("pkv_bm_seq_extend", _i32, [_p, _i32, _i32])
+_sig("pkv_bm_seq_adopt_prefix", _i32, [_p, _i32, _i32, _i32])
+_sig("pkv_bm_seq_fork", _i32, [_p, _i32, _intp])
+_sig("pkv_bm_seq_append_slot", _i32, [_p, _i32, _intp, _intp, _intp])
+_sig("pkv_bm_append_batch", _i32, [_p, _p, _i32, _p, _p, _p, _p, _intp])
+_sig("pkv_bm_seq_free", _i32, [_p, _i32])
+_sig("pkv_bm_seq_len", _i32, [_p, _i32])
+_sig("pkv_bm_seq_num_blocks", _i32, [_p, _i32])
+_sig("pkv_bm_seq_table", _i32, [_p, _i32, _p, _i32])
+_sig("pkv_bm_export_tables", _i32, [_p, _p, _i32, _p, _i32, _p])
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {pkv_status_string(status)} ({status})")
+
+
+class NoFreeBlockError(PagedKVError):
+    """The block manager's free list cannot cover the request."""
+
+
+def _check(status: int, where: str) -> int:
+    if status < 0:
+        if status == PKV_ERR_NO_FREE_BLOCK:
+            raise NoFreeBlockError(status, where)
+        raise PagedKVError(status, where)
+    return status
+
+
+def pkv_status_string(status: int) -> str:
+    return _lib.pkv_status_string(status).decode()
+
+
+def pkv_version() -> int:
+    return _lib.pkv_version()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+# ---------------------------------------------------------------------------
+# Device operations
+# ---------------------------------------------------------------------------
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _pool_dims(k_pool: torch.Tensor, v_pool: torch.Tensor):
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool and v_pool must both be [num_blocks, block_size, kv_heads, head_dim]")
+    if k_pool.dtype not in _DTYPE_CODE:
+        raise TypeError(f"unsupported pool dtype {k_pool.dtype}")
+    n, b, h, d = k_pool.shape
+    return n, b, h, d, _DTYPE_CODE[k_pool.dtype]
+
+
+def paged_kv_append(k_pool, v_pool, k_new, v_new, block_tables, context_lens_pre, *, stream=None):
+    """Write one new token per sequence into slot len % B of block table[len / B]."""
+    n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    s = k_new.shape[0]
+    if k_new.shape != (s, h, d) or v_new.shape != (s, h, d):
+        raise ValueError("k_new / v_new must be [num_seqs, kv_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens_pre.shape != (s,):
+        raise ValueError("block_tables [num_seqs, max_blocks] and context_lens_pre [num_seqs]")
+    _check(_lib.paged_kv_append(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new", k_pool.dtype),
+        _dev(v_new, "v_new", k_pool.dtype), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens_pre, "context_lens_pre", torch.int32), s, n, b,
+        h, d, dt, _stream(stream)), "paged_kv_append")
+
+
+def paged_kv_copy_blocks(k_pool, v_pool, src, dst, *, stream=None):
+    """Copy whole blocks src[i] -> dst[i] in both pools (copy-on-write)."""
+    n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    if src.shape != dst.shape or src.dim() != 1:
+        raise ValueError("src and dst must be 1-D of equal length")
+    _check(_lib.paged_kv_copy_blocks(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(src, "src", torch.int32),
+        _dev(dst, "dst", torch.int32), src.shape[0], n, b, h, d, dt, _stream(stream)),
+        "paged_kv_copy_blocks")
+
+
+def paged_kv_gather(k_out, v_out, k_pool, v_pool, block_tables, context_lens, *, stream=None):
+    """Materialise contiguous [num_seqs, max_len_out, kv_heads, head_dim] histories."""
+    n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    s = block_tables.shape[0]
+    if k_out.dim() != 4 or k_out.shape[0] != s or k_out.shape[2:] != (h, d) or v_out.shape != k_out.shape:
+        raise ValueError("k_out / v_out must be [num_seqs, max_len_out, kv_heads, head_dim]")
+    _check(_lib.paged_kv_gather(
+        _dev(k_out, "k_out", k_pool.dtype), _dev(v_out, "v_out", k_pool.dtype),
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), s, n, b, h, d, k_out.shape[1], dt,
+        _stream(stream)), "paged_kv_gather")
+
+
+def paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                 partition_tokens=0) -> int:
+    return int(_lib.paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                 max_context_len, partition_tokens))
+
+
+def _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partition_tokens,
+               workspace, stream):
+    n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    s, hq, dq = q.shape
+    if dq != d or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs, num_q_heads, head_dim]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
+        raise ValueError("block_tables [num_seqs, max_blocks] and context_lens [num_seqs]")
+    mb = block_tables.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        need = paged_decode_workspace_bytes(s, hq, d, mb * b, partition_tokens)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace", torch.uint8)
+    return (_dev(out, "out", k_pool.dtype), _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+            _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32), mb,
+            _dev(context_lens, "context_lens", torch.int32), s, n, b, hq, h, d, float(scale),
+            int(partition_tokens), ws_ptr, workspace.numel(), dt, _stream(stream))
+
+
+def paged_decode_attention_partitions(kernel, out, q, k_pool, v_pool, block_tables, context_lens,
+                                      *, scale=None, partition_tokens=0, workspace, stream=None):
+    """First launch of paged_decode_attention (per-partition states)."""
+    args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                      partition_tokens, workspace, stream)
+    _check(_lib.paged_decode_attention_partitions(int(kernel), *args),
+           "paged_decode_attention_partitions")
+
+
+def paged_decode_attention_merge(out, q, k_pool, v_pool, block_tables, context_lens, *,
+                                 scale=None, partition_tokens=0, workspace, stream=None):
+    """Second launch of paged_decode_attention (log-sum-exp merge)."""
+    args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                      partition_tokens, workspace, stream)
+    _check(_lib.paged_decode_attention_merge(*args), "paged_decode_attention_merge")
+
+
+def paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens, *, scale=None,
+                           partition_tokens=0, workspace=None, stream=None, kernel=None):
+    """Decode attention of q [num_seqs, H_q, D] over each sequence's paged history.
+
+    ``workspace`` is a uint8 GPU tensor of at least paged_decode_workspace_bytes(...)
+    bytes (256-byte aligned, as torch allocations are).  When it is None a
+    tensor of that size is allocated here for the call.  ``kernel`` selects
+    the partition kernel (PKV_ATTN_*) via paged_decode_attention_with.
+    """
+    args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                      partition_tokens, workspace, stream)
+    if kernel is None:
+        _check(_lib.paged_decode_attention(*args), "paged_decode_attention")
+    else:
+        _check(_lib.paged_decode_attention_with(int(kernel), *args), "paged_decode_attention_with")
+
+
+def paged_decode_attention_with(kernel, out, q, k_pool, v_pool, block_tables, context_lens, **kw):
+    paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens, kernel=kernel, **kw)
+
+
+def pkv_validate_tables(block_tables, context_lens, num_blocks: int, block_size: int):
+    """Host check of the block-id contract; returns the first bad sequence or -1."""
+    bt = torch.as_tensor(block_tables, dtype=torch.int32).contiguous()
+    ln = torch.as_tensor(context_lens, dtype=torch.int32).contiguous()
+    if bt.is_cuda or ln.is_cuda:
+        raise ValueError("pkv_validate_tables takes host arrays")
+    bad = ctypes.c_int(-1)
+    st = _lib.pkv_validate_tables(bt.data_ptr(), bt.shape[1], ln.data_ptr(), bt.shape[0],
+                                  num_blocks, block_size, ctypes.byref(bad))
+    if st == PKV_OK:
+        return -1
+    if bad.value < 0:
+        _check(st, "pkv_validate_tables")
+    return bad.value
+
+
+# ---------------------------------------------------------------------------
+# Host block manager
+# ---------------------------------------------------------------------------
+
+class BlockManager:
+    """Owner of a pkv_block_manager handle (free list, refcounts, tables)."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        h = _p()
+        _check(_lib.pkv_bm_create(num_blocks, block_size, ctypes.byref(h)), "pkv_bm_create")
+        self._h = h
+        self._destroy = _lib.pkv_bm_destroy
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def num_free(self) -> int:
+        return _check(_lib.pkv_bm_num_free(self._h), "pkv_bm_num_free")
+
+    def refcount(self, block: int) -> int:
+        return _check(_lib.pkv_bm_refcount(self._h, block), "pkv_bm_refcount")
+
+    def alloc(self) -> int:
+        out = ctypes.c_int()
+        _check(_lib.pkv_bm_alloc(self._h, ctypes.byref(out)), "pkv_bm_alloc")
+        return out.value
+
+    def share(self, block: int) -> None:
+        _check(_lib.pkv_bm_share(self._h, block), "pkv_bm_share")
+
+    def release(self, block: int) -> None:
+        _check(_lib.pkv_bm_release(self._h, block), "pkv_bm_release")
+
+    def seq_new(self) -> int:
+        out = ctypes.c_int()
+        _check(_lib.pkv_bm_seq_new(self._h, ctypes.byref(out)), "pkv_bm_seq_new")
+        return out.value
+
+    def seq_extend(self, seq: int, n_tokens: int) -> None:
+        _check(_lib.pkv_bm_seq_extend(self._h, seq, n_tokens), "pkv_bm_seq_extend")
+
+    def seq_adopt_prefix(self, seq: int, src: int, n_blocks: int) -> None:
+        _check(_lib.pkv_bm_seq_adopt_prefix(self._h, seq, src, n_blocks), "pkv_bm_seq_adopt_prefix")
+
+    def seq_fork(self, parent: int) -> int:
+        out = ctypes.c_int()
+        _check(_lib.pkv_bm_seq_fork(self._h, parent, ctypes.byref(out)), "pkv_bm_seq_fork")
+        return out.value
+
+    def seq_append_slot(self, seq: int):
+        """Returns (block, slot, cow_src) with cow_src -1 when no copy is needed."""
+        blk, slot, cow = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        _check(_lib.pkv_bm_seq_append_slot(self._h, seq, ctypes.byref(blk), ctypes.byref(slot),
+                                           ctypes.byref(cow)), "pkv_bm_seq_append_slot")
+        return blk.value, slot.value, cow.value
+
+    def append_batch(self, seqs):
+        """One decode step for many sequences, all or nothing.
+        Returns (blocks, slots, cow_src, cow_dst) as int32 CPU tensors."""
+        ids = torch.as_tensor(list(seqs), dtype=torch.int32)
+        n = ids.numel()
+        blocks = torch.empty(n, dtype=torch.int32)
+        slots = torch.empty(n, dtype=torch.int32)
+        csrc = torch.empty(n, dtype=torch.int32)
+        cdst = torch.empty(n, dtype=torch.int32)
+        ncow = ctypes.c_int()
+        _check(_lib.pkv_bm_append_batch(self._h, ids.data_ptr(), n, blocks.data_ptr(),
+                                        slots.data_ptr(), csrc.data_ptr(), cdst.data_ptr(),
+                                        ctypes.byref(ncow)), "pkv_bm_append_batch")
+        return blocks, slots, csrc[: ncow.value].clone(), cdst[: ncow.value].clone()
+
+    def seq_free(self, seq: int) -> None:
+        _check(_lib.pkv_bm_seq_free(self._h, seq), "pkv_bm_seq_free")
+
+    def seq_len(self, seq: int) -> int:
+        return _check(_lib.pkv_bm_seq_len(self._h, seq), "pkv_bm_seq_len")
+
+    def seq_num_blocks(self, seq: int) -> int:
+        return _check(_lib.pkv_bm_seq_num_blocks(self._h, seq), "pkv_bm_seq_num_blocks")
+
+    def seq_table(self, seq: int) -> list:
+        n = self.seq_num_blocks(seq)
+        buf = (ctypes.c_int32 * max(n, 1))()
+        got = _check(_lib.pkv_bm_seq_table(self._h, seq, ctypes.cast(buf, _p), n), "pkv_bm_seq_table")
+        return list(buf[:got])
+
+    def export_tables(self, seqs, ld: int):
+        """(tables int32 [n, ld] padded with -1, lens int32 [n]) on the CPU."""
+        ids = torch.as_tensor(list(seqs), dtype=torch.int32)
+        n = ids.numel()
+        out = torch.empty((n, ld), dtype=torch.int32)
+        lens = torch.empty(n, dtype=torch.int32)
+        _check(_lib.pkv_bm_export_tables(self._h, ids.data_ptr(), n, out.data_ptr(), ld,
+                                         lens.data_ptr()), "pkv_bm_export_tables")
+        return out, lens

@@ -1,0 +1,100 @@
+"""Build libpagedkv.so in-tree for gfx950 (MI355X).
+
+    python paged_kv_cache_116_amd/build.py [--jobs N]
+
+Every HIP source is compiled with hipcc for gfx950 only; the host runtime is
+plain C++ (g++).  The shared library lands next to this file, where the
+binding loads it from.  Nothing is cached: each call recompiles.
+"""
+
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
+BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
+LIB_NAME = "libpagedkv.so"
+ARCH = "gfx950"
+
+HIP_SOURCES = ["kv_cache_ops.hip", "decode_attention.hip"]
+HOST_SOURCES = ["host_runtime.cpp"]
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",
+    "-Wno-unused-function",
+    # Packed fp32 instructions stay off: hipcc would otherwise form them from
+    # scalar float code.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+]
+CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall", f"-I{INCLUDE}"]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: install ROCm (gfx950 support) to build libpagedkv")
+
+
+def _run(cmd):
+    t0 = time.time()
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    noise = "is not a recognized feature for this target"
+    out = "\n".join(l for l in proc.stdout.splitlines() if noise not in l)
+    if proc.returncode != 0:
+        raise RuntimeError(f"command failed ({proc.returncode}): {' '.join(cmd)}\n{out}")
+    return time.time() - t0, out
+
+
+def build(jobs: int | None = None, verbose: bool = False) -> str:
+    """Compile every source and link libpagedkv.so; returns the library path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    hipcc = _hipcc()
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        raise RuntimeError("no host C++ compiler (g++) found")
+    jobs = jobs or min(8, os.cpu_count() or 1)
+    cmds = []
+    objs = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        cmds.append([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD_DIR, src + ".o")
+        cmds.append([cxx, *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        objs.append(obj)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for cmd, (dt, out) in zip(cmds, ex.map(_run, cmds)):
+            if verbose:
+                print(f"[{dt:6.1f}s] {os.path.basename(cmd[-3])}", flush=True)
+            if out.strip() and verbose:
+                print(out, flush=True)
+    lib = os.path.join(HERE, LIB_NAME)
+    tmp = lib + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, lib)
+    return lib
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--jobs", type=int, default=None)
+    ap.add_argument("-q", "--quiet", action="store_true")
+    args = ap.parse_args(argv)
+    lib = build(args.jobs, verbose=not args.quiet)
+    print(lib)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,312 @@
+// host_runtime.cpp - host side of libpagedkv: status names, version, table
+// validation and the block manager (free list, reference counts, per-sequence
+// tables with fork and copy-on-write).  CPU only; no device calls.
+//
+// Sources cited by tag and section:
+//   [pofe] "PagedAttention: paging the KV cache"
+//   [note] "PagedAttention: Manage the Cache Without Moving the Sequence"
+//   [arch] "PagedAttention: Virtual-Memory KV Cache Management, Continuous
+//          Batching, and PyTorch Architecture"
+#include <stdint.h>
+
+#include <new>
+#include <vector>
+
+#include "../../include/pagedkv.h"
+
+extern "C" const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_NO_FREE_BLOCK: return "PKV_ERR_NO_FREE_BLOCK";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    default: return "PKV_ERR_UNKNOWN";
+  }
+}
+
+extern "C" int pkv_version(void) { return 100; }  // 0.1.0
+
+extern "C" int pkv_validate_tables(const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int num_seqs, int num_blocks,
+                                   int block_size, int* bad_seq_out) {
+  if (bad_seq_out) *bad_seq_out = -1;
+  if (num_seqs < 0 || max_blocks_per_seq < 1 || num_blocks < 1 || block_size < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!block_tables || !context_lens)) return PKV_ERR_INVALID_ARG;
+  for (int s = 0; s < num_seqs; ++s) {
+    const long long len = context_lens[s];
+    const long long nb = len <= 0 ? 0 : (len + block_size - 1) / block_size;
+    bool ok = nb <= max_blocks_per_seq;
+    for (long long j = 0; ok && j < nb; ++j) {
+      const int id = block_tables[(size_t)s * max_blocks_per_seq + j];
+      ok = id >= 0 && id < num_blocks;
+    }
+    if (!ok) {
+      if (bad_seq_out) *bad_seq_out = s;
+      return PKV_ERR_INVALID_ARG;
+    }
+  }
+  return PKV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Block manager.  Semantics of [pofe] "Minimal implementation" (BlockPool and
+// Sequence) and the decode-step pseudocode of [pofe] "How it works".
+// ---------------------------------------------------------------------------
+struct pkv_block_manager {
+  struct Seq {
+    std::vector<int32_t> table;
+    int len = 0;
+    bool live = false;
+  };
+  int num_blocks = 0;
+  int block_size = 0;
+  std::vector<int32_t> free_list;   // LIFO: ids handed out from the back
+  std::vector<int32_t> ref;
+  std::vector<Seq> seqs;
+
+  bool block_ok(int b) const { return b >= 0 && b < num_blocks; }
+  bool seq_ok(int s) const { return s >= 0 && s < (int)seqs.size() && seqs[s].live; }
+
+  int alloc() {   // caller has checked that the free list is not empty
+    const int i = free_list.back();
+    free_list.pop_back();
+    ref[i] = 1;
+    return i;
+  }
+  void release(int i) {
+    if (--ref[i] == 0) free_list.push_back(i);
+  }
+
+  // Blocks the next append of sequence s needs from the free list (0 or 1):
+  // one at a block boundary, one for copy-on-write of a shared partial block.
+  int append_need(const Seq& q) const {
+    if (q.len % block_size == 0) return 1;
+    return ref[q.table.back()] > 1 ? 1 : 0;
+  }
+
+  void append(Seq& q, int* block, int* slot, int* cow_src) {
+    *cow_src = -1;
+    if (q.len % block_size == 0) {
+      q.table.push_back(alloc());
+    } else if (ref[q.table.back()] > 1) {
+      // [arch] "4. Automatic Prefix Caching (APC) and Copy-on-Write (CoW)":
+      // fresh block, caller copies the B slots, old count - 1, remap.
+      const int old = q.table.back();
+      const int fresh = alloc();
+      release(old);
+      q.table.back() = fresh;
+      *cow_src = old;
+    }
+    *block = q.table.back();
+    *slot = q.len % block_size;
+    q.len += 1;
+  }
+};
+
+extern "C" int pkv_bm_create(int num_blocks, int block_size, pkv_block_manager** out) {
+  if (!out) return PKV_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (num_blocks < 1 || block_size < 1) return PKV_ERR_INVALID_ARG;
+  pkv_block_manager* bm = new (std::nothrow) pkv_block_manager();
+  if (!bm) return PKV_ERR_INVALID_ARG;
+  try {
+    bm->num_blocks = num_blocks;
+    bm->block_size = block_size;
+    bm->free_list.resize(num_blocks);
+    for (int i = 0; i < num_blocks; ++i) bm->free_list[i] = i;
+    bm->ref.assign(num_blocks, 0);
+  } catch (...) {
+    delete bm;
+    return PKV_ERR_INVALID_ARG;
+  }
+  *out = bm;
+  return PKV_OK;
+}
+
+extern "C" void pkv_bm_destroy(pkv_block_manager* bm) { delete bm; }
+
+extern "C" int pkv_bm_num_free(const pkv_block_manager* bm) {
+  if (!bm) return PKV_ERR_INVALID_ARG;
+  return (int)bm->free_list.size();
+}
+
+extern "C" int pkv_bm_refcount(const pkv_block_manager* bm, int block) {
+  if (!bm || !bm->block_ok(block)) return PKV_ERR_INVALID_ARG;
+  return bm->ref[block];
+}
+
+extern "C" int pkv_bm_alloc(pkv_block_manager* bm, int* block_out) {
+  if (!bm || !block_out) return PKV_ERR_INVALID_ARG;
+  if (bm->free_list.empty()) return PKV_ERR_NO_FREE_BLOCK;
+  *block_out = bm->alloc();
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_share(pkv_block_manager* bm, int block) {
+  if (!bm || !bm->block_ok(block) || bm->ref[block] <= 0) return PKV_ERR_INVALID_ARG;
+  bm->ref[block] += 1;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_release(pkv_block_manager* bm, int block) {
+  if (!bm || !bm->block_ok(block) || bm->ref[block] <= 0) return PKV_ERR_INVALID_ARG;
+  bm->release(block);
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_seq_new(pkv_block_manager* bm, int* seq_out) {
+  if (!bm || !seq_out) return PKV_ERR_INVALID_ARG;
+  try {
+    bm->seqs.emplace_back();
+  } catch (...) {
+    return PKV_ERR_INVALID_ARG;
+  }
+  bm->seqs.back().live = true;
+  *seq_out = (int)bm->seqs.size() - 1;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_seq_extend(pkv_block_manager* bm, int seq, int n_tokens) {
+  if (!bm || !bm->seq_ok(seq) || n_tokens < 0) return PKV_ERR_INVALID_ARG;
+  auto& q = bm->seqs[seq];
+  const int b = bm->block_size;
+  if (q.len % b != 0 && bm->ref[q.table.back()] > 1) return PKV_ERR_INVALID_ARG;
+  const long long total = (long long)q.len + n_tokens;
+  if (total > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  const long long need = (total + b - 1) / b - (long long)q.table.size();
+  if (need > (long long)bm->free_list.size()) return PKV_ERR_NO_FREE_BLOCK;
+  for (long long i = 0; i < need; ++i) q.table.push_back(bm->alloc());
+  q.len = (int)total;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_seq_adopt_prefix(pkv_block_manager* bm, int seq, int src, int n_blocks) {
+  if (!bm || !bm->seq_ok(seq) || !bm->seq_ok(src) || n_blocks < 0 || seq == src)
+    return PKV_ERR_INVALID_ARG;
+  auto& q = bm->seqs[seq];
+  const auto& from = bm->seqs[src];
+  if (!q.table.empty() || q.len != 0) return PKV_ERR_INVALID_ARG;
+  if ((long long)n_blocks * bm->block_size > from.len) return PKV_ERR_INVALID_ARG;
+  for (int j = 0; j < n_blocks; ++j) {
+    bm->ref[from.table[j]] += 1;
+    q.table.push_back(from.table[j]);
+  }
+  q.len = n_blocks * bm->block_size;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_seq_fork(pkv_block_manager* bm, int parent, int* child_out) {
+  if (!bm || !bm->seq_ok(parent) || !child_out) return PKV_ERR_INVALID_ARG;
+  int child = -1;
+  int st = pkv_bm_seq_new(bm, &child);
+  if (st != PKV_OK) return st;
+  auto& c = bm->seqs[child];
+  const auto& par = bm->seqs[parent];   // reference taken after the push_back
+  c.table = par.table;
+  c.len = par.len;
+  for (int32_t b : c.table) bm->ref[b] += 1;
+  *child_out = child;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_seq_append_slot(pkv_block_manager* bm, int seq, int* block_out,
+                                      int* slot_out, int* cow_src_out) {
+  if (!bm || !bm->seq_ok(seq) || !block_out || !slot_out || !cow_src_out)
+    return PKV_ERR_INVALID_ARG;
+  auto& q = bm->seqs[seq];
+  if (q.len == 0x7fffffff) return PKV_ERR_INVALID_ARG;
+  if (bm->append_need(q) > (int)bm->free_list.size()) return PKV_ERR_NO_FREE_BLOCK;
+  bm->append(q, block_out, slot_out, cow_src_out);
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_append_batch(pkv_block_manager* bm, const int* seqs, int n,
+                                   int32_t* block_out, int32_t* slot_out, int32_t* cow_src_out,
+                                   int32_t* cow_dst_out, int* num_cow_out) {
+  if (!bm || n < 0 || !num_cow_out) return PKV_ERR_INVALID_ARG;
+  *num_cow_out = 0;
+  if (n == 0) return PKV_OK;
+  if (!seqs || !block_out || !slot_out || !cow_src_out || !cow_dst_out) return PKV_ERR_INVALID_ARG;
+  // All or nothing: a sequence may appear once, and the free list must cover
+  // every allocation of the step before anything changes.
+  long long need = 0;
+  std::vector<char> seen;
+  try {
+    seen.assign(bm->seqs.size(), 0);
+  } catch (...) {
+    return PKV_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < n; ++i) {
+    const int s = seqs[i];
+    if (!bm->seq_ok(s) || seen[s] || bm->seqs[s].len == 0x7fffffff) return PKV_ERR_INVALID_ARG;
+    seen[s] = 1;
+    need += bm->append_need(bm->seqs[s]);
+  }
+  if (need > (long long)bm->free_list.size()) return PKV_ERR_NO_FREE_BLOCK;
+  int ncow = 0;
+  for (int i = 0; i < n; ++i) {
+    int blk, slot, cow;
+    bm->append(bm->seqs[seqs[i]], &blk, &slot, &cow);
+    block_out[i] = blk;
+    slot_out[i] = slot;
+    if (cow >= 0) {
+      cow_src_out[ncow] = cow;
+      cow_dst_out[ncow] = blk;
+      ++ncow;
+    }
+  }
+  *num_cow_out = ncow;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_seq_free(pkv_block_manager* bm, int seq) {
+  if (!bm || !bm->seq_ok(seq)) return PKV_ERR_INVALID_ARG;
+  auto& q = bm->seqs[seq];
+  for (int32_t b : q.table) bm->release(b);
+  q.table.clear();
+  q.table.shrink_to_fit();
+  q.len = 0;
+  q.live = false;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_seq_len(const pkv_block_manager* bm, int seq) {
+  if (!bm || !bm->seq_ok(seq)) return PKV_ERR_INVALID_ARG;
+  return bm->seqs[seq].len;
+}
+
+extern "C" int pkv_bm_seq_num_blocks(const pkv_block_manager* bm, int seq) {
+  if (!bm || !bm->seq_ok(seq)) return PKV_ERR_INVALID_ARG;
+  return (int)bm->seqs[seq].table.size();
+}
+
+extern "C" int pkv_bm_seq_table(const pkv_block_manager* bm, int seq, int32_t* out, int cap) {
+  if (!bm || !bm->seq_ok(seq) || cap < 0 || (cap > 0 && !out)) return PKV_ERR_INVALID_ARG;
+  const auto& t = bm->seqs[seq].table;
+  const int n = (int)t.size() < cap ? (int)t.size() : cap;
+  for (int i = 0; i < n; ++i) out[i] = t[i];
+  return n;
+}
+
+extern "C" int pkv_bm_export_tables(const pkv_block_manager* bm, const int* seqs, int n,
+                                    int32_t* out, int ld, int32_t* lens_out) {
+  if (!bm || n < 0 || ld < 1) return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  if (!seqs || !out || !lens_out) return PKV_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i) {
+    if (!bm->seq_ok(seqs[i]) || (int)bm->seqs[seqs[i]].table.size() > ld)
+      return PKV_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < n; ++i) {
+    const auto& q = bm->seqs[seqs[i]];
+    int32_t* row = out + (size_t)i * ld;
+    const int nb = (int)q.table.size();
+    for (int j = 0; j < nb; ++j) row[j] = q.table[j];
+    for (int j = nb; j < ld; ++j) row[j] = -1;
+    lens_out[i] = q.len;
+  }
+  return PKV_OK;
+}

@@ -1,0 +1,149 @@
+// kv_cache_ops.hip - cache append, whole-block copy and debug gather (gfx950).
+//
+// Sources cited by tag and section:
+//   [pofe] "PagedAttention: paging the KV cache"
+//   [arch] "PagedAttention: Virtual-Memory KV Cache Management, Continuous
+//          Batching, and PyTorch Architecture"
+//
+// All three are byte moves of whole 16-byte chunks: a token's row in the pool
+// (all KV heads, all channels) is contiguous, Hkv * D * sizeof(T) bytes, and a
+// multiple of 16 for every supported head size.  Each kernel resolves block
+// ids through pkv::row_offset, the same function the attention kernels use.
+#include "pkv_common.h"
+#include "pkv_host.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kThreads = 256;
+
+// One workgroup per sequence: copy the new token's row into slot len % B of
+// block table[len / B] ([pofe] "How it works", decode-step write).
+__global__ __launch_bounds__(kThreads) void append_kernel(
+    char* __restrict__ k_pool, char* __restrict__ v_pool, const char* __restrict__ k_new,
+    const char* __restrict__ v_new, const int32_t* __restrict__ tables, int max_blocks,
+    const int32_t* __restrict__ lens_pre, int num_blocks, int log2_b, int num_kv_heads,
+    int head_dim, int elem_bytes) {
+  const int s = blockIdx.x;
+  const int len = lens_pre[s];
+  if (len < 0) return;                                   // padding row
+  const int lb = logical_block(len, log2_b);
+  if (lb >= max_blocks) return;                          // table row too short: skip
+  const int blk = tables[(size_t)s * max_blocks + lb];
+  if (!valid_block(blk, num_blocks)) return;             // id outside the pool: skip
+  const size_t row_bytes = (size_t)num_kv_heads * head_dim * elem_bytes;
+  const size_t dst = row_offset(blk, len, log2_b, num_kv_heads, 0, head_dim) * elem_bytes;
+  const size_t src = (size_t)s * row_bytes;
+  const int chunks = (int)(row_bytes / 16);
+  for (int c = threadIdx.x; c < chunks; c += kThreads) {
+    store16(k_pool + dst + 16 * (size_t)c, load16(k_new + src + 16 * (size_t)c));
+    store16(v_pool + dst + 16 * (size_t)c, load16(v_new + src + 16 * (size_t)c));
+  }
+}
+
+// blockIdx.x = pair, blockIdx.y = slice of the block's chunks.
+__global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
+    char* __restrict__ k_pool, char* __restrict__ v_pool, const int32_t* __restrict__ src,
+    const int32_t* __restrict__ dst, int num_blocks, size_t block_bytes) {
+  const int a = src[blockIdx.x];
+  const int b = dst[blockIdx.x];
+  if (!valid_block(a, num_blocks) || !valid_block(b, num_blocks)) return;
+  const size_t chunks = block_bytes / 16;
+  const size_t sa = (size_t)a * block_bytes, sb = (size_t)b * block_bytes;
+  for (size_t c = (size_t)blockIdx.y * kThreads + threadIdx.x; c < chunks;
+       c += (size_t)gridDim.y * kThreads) {
+    store16(k_pool + sb + 16 * c, load16(k_pool + sa + 16 * c));
+    store16(v_pool + sb + 16 * c, load16(v_pool + sa + 16 * c));
+  }
+}
+
+constexpr int kGatherTokens = 16;
+
+// blockIdx.y = sequence, blockIdx.x = group of kGatherTokens tokens.
+__global__ __launch_bounds__(kThreads) void gather_kernel(
+    char* __restrict__ k_out, char* __restrict__ v_out, const char* __restrict__ k_pool,
+    const char* __restrict__ v_pool, const int32_t* __restrict__ tables, int max_blocks,
+    const int32_t* __restrict__ lens, int num_blocks, int log2_b, int num_kv_heads, int head_dim,
+    int elem_bytes, int max_len_out) {
+  const int s = blockIdx.y;
+  const int len = min(lens[s], max_len_out);
+  const int t0 = blockIdx.x * kGatherTokens;
+  if (t0 >= len) return;
+  const size_t row_bytes = (size_t)num_kv_heads * head_dim * elem_bytes;
+  const int row_chunks = (int)(row_bytes / 16);
+  for (int i = threadIdx.x; i < kGatherTokens * row_chunks; i += kThreads) {
+    const int t = t0 + i / row_chunks;
+    const int c = i % row_chunks;
+    if (t >= len) continue;
+    const int lb = logical_block(t, log2_b);
+    if (lb >= max_blocks) continue;
+    const int blk = tables[(size_t)s * max_blocks + lb];
+    if (!valid_block(blk, num_blocks)) continue;
+    const size_t from = row_offset(blk, t, log2_b, num_kv_heads, 0, head_dim) * elem_bytes + 16 * (size_t)c;
+    const size_t to = ((size_t)s * max_len_out + t) * row_bytes + 16 * (size_t)c;
+    store16(k_out + to, load16(k_pool + from));
+    store16(v_out + to, load16(v_pool + from));
+  }
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int paged_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens_pre, int num_seqs, int num_blocks,
+                               int block_size, int num_kv_heads, int head_dim, int dtype,
+                               void* stream) {
+  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || max_blocks_per_seq < 1) return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !context_lens_pre)
+    return PKV_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(append_kernel, dim3(num_seqs), dim3(kThreads), 0, (hipStream_t)stream,
+                     (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new,
+                     block_tables, max_blocks_per_seq, context_lens_pre, num_blocks,
+                     log2_exact(block_size), num_kv_heads, head_dim, dtype_bytes(dtype));
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" int paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* src,
+                                    const int32_t* dst, int num_pairs, int num_blocks,
+                                    int block_size, int num_kv_heads, int head_dim, int dtype,
+                                    void* stream) {
+  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  if (num_pairs < 0) return PKV_ERR_INVALID_ARG;
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src || !dst) return PKV_ERR_INVALID_ARG;
+  const size_t block_bytes = (size_t)block_size * num_kv_heads * head_dim * dtype_bytes(dtype);
+  const size_t chunks = block_bytes / 16;
+  const int slices = (int)std::min<size_t>(16, (chunks + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, slices), dim3(kThreads), 0,
+                     (hipStream_t)stream, (char*)k_pool, (char*)v_pool, src, dst, num_blocks,
+                     block_bytes);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int num_seqs, int num_blocks,
+                               int block_size, int num_kv_heads, int head_dim, int max_len_out,
+                               int dtype, void* stream) {
+  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_seqs > 65535 || max_blocks_per_seq < 1 || max_len_out < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || max_len_out == 0) return PKV_OK;
+  if (!k_out || !v_out || !k_pool || !v_pool || !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  const int groups = (max_len_out + kGatherTokens - 1) / kGatherTokens;
+  hipLaunchKernelGGL(gather_kernel, dim3(groups, num_seqs), dim3(kThreads), 0,
+                     (hipStream_t)stream, (char*)k_out, (char*)v_out, (const char*)k_pool,
+                     (const char*)v_pool, block_tables, max_blocks_per_seq, context_lens,
+                     num_blocks, log2_exact(block_size), num_kv_heads, head_dim,
+                     dtype_bytes(dtype), max_len_out);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

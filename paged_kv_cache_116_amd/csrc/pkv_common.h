@@ -1,0 +1,113 @@
+// pkv_common.h - device helpers shared by the libpagedkv kernels (gfx950 only).
+//
+// Sources cited by tag and section:
+//   [arch] "PagedAttention: Virtual-Memory KV Cache Management, Continuous
+//          Batching, and PyTorch Architecture"
+//   [note] "PagedAttention: Manage the Cache Without Moving the Sequence"
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+
+namespace pkv {
+
+// 16-bit element types are carried as raw bits; the tag selects conversions.
+struct F32 { using storage = float;    static constexpr int bytes = 4; static constexpr int code = PKV_F32; };
+struct F16 { using storage = uint16_t; static constexpr int bytes = 2; static constexpr int code = PKV_F16; };
+struct BF16 { using storage = uint16_t; static constexpr int bytes = 2; static constexpr int code = PKV_BF16; };
+
+inline int dtype_bytes(int dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16: return 2;
+    case PKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-table resolution.  Token t of a sequence lives in physical block
+// table[t / B] at offset t % B ([arch] "1. Paged Virtual Memory Mapping";
+// [note] "Map a ten-token sequence into pages").  The page's address formula
+// omits the head term and mixes bytes with elements; in the
+// [num_blocks, B, H_kv, D] pool the element (head h, channel 0) of that row is
+// at ((block * B + t % B) * H_kv + h) * D.  B is a power of two, passed as
+// its log2.  Every kernel that touches the pool goes through this function.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ size_t row_offset(int block, int token, int log2_b, int num_kv_heads,
+                                             int kv_head, int head_dim) {
+  const int offset = token & ((1 << log2_b) - 1);
+  return ((((size_t)block << log2_b) + offset) * (size_t)num_kv_heads + kv_head) * (size_t)head_dim;
+}
+
+// Logical block index of token t.
+__device__ __forceinline__ int logical_block(int token, int log2_b) { return token >> log2_b; }
+
+// True when a table entry names a block of the pool.
+__device__ __forceinline__ bool valid_block(int id, int num_blocks) {
+  return id >= 0 && id < num_blocks;
+}
+
+// ---------------------------------------------------------------------------
+// Conversions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp32 -> fp16 bits with the hardware conversion (round to nearest even).
+__device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
+template <typename T> struct Cvt;
+template <> struct Cvt<F32> {
+  // Unpack the 4 floats of a 16-byte chunk.
+  __device__ static __forceinline__ void unpack(const uint4& c, float* out) {
+    out[0] = __uint_as_float(c.x); out[1] = __uint_as_float(c.y);
+    out[2] = __uint_as_float(c.z); out[3] = __uint_as_float(c.w);
+  }
+  __device__ static __forceinline__ void store(float* dst, float v) { *dst = v; }
+};
+template <> struct Cvt<BF16> {
+  __device__ static __forceinline__ void unpack(const uint4& c, float* out) {
+    out[0] = bf16_lo(c.x); out[1] = bf16_hi(c.x); out[2] = bf16_lo(c.y); out[3] = bf16_hi(c.y);
+    out[4] = bf16_lo(c.z); out[5] = bf16_hi(c.z); out[6] = bf16_lo(c.w); out[7] = bf16_hi(c.w);
+  }
+  __device__ static __forceinline__ void store(uint16_t* dst, float v) { *dst = f32_to_bf16_rne(v); }
+};
+template <> struct Cvt<F16> {
+  __device__ static __forceinline__ void unpack(const uint4& c, float* out) {
+    out[0] = f16_lo(c.x); out[1] = f16_hi(c.x); out[2] = f16_lo(c.y); out[3] = f16_hi(c.y);
+    out[4] = f16_lo(c.z); out[5] = f16_hi(c.z); out[6] = f16_lo(c.w); out[7] = f16_hi(c.w);
+  }
+  __device__ static __forceinline__ void store(uint16_t* dst, float v) { *dst = f32_to_f16_rne(v); }
+};
+
+__device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+inline int log2_exact(int x) {
+  if (x <= 0 || (x & (x - 1)) != 0) return -1;
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+}  // namespace pkv

@@ -1,0 +1,34 @@
+// pkv_host.h - host-side argument checks shared by the libpagedkv entry points.
+#pragma once
+
+#include <algorithm>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/pagedkv.h"
+
+namespace pkv {
+
+inline bool supported_block_size(int b) {
+  return b == 1 || b == 2 || b == 4 || b == 8 || b == 16 || b == 32 || b == 64 || b == 128;
+}
+
+inline bool supported_head_dim(int d) {
+  return d == 16 || d == 32 || d == 64 || d == 128 || d == 256;
+}
+
+inline bool supported_dtype(int dt) { return dt == PKV_F32 || dt == PKV_F16 || dt == PKV_BF16; }
+
+// Shape checks every pool operation shares.  Sizes must be positive; block
+// size, head size and dtype must be in the supported lists.
+inline int check_pool_shape(int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                            int dtype) {
+  if (num_blocks < 1 || num_kv_heads < 1 || block_size < 1 || head_dim < 1)
+    return PKV_ERR_INVALID_ARG;
+  if (!supported_block_size(block_size) || !supported_head_dim(head_dim) ||
+      !supported_dtype(dtype))
+    return PKV_ERR_UNSUPPORTED;
+  return PKV_OK;
+}
+
+}  // namespace pkv

@@ -225,3 +225,25 @@ def make_workload(config_id: int, seed: int | None = None, *, batch: int | None 
 def to_f64(t: torch.Tensor) -> np.ndarray:
     """Exact widening of a float32 / float16 / bfloat16 tensor to numpy float64."""
     return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def extract_sequences(w: Workload, seqs, dtype=np.float64):
+    """Host float64 copies of the inputs of the chosen sequences only: the
+    blocks their tables name (renumbered densely), their tables, lengths,
+    queries and new tokens.  Lets a CPU reference run on a sample of a
+    large GPU-resident workload."""
+    seqs = [int(s) for s in seqs]
+    nbs = [-(-int(w.lens[s]) // w.block_size) for s in seqs]
+    ids = np.unique(np.concatenate([w.tables[s, :n] for s, n in zip(seqs, nbs)]))
+    remap = {int(b): i for i, b in enumerate(ids)}
+    idx = torch.as_tensor(ids, device=w.k_pool.device, dtype=torch.long)
+    sel = torch.as_tensor(seqs, device=w.q.device, dtype=torch.long)
+    tables = np.full((len(seqs), max(nbs)), -1, dtype=np.int64)
+    for i, (s, n) in enumerate(zip(seqs, nbs)):
+        tables[i, :n] = [remap[int(b)] for b in w.tables[s, :n]]
+    def host(t):   # exact: every element type here widens exactly to float32/64
+        return t.detach().to("cpu").to(torch.float64).numpy().astype(dtype)
+
+    return dict(k_pool=host(w.k_pool[idx]), v_pool=host(w.v_pool[idx]), tables=tables,
+                lens=w.lens[seqs].copy(), lens_pre=w.lens_pre[seqs].copy(),
+                q=host(w.q[sel]), k_new=host(w.k_new[sel]), v_new=host(w.v_new[sel]))
