@@ -2,9 +2,9 @@
 """Paged decode benchmark on one MI355X.
 
 A step is one pass of the whole decode hot path over one batch: the cache
-append of one new token per sequence (paged_kv_append), the per-partition
-attention kernel and the log-sum-exp merge (paged_decode_attention_partitions
-+ paged_decode_attention_merge).  Host slot allocation is done once before
+append of one new token per sequence (paged_kv_append), then the three
+launches of paged decode attention: the work plan, the partition kernel and
+the log-sum-exp merge (paged_decode_attention_plan / _partitions / _merge).  Host slot allocation is done once before
 timing (the tables already list the slot), and the append rewrites the same
 bytes every step, so the timed steps are identical.
 
@@ -40,7 +40,7 @@ WORKLOAD_DESC = {
     2: "13B-shaped MHA bf16: 40 q = 40 kv heads, D 128, B 16, batch 64, lengths U[64,2048], pool 16384 blocks",
     3: "70B-shaped GQA bf16: 64 q / 8 kv heads, D 128, B 16, batch 256, lengths log-uniform [512,8192], pool 1.1x needed",
     4: "shared-prefix GQA fp16: 32 q / 8 kv heads, D 128, B 16, batch 128, 1024-token shared prefix + U[1,512] private",
-    5: "long-context GQA bf16: 64 q / 8 kv heads, D 128, batch 8, lengths U[8192,32768], 512-token partitions",
+    5: "long-context GQA bf16: 64 q / 8 kv heads, D 128, batch 8, lengths U[8192,32768]",
 }
 
 
@@ -51,13 +51,18 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None)
-    ap.add_argument("--partition-tokens", type=int, default=512)
+    ap.add_argument("--partition-tokens", type=int, default=0,
+                    help="0 = balanced ranges; > 0 = also cap each range at this many tokens")
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
     ap.add_argument("--copy-gib", type=float, default=2.0,
                     help="size of the device-to-device copy that measures practical bandwidth")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="after timing, run three plain kernels of known size on a 1 GiB fp32 "
+                         "buffer written at start-up (read-only sum, fill, elementwise copy) so "
+                         "that rocprofv3 FETCH_SIZE / WRITE_SIZE can be scaled to bytes")
     return ap.parse_args(argv)
 
 
@@ -102,6 +107,14 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    calib = None
+    if args.calibrate:
+        # Written now, read after the timed steps: by then gigabytes of KV
+        # traffic have evicted it from L2 and the 256 MB MALL.
+        calib = torch.ones(2**28, dtype=torch.float32, device=dev)
+        calib_out = torch.empty_like(calib)
+        torch.cuda.synchronize()
+
     kw = {}
     if args.block_size:
         kw["block_size"] = args.block_size
@@ -140,6 +153,11 @@ def main(argv=None) -> int:
     def append():
         pkv.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens_pre, stream=stream)
 
+    def plan():
+        pkv.paged_decode_attention_plan(out, w.q, w.k_pool, w.v_pool, tables, lens,
+                                        scale=w.scale, partition_tokens=P, workspace=ws,
+                                        stream=stream)
+
     def partitions():
         pkv.paged_decode_attention_partitions(kernel, out, w.q, w.k_pool, w.v_pool, tables, lens,
                                               scale=w.scale, partition_tokens=P, workspace=ws,
@@ -152,13 +170,14 @@ def main(argv=None) -> int:
 
     for _ in range(args.warmup):
         append()
+        plan()
         partitions()
         merge()
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    marks = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
     start, end = ev(), ev()
     torch.cuda.synchronize()
     start.record(stream)
@@ -166,17 +185,20 @@ def main(argv=None) -> int:
         m[0].record(stream)
         append()
         m[1].record(stream)
-        partitions()
+        plan()
         m[2].record(stream)
-        merge()
+        partitions()
         m[3].record(stream)
+        merge()
+        m[4].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_step = total_ms / args.steps
     t_app = [m[0].elapsed_time(m[1]) for m in marks]
-    t_part = [m[1].elapsed_time(m[2]) for m in marks]
-    t_merge = [m[2].elapsed_time(m[3]) for m in marks]
+    t_plan = [m[1].elapsed_time(m[2]) for m in marks]
+    t_part = [m[2].elapsed_time(m[3]) for m in marks]
+    t_merge = [m[3].elapsed_time(m[4]) for m in marks]
     part_ms = statistics.mean(t_part)
     print(f"# timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, partition {part_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
@@ -196,6 +218,17 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         copy_gbps = 5 * 2 * n * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
         del a, b
+
+    if calib is not None:
+        # Plain kernels of known size for counter calibration: 1 GiB read
+        # (sum), 1 GiB written (fill), 1 GiB read + 1 GiB written (x * 1).
+        total = calib.sum()
+        calib_out.fill_(2.0)
+        torch.mul(calib, 1.0, out=calib_out)
+        torch.cuda.synchronize()
+        print(f"# calibration kernels ran on 1 GiB buffers (sum={float(total):.0f})",
+              file=sys.stderr, flush=True)
+        del calib, calib_out
 
     parity = None
     if check_inputs is not None:
@@ -240,7 +273,7 @@ def main(argv=None) -> int:
         print(f"# cpu oracle: {cpu['value']:.4f} GB/s over {spent:.1f}s", file=sys.stderr, flush=True)
 
     kv_gbps_step = kv_bytes / (ms_step * 1e-3) / 1e9
-    attn_ms = statistics.mean(t_part) + statistics.mean(t_merge)
+    attn_ms = statistics.mean(t_plan) + statistics.mean(t_part) + statistics.mean(t_merge)
     achieved = alg_bytes / (part_ms * 1e-3) / 1e9
     kname = {"auto": "mfma" if w.dtype != "f32" and D >= 32 else "valu"}.get(args.kernel, args.kernel)
     traffic = measured_traffic(w.name + (f"_B{B}" if args.config == 5 else ""), kname)
@@ -266,6 +299,7 @@ def main(argv=None) -> int:
         "kv_bytes_per_step": kv_bytes,
         "kv_gbps_attention": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 2),
         "us": {"step": round(ms_step * 1e3, 2), "append": round(statistics.mean(t_app) * 1e3, 2),
+               "plan": round(statistics.mean(t_plan) * 1e3, 2),
                "partitions": round(part_ms * 1e3, 2),
                "partitions_p10": round(np.percentile(t_part, 10) * 1e3, 2),
                "partitions_p90": round(np.percentile(t_part, 90) * 1e3, 2),

@@ -36,7 +36,9 @@
  *   with round-to-nearest-even.
  * - Supported shapes: block_size in {1, 2, 4, 8, 16, 32, 64, 128}; head_dim in
  *   {16, 32, 64, 128, 256}.  Other shapes return PKV_ERR_UNSUPPORTED; there is no
- *   slower fallback path.
+ *   slower fallback path.  Attention also needs
+ *   num_seqs * ceil(max_blocks_per_seq * block_size / 16) * num_kv_heads * ceil(g / 8)
+ *   below 2^31 (PKV_ERR_INVALID_ARG otherwise).
  * - Block ids are the caller's contract: entries a call reads must lie in
  *   [0, num_blocks).  Kernels never touch memory outside the pools for a bad id:
  *   append and copy skip the row, and attention writes NaN for every head of a
@@ -121,10 +123,14 @@ int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_
                     int num_kv_heads, int head_dim, int max_len_out, int dtype, void* stream);
 
 /*
- * paged_decode_workspace_bytes - scratch size paged_decode_attention needs.
+ * paged_decode_workspace_bytes - scratch size paged_decode_attention needs on
+ * the current device.
  *
- * max_context_len bounds every L_s of the call (max_blocks_per_seq * block_size
- * always does).  partition_tokens 0 selects the default of 512.  Returns 0 for
+ * The workspace holds the work plan (prefix sums of every sequence's 16-token
+ * tiles and one start descriptor per range of work) and the partial softmax
+ * states of sequences split across workgroups.  Its size depends on num_seqs,
+ * num_q_heads, head_dim, the device's compute-unit count and, when
+ * partition_tokens > 0, on max_context_len / partition_tokens.  Returns 0 for
  * invalid arguments.
  */
 size_t paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
@@ -140,17 +146,24 @@ size_t paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
  * where K_s[t] is the pool row of token t resolved through block_tables[s].
  * This is the ordinary attention sum regrouped by block ([pofe] "How it works";
  * [arch] "3. Non-Contiguous Online Softmax Attention Kernel": running maximum,
- * normaliser and unnormalised accumulator per block, in fp32).  The history is
- * cut into partitions of partition_tokens tokens (a multiple of block_size;
- * 0 = 512) processed in parallel; their partial states are merged with the
- * log-sum-exp rule O = sum_p e^(m_p-M) o_p / sum_p e^(m_p-M) l_p, M = max_p m_p.
- * L = 0 yields zeros.  Slots at or past L are never read.
+ * normaliser and unnormalised accumulator, in fp32).  L <= 0 yields zeros; a
+ * length above max_blocks_per_seq * block_size yields NaN.  Slots at or past L
+ * are never read.
  *
- *   scale     : usually 1/sqrt(head_dim) ([arch] section 3)
- *   workspace : device scratch of at least
- *               paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
- *                                            max_blocks_per_seq*block_size, partition_tokens)
- *               bytes, 256-byte aligned; contents on entry do not matter.
+ * Work split: the (KV head, sequence, 16-token tile) space is cut into equal
+ * ranges, one per resident workgroup, so every compute unit gets the same
+ * number of tokens whatever the length mix.  A sequence cut across ranges is
+ * finished by a log-sum-exp merge of the ranges' partial states,
+ * O = sum_p e^(m_p-M) o_p / sum_p e^(m_p-M) l_p with M = max_p m_p.
+ *   partition_tokens : 0 = balanced ranges (recommended); > 0 = in addition no
+ *                      range longer than this many tokens (a multiple of 16),
+ *                      i.e. classic fixed split-K partitions.
+ *   scale            : usually 1/sqrt(head_dim) ([arch] section 3)
+ *   workspace        : device scratch of at least
+ *                      paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ *                          max_blocks_per_seq*block_size, partition_tokens)
+ *                      bytes, 256-byte aligned; contents on entry do not matter.
+ *                      Calls that share a workspace must not overlap in time.
  */
 int paged_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
                            const int32_t* block_tables, int max_blocks_per_seq,
@@ -180,18 +193,26 @@ int paged_decode_attention_with(int kernel, void* out, const void* q, const void
                                 int dtype, void* stream);
 
 /*
- * paged_decode_attention_partitions / paged_decode_attention_merge - the two
- * launches paged_decode_attention_with(kernel, ...) makes, exposed so a caller
- * can time or schedule them separately.  Same arguments; call partitions then
- * merge on the same stream with the same workspace.
- *  - partitions: every (sequence, KV head, partition) workgroup runs the block
- *    recurrence of [arch] section 3 over its tokens; a sequence with a single
- *    partition gets its final output here, the others leave their partial
- *    state (m, l, o) in the workspace;
- *  - merge: for every sequence with more than one partition, combines the
- *    partial states with O = sum_p e^(m_p-M) o_p / sum_p e^(m_p-M) l_p and
- *    writes the output.  Does nothing when every L fits one partition.
+ * paged_decode_attention_plan / _partitions / _merge - the three launches
+ * paged_decode_attention_with(kernel, ...) makes, exposed so a caller can time
+ * or schedule them separately.  Same arguments; call them in this order on one
+ * stream with one workspace.
+ *  - plan: one workgroup prefix-sums the tile counts of all sequences, writes
+ *    the start of every range of work and fills the rows of sequences with
+ *    L <= 0 (zeros) or an over-long L (NaN);
+ *  - partitions: persistent workgroups walk their ranges with the block
+ *    recurrence of [arch] section 3; a sequence inside one range gets its
+ *    final output, a split one leaves partial states (m, l, o);
+ *  - merge: the range where a split sequence starts combines its partial
+ *    states with the rule above and writes the output.
  */
+int paged_decode_attention_plan(void* out, const void* q, const void* k_pool,
+                                const void* v_pool, const int32_t* block_tables,
+                                int max_blocks_per_seq, const int32_t* context_lens,
+                                int num_seqs, int num_blocks, int block_size, int num_q_heads,
+                                int num_kv_heads, int head_dim, float scale,
+                                int partition_tokens, void* workspace, size_t workspace_bytes,
+                                int dtype, void* stream);
 int paged_decode_attention_partitions(int kernel, void* out, const void* q, const void* k_pool,
                                       const void* v_pool, const int32_t* block_tables,
                                       int max_blocks_per_seq, const int32_t* context_lens,

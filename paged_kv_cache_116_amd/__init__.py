@@ -62,6 +62,7 @@ _ATTN_ARGS = [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, 
               _i32, _p, _sz, _i32, _p]
 _sig("paged_decode_attention", _i32, _ATTN_ARGS)
 _sig("paged_decode_attention_with", _i32, [_i32] + _ATTN_ARGS)
+_sig("paged_decode_attention_plan", _i32, _ATTN_ARGS)
 _sig("paged_decode_attention_partitions", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_attention_merge", _i32, _ATTN_ARGS)
 _sig("pkv_validate_tables", _i32, [_p, _i32, _p, _i32, _i32, _i32, _intp])
@@ -215,9 +216,17 @@ def _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partit
             int(partition_tokens), ws_ptr, workspace.numel(), dt, _stream(stream))
 
 
+def paged_decode_attention_plan(out, q, k_pool, v_pool, block_tables, context_lens, *,
+                                scale=None, partition_tokens=0, workspace, stream=None):
+    """First launch of paged_decode_attention (work plan, empty-row fills)."""
+    args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                      partition_tokens, workspace, stream)
+    _check(_lib.paged_decode_attention_plan(*args), "paged_decode_attention_plan")
+
+
 def paged_decode_attention_partitions(kernel, out, q, k_pool, v_pool, block_tables, context_lens,
                                       *, scale=None, partition_tokens=0, workspace, stream=None):
-    """First launch of paged_decode_attention (per-partition states)."""
+    """Second launch of paged_decode_attention (the partition kernel)."""
     args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                       partition_tokens, workspace, stream)
     _check(_lib.paged_decode_attention_partitions(int(kernel), *args),
@@ -226,7 +235,7 @@ def paged_decode_attention_partitions(kernel, out, q, k_pool, v_pool, block_tabl
 
 def paged_decode_attention_merge(out, q, k_pool, v_pool, block_tables, context_lens, *,
                                  scale=None, partition_tokens=0, workspace, stream=None):
-    """Second launch of paged_decode_attention (log-sum-exp merge)."""
+    """Third launch of paged_decode_attention (log-sum-exp merge)."""
     args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                       partition_tokens, workspace, stream)
     _check(_lib.paged_decode_attention_merge(*args), "paged_decode_attention_merge")

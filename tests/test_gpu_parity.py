@@ -214,16 +214,12 @@ def test_attention_matches_oracle(cid, seed_off):
 
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
-@pytest.mark.parametrize("part", [16, 64, 512])
+@pytest.mark.parametrize("part", [0, 16, 48, 512])
 def test_attention_kernels_and_partitions(cid, kernel, part):
     kw = dict(SMALL[cid])
     if cid == 5:
-        kw["block_size"] = 8 if part < 512 else 32
-        if kw["block_size"] > part:
-            kw["block_size"] = 16
+        kw["block_size"] = {0: 8, 16: 32, 48: 8, 512: 32}[part]
     w = workloads.make_workload(cid, **kw)
-    if part % w.block_size:
-        pytest.skip("partition must be a multiple of the block size")
     dev = to_dev(w)
     ref = oracle_step(w, w.k_pool, w.v_pool)
     k = pkv.PKV_ATTN_VALU if kernel == "valu" else pkv.PKV_ATTN_MFMA
@@ -278,6 +274,7 @@ def _with_lengths(w, lens):
     """A config-3-shaped workload with explicit lengths (same generator rules)."""
     import workloads as wl
     rng = np.random.default_rng(77)
+    lens = [int(x) for x in lens]
     B = w.block_size
     nbs = [-(-L // B) for L in lens]
     N = sum(nbs) + 5
@@ -305,6 +302,22 @@ def _with_lengths(w, lens):
                        q=torch.randn(S, Hq, D, generator=gen).to(dt),
                        k_new=torch.randn(S, Hkv, D, generator=gen).to(dt),
                        v_new=torch.randn(S, Hkv, D, generator=gen).to(dt), k_pool=kp, v_pool=vp)
+
+
+@pytest.mark.parametrize("part", [0, 64])
+def test_many_sequences_and_long_ones(part):
+    # More sequences than the plan keeps in LDS (global binary search), mixed
+    # with a few long ones that span many ranges.
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, 40, size=9000)
+    lens[[5, 4000, 8999]] = [3000, 2500, 1777]
+    w = workloads.make_workload(3, batch=len(lens), len_range=(1, 2), block_size=8,
+                                num_q_heads=4, num_kv_heads=2, head_dim=32)
+    w = _with_lengths(w, lens.tolist())
+    dev = to_dev(w)
+    ref = oracle_step(w, w.k_pool, w.v_pool)
+    out = run_step(w, dev, partition_tokens=part)
+    check_close(out, ref, w.dtype, f"9000 seqs P={part}")
 
 
 def test_zero_length_gives_zeros_and_bad_ids_give_nan():

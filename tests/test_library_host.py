@@ -64,13 +64,13 @@ def attn(**kw):
     (dict(dt=7), pkv.PKV_ERR_UNSUPPORTED),
     (dict(n=0), pkv.PKV_ERR_INVALID_ARG),
     (dict(s=-1), pkv.PKV_ERR_INVALID_ARG),
-    (dict(s=70000), pkv.PKV_ERR_INVALID_ARG),
     (dict(part=24), pkv.PKV_ERR_INVALID_ARG),      # not a multiple of 16
-    (dict(b=32, part=16), pkv.PKV_ERR_INVALID_ARG),  # not a multiple of B
-    (dict(part=8192), pkv.PKV_ERR_INVALID_ARG),
+    (dict(part=-16), pkv.PKV_ERR_INVALID_ARG),
+    (dict(mb=1 << 27, b=16), pkv.PKV_ERR_INVALID_ARG),   # context beyond 2^30 tokens
+    (dict(s=4096, mb=1 << 22, b=16, part=0), pkv.PKV_ERR_INVALID_ARG),  # tile count overflow
     (dict(q=None), pkv.PKV_ERR_INVALID_ARG),
     (dict(scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
-    (dict(mb=64, ws=None), pkv.PKV_ERR_WORKSPACE),   # 1024 tokens: two partitions
+    (dict(ws=None), pkv.PKV_ERR_WORKSPACE),          # the plan always needs one
     (dict(mb=64, wsb=16), pkv.PKV_ERR_WORKSPACE),
     (dict(mb=64, ws=FAKE + 4), pkv.PKV_ERR_WORKSPACE),  # misaligned
 ])
@@ -105,11 +105,17 @@ def test_cache_ops_reject_bad_arguments():
 
 
 def test_workspace_size():
-    assert pkv.paged_decode_workspace_bytes(4, 8, 128, 512, 512) == 0     # one partition
-    got = pkv.paged_decode_workspace_bytes(256, 64, 128, 8192, 512)
-    rows = 256 * 64 * 16
-    assert got >= rows * (128 + 2) * 4 and got % 256 == 0
+    small = pkv.paged_decode_workspace_bytes(4, 8, 128, 512, 0)
+    assert small > 0 and small % 256 == 0
+    # balanced ranges: independent of the context length
+    assert pkv.paged_decode_workspace_bytes(4, 8, 128, 1 << 20, 0) == small
+    # fixed partitions: room for one partial state per partition and head
+    capped = pkv.paged_decode_workspace_bytes(256, 64, 128, 8192, 512)
+    assert capped >= 256 * 64 * 16 * (128 + 2) * 4
+    assert pkv.paged_decode_workspace_bytes(512, 64, 128, 8192, 0) > \
+        pkv.paged_decode_workspace_bytes(256, 64, 128, 8192, 0)
     assert pkv.paged_decode_workspace_bytes(-1, 8, 128, 512, 512) == 0
+    assert pkv.paged_decode_workspace_bytes(4, 8, 128, 512, -16) == 0
 
 
 def test_validate_tables():

@@ -115,9 +115,10 @@ def make_workload(config_id: int, seed: int | None = None, *, batch: int | None 
                   len_range=None, block_size: int | None = None, prefix_tokens: int = 1024,
                   device="cpu", poison: bool = True, dtype: str | None = None,
                   num_q_heads: int | None = None, num_kv_heads: int | None = None,
-                  head_dim: int | None = None) -> Workload:
+                  head_dim: int | None = None, shuffle: bool = True) -> Workload:
     """Draw config ``config_id`` (1-5).  Keyword overrides shrink a config for
-    tests while keeping its structure (length law, sharing, shuffled ids)."""
+    tests while keeping its structure (length law, sharing, shuffled ids).
+    ``shuffle=False`` hands out physical ids in order (identity-like tables)."""
     if seed is None:
         seed = default_seed(config_id)
     spec_dtype, spec_b, spec_hq, spec_hkv, spec_d, spec_batch, spec_range = SPECS[config_id]
@@ -151,7 +152,7 @@ def make_workload(config_id: int, seed: int | None = None, *, batch: int | None 
         else:
             num_blocks = int(math.ceil(1.1 * sum(nb))) + 1
 
-    perm = rng.permutation(num_blocks)
+    perm = rng.permutation(num_blocks) if shuffle else np.arange(num_blocks)
     nbs = [-(-int(L) // B) for L in lens]
     max_blocks = max(nbs)
     if config_id == 4 and full_size:
