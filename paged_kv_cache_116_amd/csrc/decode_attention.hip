@@ -136,6 +136,45 @@ template <> struct Mfma<F16> {
   }
 };
 
+// Pairs of 16-bit values for the P.V product: probabilities of two tokens
+// packed to the element type (round to nearest even) and multiplied with the
+// same channel of the two tokens' V rows, accumulated in fp32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <typename T> struct Pair;
+template <> struct Pair<BF16> {
+  __device__ static __forceinline__ uint32_t pack(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ float lo(uint32_t w) { return bf16_lo(w); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return bf16_hi(w); }
+  __device__ static __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+  }
+};
+template <> struct Pair<F16> {
+  __device__ static __forceinline__ uint32_t pack(float a, float b) {
+    const f16x2_t v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  __device__ static __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
+  __device__ static __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
+  __device__ static __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c,
+                                  false);
+  }
+};
+
+// (v0, v1) -> low halves and high halves of two dwords, paired per channel.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t t0, uint32_t t1) {
+  return __builtin_amdgcn_perm(t1, t0, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t t0, uint32_t t1) {
+  return __builtin_amdgcn_perm(t1, t0, 0x07060302u);
+}
+
 // A sequence is live when 0 < L <= max_blocks * B; it then has ceil(L/16) tiles.
 __device__ __forceinline__ int live_tiles(int L, int max_len) {
   return (L > 0 && L <= max_len) ? (L + kTile - 1) / kTile : 0;
@@ -364,11 +403,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
   constexpr int kSlots = ((KCH + TPR) * 4 <= 32 && G >= 4) ? 3 : 2;
   static_assert(D % 32 == 0 && TPR >= 1 && G <= kMaxGroup && G * D <= kMaxGD, "shape");
 
+  // Probabilities of the current tile per head: fp32 for the FMA form,
+  // pairs of 16-bit values (tokens 2j, 2j+1) for the dot2 form.
+  constexpr bool kDot2 = TPR >= 2;
   __shared__ __align__(16) float p_lds[kWaves][G][kTile];
   __shared__ __align__(16) float alpha_lds[kWaves][G];
   __shared__ float red_m[kWaves][G];
   __shared__ float red_l[kWaves][G];
   __shared__ __align__(16) float red_acc[kWaves][G][D];
+  uint32_t (*p2_lds)[G][kTile / 2] = reinterpret_cast<uint32_t (*)[G][kTile / 2]>(p_lds);
 
   const int lane = threadIdx.x & 63;
   // The wave index is uniform across the wave; saying so lets the tile loop
@@ -406,16 +449,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
       int first, nid;
       const int ids = tile_block_ids(p, trow, tb, L, first, nid, bad);
       const int id0 = __builtin_amdgcn_readfirstlane(ids);
-      auto row = [&](int t, int ch) -> size_t {
-        const int tt = min(t, last);
-        const int blk = nid == 1 ? id0 : __shfl(ids, (tt >> p.log2_b) - first);
-        return (row_offset(blk, tt, p.log2_b, p.num_kv_heads, sg.kvh, D) + ch) * bytes;
-      };
-      const size_t ko = row(tb + col, kgrp * 8);
+      if (nid == 1) {
+        // The whole tile lies in one block: one scalar base per pool, and
+        // per-lane 32-bit offsets of rows (clamped to the last valid token).
+        const int rlim = last - tb;
+        const size_t base = row_offset(id0, tb, p.log2_b, p.num_kv_heads, sg.kvh, D) * bytes;
+        const char* kbase = p.k_pool + base;
+        const char* vbase = p.v_pool + base;
+        const uint32_t rstride = (uint32_t)(p.num_kv_heads * D * bytes);
+        const uint32_t ko = (uint32_t)min(col, rlim) * rstride + kgrp * 8 * bytes;
 #pragma unroll
-      for (int j = 0; j < KCH; ++j) kb[SL][j] = load16(p.k_pool + ko + 32 * j * bytes);
+        for (int j = 0; j < KCH; ++j) kb[SL][j] = load16(kbase + ko + 32 * j * bytes);
 #pragma unroll
-      for (int i = 0; i < TPR; ++i) vb[SL][i] = load16(p.v_pool + row(tb + TPR * vr + i, vc * 8));
+        for (int i = 0; i < TPR; ++i)
+          vb[SL][i] = load16(vbase + (uint32_t)min(TPR * vr + i, rlim) * rstride + vc * 8 * bytes);
+      } else {
+        auto row = [&](int t, int ch) -> size_t {
+          const int tt = min(t, last);
+          const int blk = __shfl(ids, (tt >> p.log2_b) - first);
+          return (row_offset(blk, tt, p.log2_b, p.num_kv_heads, sg.kvh, D) + ch) * bytes;
+        };
+        const size_t ko = row(tb + col, kgrp * 8);
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) kb[SL][j] = load16(p.k_pool + ko + 32 * j * bytes);
+#pragma unroll
+        for (int i = 0; i < TPR; ++i) vb[SL][i] = load16(p.v_pool + row(tb + TPR * vr + i, vc * 8));
+      }
     };
 
     float m_run = -INFINITY;  // running maximum of head `col` (log2 units)
@@ -462,28 +521,58 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
 
       float pv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pv[i] = fast_exp2(sv[i] - m_run);   // masked tokens: exp2(-inf) = 0
-        l_run += pv[i];
+      for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[i] - m_run);   // masked: exp2(-inf) = 0
+      if constexpr (kDot2) {
+        // P rounded to the element type for the dot2 product; the normaliser
+        // sums the same rounded values, so the weights still sum to one.
+        const uint32_t q01 = Pair<T>::pack(pv[0], pv[1]);
+        const uint32_t q23 = Pair<T>::pack(pv[2], pv[3]);
+        l_run += (Pair<T>::lo(q01) + Pair<T>::hi(q01)) + (Pair<T>::lo(q23) + Pair<T>::hi(q23));
+        if (col < G) *reinterpret_cast<uint2*>(&p2_lds[w][col][2 * kgrp]) = make_uint2(q01, q23);
+      } else {
+        l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
+        if (col < G)
+          *reinterpret_cast<float4*>(&p_lds[w][col][4 * kgrp]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
       }
-      if (col < G)
-        *reinterpret_cast<float4*>(&p_lds[w][col][4 * kgrp]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
       wave_lds_sync();
 
       // P.V on the vector ALU: lane (vr, vc) owns channels 8vc..8vc+7 of the
       // tile's tokens TPR*vr + i.
-      float vf[TPR][8];
+      if constexpr (kDot2) {
+        constexpr int NP = TPR / 2;   // token pairs per lane
+        uint32_t vp[NP][8];           // channel e of tokens (2k, 2k+1)
 #pragma unroll
-      for (int i = 0; i < TPR; ++i) Cvt<T>::unpack(vb[SL][i], vf[i]);
+        for (int k = 0; k < NP; ++k) {
+          const uint4 a = vb[SL][2 * k], b = vb[SL][2 * k + 1];
+          vp[k][0] = pair_lo(a.x, b.x); vp[k][1] = pair_hi(a.x, b.x);
+          vp[k][2] = pair_lo(a.y, b.y); vp[k][3] = pair_hi(a.y, b.y);
+          vp[k][4] = pair_lo(a.z, b.z); vp[k][5] = pair_hi(a.z, b.z);
+          vp[k][6] = pair_lo(a.w, b.w); vp[k][7] = pair_hi(a.w, b.w);
+        }
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float ph[TPR];
+        for (int h = 0; h < G; ++h) {
+          uint32_t pp[NP];
 #pragma unroll
-        for (int i = 0; i < TPR; ++i) ph[i] = p_lds[w][h][TPR * vr + i];
+          for (int k = 0; k < NP; ++k) pp[k] = p2_lds[w][h][NP * vr + k];
 #pragma unroll
-        for (int i = 0; i < TPR; ++i)
+          for (int k = 0; k < NP; ++k)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[i], vf[i][e], acc[h][e]);
+            for (int e = 0; e < 8; ++e) acc[h][e] = Pair<T>::dot2(pp[k], vp[k][e], acc[h][e]);
+        }
+      } else {
+        float vf[TPR][8];
+#pragma unroll
+        for (int i = 0; i < TPR; ++i) Cvt<T>::unpack(vb[SL][i], vf[i]);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float ph[TPR];
+#pragma unroll
+          for (int i = 0; i < TPR; ++i) ph[i] = p_lds[w][h][TPR * vr + i];
+#pragma unroll
+          for (int i = 0; i < TPR; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[i], vf[i][e], acc[h][e]);
+        }
       }
     };
 
