@@ -54,6 +54,8 @@ def parse_args(argv=None):
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="0 = balanced ranges; > 0 = also cap each range at this many tokens")
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--cache-kv", choices=["auto", "on", "off"], default="auto",
+                    help="PKV_ATTN_CACHE_KV: auto = on when the tables share blocks")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--no-check", action="store_true", help="skip the sampled parity check")
@@ -148,13 +150,21 @@ def main(argv=None) -> int:
     ws = torch.empty(max(1, pkv.paged_decode_workspace_bytes(S, Hq, D, w.max_blocks * B, P)),
                      dtype=torch.uint8, device=dev)
     kernel = {"auto": pkv.PKV_ATTN_AUTO, "valu": pkv.PKV_ATTN_VALU, "mfma": pkv.PKV_ATTN_MFMA}[args.kernel]
+    # A serving system's block manager knows whether any block is referenced by
+    # more than one sequence; here the tables say it.
+    used = np.concatenate([w.tables[s, : -(-int(w.lens[s]) // B)] for s in range(S)
+                           if w.lens[s] > 0] or [np.zeros(0, np.int64)])
+    shared = bool(used.size and np.bincount(used).max() > 1)
+    cache_kv = shared if args.cache_kv == "auto" else args.cache_kv == "on"
+    if cache_kv:
+        kernel |= pkv.PKV_ATTN_CACHE_KV
     stream = torch.cuda.current_stream()
 
     def append():
         pkv.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens_pre, stream=stream)
 
     def plan():
-        pkv.paged_decode_attention_plan(out, w.q, w.k_pool, w.v_pool, tables, lens,
+        pkv.paged_decode_attention_plan(kernel, out, w.q, w.k_pool, w.v_pool, tables, lens,
                                         scale=w.scale, partition_tokens=P, workspace=ws,
                                         stream=stream)
 
@@ -164,7 +174,7 @@ def main(argv=None) -> int:
                                               stream=stream)
 
     def merge():
-        pkv.paged_decode_attention_merge(out, w.q, w.k_pool, w.v_pool, tables, lens,
+        pkv.paged_decode_attention_merge(kernel, out, w.q, w.k_pool, w.v_pool, tables, lens,
                                          scale=w.scale, partition_tokens=P, workspace=ws,
                                          stream=stream)
 
@@ -293,7 +303,8 @@ def main(argv=None) -> int:
         "config": {"workload": WORKLOAD_DESC[args.config] + (f" (B={B})" if args.config == 5 else ""),
                    "name": w.name, "batch": S, "block_size": B, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "tokens": int(lens64.sum()),
-                   "partition_tokens": P, "kernel": kname},
+                   "partition_tokens": P, "kernel": kname, "shared_blocks": shared,
+                   "cache_kv": cache_kv},
         "pct_of_hbm_peak": round(100 * kv_gbps_step / HBM_PEAK_GBPS, 2),
         "seq_layer_steps_per_s": round(S / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,

@@ -151,8 +151,10 @@ size_t paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
  * are never read.
  *
  * Work split: the (KV head, sequence, 16-token tile) space is cut into equal
- * ranges, one per resident workgroup, so every compute unit gets the same
- * number of tokens whatever the length mix.  A sequence cut across ranges is
+ * ranges, a few per resident workgroup, which the workgroups claim first come
+ * first served, so every compute unit stays busy to the end whatever the
+ * length mix and however unevenly the memory system serves the units.  Which
+ * workgroup takes a range never changes a result.  A sequence cut across ranges is
  * finished by a log-sum-exp merge of the ranges' partial states,
  * O = sum_p e^(m_p-M) o_p / sum_p e^(m_p-M) l_p with M = max_p m_p.
  *   partition_tokens : 0 = balanced ranges (recommended); > 0 = in addition no
@@ -174,15 +176,30 @@ int paged_decode_attention(void* out, const void* q, const void* k_pool, const v
 
 /*
  * paged_decode_attention_with - paged_decode_attention with an explicit choice
- * of partition kernel, for measuring one design against the other:
+ * of partition kernel (for measuring one design against the other) and of
+ * the cache policy (PKV_ATTN_CACHE_KV below, OR-ed in):
  *   PKV_ATTN_AUTO  the default choice (MFMA for fp16/bf16 with head_dim >= 32,
  *                  vector ALU otherwise);
  *   PKV_ATTN_VALU  the vector-ALU kernel (every dtype and head size);
  *   PKV_ATTN_MFMA  the matrix-core kernel (fp16/bf16, head_dim >= 32 only,
  *                  else PKV_ERR_UNSUPPORTED).
- * Results agree to fp32 rounding; other arguments as paged_decode_attention.
+ * Results agree to fp32 rounding; other arguments as paged_decode_attention,
+ * which is paged_decode_attention_with(PKV_ATTN_AUTO, ...).  Other bits in
+ * `kernel` give PKV_ERR_INVALID_ARG.
  */
-enum pkv_attn_kernel { PKV_ATTN_AUTO = 0, PKV_ATTN_VALU = 1, PKV_ATTN_MFMA = 2 };
+enum pkv_attn_kernel {
+  PKV_ATTN_AUTO = 0,
+  PKV_ATTN_VALU = 1,
+  PKV_ATTN_MFMA = 2,
+  PKV_ATTN_KERNEL_MASK = 15,
+  /* Flag, OR-ed into the kernel choice: blocks are shared between sequences
+   * of the batch (a common prefix, forked sequences).  K/V are then read with
+   * cache-retaining loads and the rows a workgroup reads are adjacent, so
+   * the second and later readers of a block hit in cache.  Without it every
+   * block is assumed to be read once per call and K/V are streamed past the
+   * caches, which is faster for unshared caches. */
+  PKV_ATTN_CACHE_KV = 16
+};
 
 int paged_decode_attention_with(int kernel, void* out, const void* q, const void* k_pool,
                                 const void* v_pool, const int32_t* block_tables,
@@ -195,18 +212,21 @@ int paged_decode_attention_with(int kernel, void* out, const void* q, const void
 /*
  * paged_decode_attention_plan / _partitions / _merge - the three launches
  * paged_decode_attention_with(kernel, ...) makes, exposed so a caller can time
- * or schedule them separately.  Same arguments; call them in this order on one
- * stream with one workspace.
+ * or schedule them separately.  Same arguments, the same `kernel` in all three
+ * (the kernel fixes how heads are grouped, and so the plan's layout); call
+ * them in this order on one stream with one workspace.
  *  - plan: one workgroup prefix-sums the tile counts of all sequences, writes
  *    the start of every range of work and fills the rows of sequences with
  *    L <= 0 (zeros) or an over-long L (NaN);
- *  - partitions: persistent workgroups walk their ranges with the block
- *    recurrence of [arch] section 3; a sequence inside one range gets its
- *    final output, a split one leaves partial states (m, l, o);
+ *  - partitions: persistent workgroups claim ranges from a counter the plan
+ *    resets and walk them with the block recurrence of [arch] section 3; a
+ *    sequence inside one range gets its final output, a split one leaves
+ *    partial states (m, l, o).  Each plan serves one partitions launch: a
+ *    second launch needs a new plan;
  *  - merge: the range where a split sequence starts combines its partial
  *    states with the rule above and writes the output.
  */
-int paged_decode_attention_plan(void* out, const void* q, const void* k_pool,
+int paged_decode_attention_plan(int kernel, void* out, const void* q, const void* k_pool,
                                 const void* v_pool, const int32_t* block_tables,
                                 int max_blocks_per_seq, const int32_t* context_lens,
                                 int num_seqs, int num_blocks, int block_size, int num_q_heads,
@@ -220,7 +240,7 @@ int paged_decode_attention_partitions(int kernel, void* out, const void* q, cons
                                       int num_q_heads, int num_kv_heads, int head_dim,
                                       float scale, int partition_tokens, void* workspace,
                                       size_t workspace_bytes, int dtype, void* stream);
-int paged_decode_attention_merge(void* out, const void* q, const void* k_pool,
+int paged_decode_attention_merge(int kernel, void* out, const void* q, const void* k_pool,
                                  const void* v_pool, const int32_t* block_tables,
                                  int max_blocks_per_seq, const int32_t* context_lens,
                                  int num_seqs, int num_blocks, int block_size, int num_q_heads,

@@ -34,6 +34,7 @@ PKV_ERR_HIP = -5
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
 PKV_ATTN_AUTO, PKV_ATTN_VALU, PKV_ATTN_MFMA = 0, 1, 2
+PKV_ATTN_CACHE_KV = 16   # flag: blocks shared between sequences (see include/pagedkv.h)
 
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
 
@@ -62,9 +63,9 @@ _ATTN_ARGS = [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, 
               _i32, _p, _sz, _i32, _p]
 _sig("paged_decode_attention", _i32, _ATTN_ARGS)
 _sig("paged_decode_attention_with", _i32, [_i32] + _ATTN_ARGS)
-_sig("paged_decode_attention_plan", _i32, _ATTN_ARGS)
+_sig("paged_decode_attention_plan", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_attention_partitions", _i32, [_i32] + _ATTN_ARGS)
-_sig("paged_decode_attention_merge", _i32, _ATTN_ARGS)
+_sig("paged_decode_attention_merge", _i32, [_i32] + _ATTN_ARGS)
 _sig("pkv_validate_tables", _i32, [_p, _i32, _p, _i32, _i32, _i32, _intp])
 _sig("pkv_bm_create", _i32, [_i32, _i32, ctypes.POINTER(_p)])
 _sig("pkv_bm_destroy", None, [_p])
@@ -216,29 +217,30 @@ def _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partit
             int(partition_tokens), ws_ptr, workspace.numel(), dt, _stream(stream))
 
 
-def paged_decode_attention_plan(out, q, k_pool, v_pool, block_tables, context_lens, *,
+def paged_decode_attention_plan(kernel, out, q, k_pool, v_pool, block_tables, context_lens, *,
                                 scale=None, partition_tokens=0, workspace, stream=None):
-    """First launch of paged_decode_attention (work plan, empty-row fills)."""
+    """First launch of paged_decode_attention_with(kernel, ...) (work plan,
+    empty-row fills).  The three phases must be given the same kernel."""
     args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                       partition_tokens, workspace, stream)
-    _check(_lib.paged_decode_attention_plan(*args), "paged_decode_attention_plan")
+    _check(_lib.paged_decode_attention_plan(int(kernel), *args), "paged_decode_attention_plan")
 
 
 def paged_decode_attention_partitions(kernel, out, q, k_pool, v_pool, block_tables, context_lens,
                                       *, scale=None, partition_tokens=0, workspace, stream=None):
-    """Second launch of paged_decode_attention (the partition kernel)."""
+    """Second launch of paged_decode_attention_with(kernel, ...) (the partition kernel)."""
     args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                       partition_tokens, workspace, stream)
     _check(_lib.paged_decode_attention_partitions(int(kernel), *args),
            "paged_decode_attention_partitions")
 
 
-def paged_decode_attention_merge(out, q, k_pool, v_pool, block_tables, context_lens, *,
+def paged_decode_attention_merge(kernel, out, q, k_pool, v_pool, block_tables, context_lens, *,
                                  scale=None, partition_tokens=0, workspace, stream=None):
-    """Third launch of paged_decode_attention (log-sum-exp merge)."""
+    """Third launch of paged_decode_attention_with(kernel, ...) (log-sum-exp merge)."""
     args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                       partition_tokens, workspace, stream)
-    _check(_lib.paged_decode_attention_merge(*args), "paged_decode_attention_merge")
+    _check(_lib.paged_decode_attention_merge(int(kernel), *args), "paged_decode_attention_merge")
 
 
 def paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens, *, scale=None,

@@ -15,30 +15,41 @@
 // Work decomposition: three launches.
 //   attn_plan (1 workgroup): counts each live sequence's 16-token tiles,
 //     prefix-sums them, and cuts the flattened space
-//         (KV-head group, sequence, tile)
-//     into R equal ranges of T tiles, one per resident workgroup of the next
-//     launch (T can be capped by the caller's partition size).  It writes a
-//     start descriptor per range and fills the rows of empty sequences.
-//   attn_partition_* (persistent workgroups, 4 waves each): a workgroup walks
-//     its ranges; each stretch of one sequence inside a range is a segment.
-//     The four waves take the segment's tiles in turn, each with its own
-//     online-softmax state, combined in LDS at the segment's end.  A segment
+//         (quad of kw KV-head groups, sequence, tile)
+//     into claims: stage 0 gives each resident workgroup one claim of half
+//     its share, each later stage halves the claim size down to a few tiles
+//     per wave.  It writes a start descriptor per claim, the lists of split
+//     sequences for the merge, and fills the rows of empty sequences.
+//   attn_partition_* (persistent workgroups, 4 waves each): a workgroup takes
+//     claim blockIdx.x, then the next unclaimed one from an atomic counter, so
+//     compute units that stream faster take more claims and all of them
+//     finish together.  Each stretch of one sequence inside a claim is a
+//     segment.  With kw = 1 the four waves take the segment's tiles in turn
+//     and combine their online-softmax states in LDS at its end; with kw = 4
+//     each wave serves its own KV-head group over the same tiles.  A segment
 //     that is the whole sequence writes the final output; otherwise it writes
-//     a partial state (m, l, o) in a slot named by (range + sequence slot).
-//   attn_merge: the range where a split sequence starts combines the partial
-//     states of every range it covers with the log-sum-exp rule
+//     a partial state (m, l, o) in a slot named by (claim + sequence slot).
+//   attn_merge: combines the partial states of each split sequence with the
+//     log-sum-exp rule
 //         O = sum_p e^(m_p - M) o_p / sum_p e^(m_p - M) l_p.
-//   The pages stop at the per-block recurrence; the balanced split and the
-//   merge are this library's addition, to keep all 256 compute units busy
-//   whatever the length mix, without launching idle workgroups.
+//   The pages stop at the per-block recurrence; the split, the claims and
+//   the merge are this library's addition, to keep all 256 compute units
+//   busy to the end whatever the length mix.
+//
+// Cache policy: by default every block is read once per call, and K/V are
+// streamed with non-temporal loads (kw = 1).  When the caller says blocks
+// are shared between sequences (PKV_ATTN_CACHE_KV) the loads keep K/V in
+// cache and kw = 4 makes a workgroup's rows adjacent.
 //
 // Two partition kernels:
 //   attn_partition_mfma  (fp16 / bf16, D >= 32): the grouped score tile
 //     S^T[16 tokens x 16 heads] = K_tile . Q^T is one chain of D/32
-//     v_mfma_f32_16x16x32 ops whose A operand is loaded straight from the pool
-//     (each lane's 8 elements are 16 contiguous bytes of one K row).  P.V is
-//     fp32 FMA on the vector ALU: each lane owns 8 channels of one V row group
-//     and reads the probabilities of its tokens from a per-wave LDS tile.
+//     v_mfma_f32_16x16x32 ops.  K and V rows are loaded whole (every load
+//     instruction covers complete rows); K goes through a per-wave swizzled
+//     LDS tile to reach the MFMA operand layout (lane: row l % 16, channels
+//     8 * (l / 16) .. +7 of each 32-channel chunk).  P.V runs on the vector
+//     ALU as packed dot2 over token pairs: each lane owns 8 channels of one
+//     V row group and reads the probabilities of its tokens from LDS.
 //     Block ids come through scalar loads, one tile at a time.
 //   attn_partition_valu  (any dtype incl. fp32): one token row per group of
 //     D*sizeof/16 lanes, dot products reduced across the group with shuffles,
@@ -69,12 +80,32 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxGD = 1024;    // G * D bound: the cross-wave LDS buffer is 16 KiB
 constexpr int kMaxGroup = 8;    // query heads per workgroup (larger groups are split)
 constexpr int kMaxWgPerCu = 8;  // 2048 threads per CU / 256
+constexpr int kClaimsPerCu = 16;    // claim descriptors per compute unit
+constexpr int kMinClaimWaveTiles = 4;  // smallest claim: tiles per wave
+constexpr int kMaxStages = 16;      // claim-size stages (sizes halve stage to stage)
+constexpr int kMergeBlock = 8;      // partial states one merge item combines
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanLdsCum = 8192;   // prefix sums kept in LDS up to this many sequences
 
-// Plan area (int32 words): header | cum[S + 1] | desc[range_cap * 4] | task[range_cap]
-constexpr int kHdrWords = 16;
-enum Hdr { kHdrTot = 0, kHdrRanges = 1, kHdrTiles = 2, kHdrTotal = 3 };
+// Plan area (int32 words): header | cum[S + 1] | desc[range_cap][4] |
+// short tasks[kvq * S][4] | long tasks[kvq * S][4]
+// Header: totals, the claim counter and the stage table; stage k covers
+// claims [C_k, C_k+1) and tiles [X_k, X_k+1), every claim z_k tiles long but
+// the last of the final stage.  Entry ns (= number of stages) is a sentinel.
+constexpr int kHdrWords = 64;
+enum Hdr {
+  kHdrTot = 0,      // tiles of one KV-head quad (sum over sequences)
+  kHdrClaims = 1,   // number of claims
+  kHdrStages = 2,   // number of stages
+  kHdrTotal = 3,    // tiles of the whole space
+  kHdrNext = 4,     // claim counter
+  kHdrShort = 5,    // split (quad, sequence) pairs of at most kMergeBlock partials
+  kHdrLong = 6,     // split pairs of more partials
+  kHdrX = 8,        // X_k, kMaxStages + 1 entries
+  kHdrC = 8 + kMaxStages + 1,
+  kHdrZ = 8 + 2 * (kMaxStages + 1),
+};
+static_assert(kHdrZ + kMaxStages + 1 <= kHdrWords, "header");
 
 typedef const __attribute__((address_space(4))) int32_t cint;   // read with scalar loads
 
@@ -97,12 +128,17 @@ struct AttnParams {
   int num_kv_heads;
   int head_dim;
   int group;        // g = Hq / Hkv
-  int gsize;        // G: query heads per workgroup slot
+  int gsize;        // G: query heads per KV-head group
   int head_groups;  // ceil(g / G)
-  int kvg_count;    // Hkv * head_groups
-  int cap_tiles;    // 0 = balanced ranges, else at most this many tiles per range
+  int kvg_count;    // Hkv * head_groups: KV-head groups of G query heads
+  int kw;           // KV-head groups a workgroup takes together (1, 2 or 4)
+  int wpk;          // waves per KV-head group: kWaves / kw
+  int kvq_count;    // ceil(kvg_count / kw): "quads" of kw groups
+  int cap_tiles;    // 0 = no cap, else at most this many tiles per claim
   int grid;         // workgroups of the partition and merge launches
-  int range_cap;    // descriptor slots
+  int range_cap;    // claim descriptor slots
+  int off_short;    // plan-area word offsets of the merge task lists
+  int off_long;
   float scale_log2;  // scale * log2(e): scores live in log2 units
 };
 
@@ -116,6 +152,15 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every outstanding global store of the workgroup, which costs a
+// full memory round trip; none of the exchanges below needs that.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -204,7 +249,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
   if (tid == 0) carry_lds = 0;
   for (int base = 0; base < S_; base += kPlanThreads) {
     if (tid == 0) dead_count = 0;
-    __syncthreads();
+    lds_barrier();
     const int s = base + tid;
     const int L = s < S_ ? p.lens[s] : 1;
     const int nt = s < S_ ? live_tiles(L, max_len) : 0;
@@ -216,7 +261,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
       if (lane >= o) incl += v;
     }
     if (lane == 63) wave_sum[wv] = incl;
-    __syncthreads();
+    lds_barrier();
     int before = carry_lds;
     for (int i = 0; i < wv; ++i) before += wave_sum[i];
     const int excl = before + incl - nt;
@@ -232,137 +277,298 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
       S* row = (S*)p.out + (size_t)sd * row_elems;
       for (size_t i = tid; i < row_elems; i += kPlanThreads) Cvt<T>::store(row + i, fill);
     }
-    __syncthreads();
+    lds_barrier();
     if (tid == kPlanThreads - 1) carry_lds = excl + nt;
-    __syncthreads();
+    lds_barrier();
   }
   const int tot = carry_lds;
   if (tid == 0) {
     cum[S_] = tot;
     if (S_ <= kPlanLdsCum) cum_lds[S_] = tot;
   }
-  __syncthreads();
+  // Past kPlanLdsCum sequences the prefix sums are read back from memory.
+  if (S_ > kPlanLdsCum) __syncthreads(); else lds_barrier();
 
-  const int total = tot * p.kvg_count;
-  int T_ = total > 0 ? (total + p.grid - 1) / p.grid : 1;
-  if (p.cap_tiles > 0 && T_ > p.cap_tiles) T_ = p.cap_tiles;
-  const int R = total > 0 ? (total + T_ - 1) / T_ : 0;
+  // Claim schedule.  Stage 0 hands every workgroup one claim of half its
+  // share; each later stage halves the claim size, down to
+  // kMinClaimWaveTiles tiles per wave; the final stage takes what is left.
+  // A workgroup claims its next piece when it finishes one, so faster units
+  // take more pieces and the last ones are short.  The descriptor budget
+  // range_cap always leaves room for the rest at the cap size (when capped).
+  __shared__ int st_x[kMaxStages + 1], st_c[kMaxStages + 1], st_z[kMaxStages + 1];
+  __shared__ int n_stages, n_claims;
+  const int total = tot * p.kvq_count;
+  if (tid == 0) {
+    const int g = p.grid;
+    const int zmin = kMinClaimWaveTiles * p.wpk;
+    const int cap = p.cap_tiles;
+    int x = 0, c = 0, ns = 0;
+    long long z = ((long long)total + 2LL * g - 1) / (2LL * g);
+    while (x < total) {
+      const int rem = total - x;
+      int zz = (int)(z > zmin ? z : zmin);
+      if (cap > 0 && zz > cap) zz = cap;
+      const long long count_all = ((long long)rem + zz - 1) / zz;
+      bool final_stage = count_all <= g || zz <= zmin || ns == kMaxStages - 1;
+      if (!final_stage) {
+        const long long rest = (long long)rem - (long long)g * zz;
+        const long long need_after = cap > 0 ? (rest + cap - 1) / cap : 1;
+        if ((long long)c + g + need_after > p.range_cap) final_stage = true;
+      }
+      int count;
+      if (final_stage) {
+        const int budget = p.range_cap - c;   // >= 1 by construction
+        if (count_all > budget) zz = (int)(((long long)rem + budget - 1) / budget);
+        count = (rem + zz - 1) / zz;
+      } else {
+        count = g;
+      }
+      st_x[ns] = x;
+      st_c[ns] = c;
+      st_z[ns] = zz;
+      ++ns;
+      c += count;
+      x = final_stage ? total : x + g * zz;
+      z = (z + 1) / 2;
+    }
+    st_x[ns] = total;
+    st_c[ns] = c;
+    st_z[ns] = 0;
+    n_stages = ns;
+    n_claims = c;
+  }
+  lds_barrier();
+  const int ns = n_stages;
+  const int C = n_claims;
   int32_t* desc = p.plan + kHdrWords + S_ + 1;
-  int32_t* task = desc + 4 * p.range_cap;
-  for (int r = tid; r < R; r += kPlanThreads) {
-    const int x = r * T_;
-    const int kvg = x / tot;
-    const int rem = x - kvg * tot;
+  for (int c = tid; c < C; c += kPlanThreads) {
+    int k = 0;
+    while (k + 1 < ns && st_c[k + 1] <= c) ++k;
+    const int x = st_x[k] + (c - st_c[k]) * st_z[k];
+    const int size = min(st_z[k], st_x[k + 1] - x);
+    const int qd = x / tot;
+    const int rem = x - qd * tot;
     // Last sequence whose first tile is at or before rem (skips empty ones).
     int lo = 0, hi = S_;   // cum[lo] <= rem < cum[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      const int c = S_ <= kPlanLdsCum ? cum_lds[mid] : cum[mid];
-      if (c <= rem) lo = mid; else hi = mid;
+      const int cm = S_ <= kPlanLdsCum ? cum_lds[mid] : cum[mid];
+      if (cm <= rem) lo = mid; else hi = mid;
     }
     const int c_lo = S_ <= kPlanLdsCum ? cum_lds[lo] : cum[lo];
-    desc[4 * r + 0] = kvg;
-    desc[4 * r + 1] = lo;
-    desc[4 * r + 2] = rem - c_lo;
-    desc[4 * r + 3] = 0;
-    task[r] = -1;
+    desc[4 * c + 0] = qd;
+    desc[4 * c + 1] = lo;
+    desc[4 * c + 2] = rem - c_lo;
+    desc[4 * c + 3] = size;
+  }
+
+  // Merge lists.  A (quad, sequence) pair whose tiles span claims c0 .. c1
+  // with c0 < c1 is a task: its partial states sit in pairs c0 + t .. c1 + t
+  // (t = quad * S + sequence).  Tasks of at most kMergeBlock partials go to
+  // the short list (one wave each), longer ones to the long list (one
+  // workgroup each).
+  __shared__ int n_short, n_long;
+  if (tid == 0) {
+    n_short = 0;
+    n_long = 0;
+  }
+  lds_barrier();
+  auto claim_at = [&](int x) {
+    int k = 0;
+    while (k + 1 < ns && st_x[k + 1] <= x) ++k;
+    return st_c[k] + (x - st_x[k]) / st_z[k];
+  };
+  for (int t = tid; t < p.kvq_count * S_; t += kPlanThreads) {
+    const int qd = t / S_;
+    const int sq = t - qd * S_;
+    const int c_a = S_ <= kPlanLdsCum ? cum_lds[sq] : cum[sq];
+    const int c_b = S_ <= kPlanLdsCum ? cum_lds[sq + 1] : cum[sq + 1];
+    if (c_b == c_a) continue;
+    const int c0 = claim_at(qd * tot + c_a);
+    const int c1 = claim_at(qd * tot + c_b - 1);
+    if (c0 == c1) continue;
+    const int n = c1 - c0 + 1;
+    int32_t* list = p.plan + (n <= kMergeBlock ? p.off_short : p.off_long);
+    const int ti = atomicAdd(n <= kMergeBlock ? &n_short : &n_long, 1);
+    *reinterpret_cast<int4*>(list + 4 * ti) = make_int4(t, c0, n, 0);
+  }
+  lds_barrier();
+  if (tid <= ns) {
+    p.plan[kHdrX + tid] = st_x[tid];
+    p.plan[kHdrC + tid] = st_c[tid];
+    p.plan[kHdrZ + tid] = st_z[tid];
   }
   if (tid == 0) {
     p.plan[kHdrTot] = tot;
-    p.plan[kHdrRanges] = R;
-    p.plan[kHdrTiles] = T_;
+    p.plan[kHdrClaims] = C;
+    p.plan[kHdrStages] = ns;
     p.plan[kHdrTotal] = total;
+    p.plan[kHdrNext] = 0;
+    p.plan[kHdrShort] = n_short;
+    p.plan[kHdrLong] = n_long;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Range walk shared by both partition kernels.
+// Claim walk shared by both partition kernels.
 // ---------------------------------------------------------------------------
 struct Segment {
-  int kvg, kvh, h0, nh, s, L, t0, take;   // tiles [t0, t0 + take) of sequence s
-  bool final;                             // the segment is the whole sequence
-  int pair;                               // partial-state slot when not final
+  int qd, s, L, t0, take;   // tiles [t0, t0 + take) of sequence s, KV-head quad qd
+  bool final;               // the segment is the whole sequence
+  int pair;                 // partial-state slot when not final
 };
 
-template <int G, typename Fn>
-__device__ __forceinline__ void walk_ranges(const AttnParams& p, Fn&& process) {
+// Runs `process` on every segment of every claim this workgroup takes.  Claim
+// blockIdx.x first (stage 0 has one per workgroup), then the next unclaimed
+// one from the counter (taken at the start of a claim, published through
+// LDS at its end).
+template <typename Fn>
+__device__ __forceinline__ void walk_claims(const AttnParams& p, Fn&& process) {
   cint* hdr = (cint*)p.plan;
   cint* cum = (cint*)(p.plan + kHdrWords);
   cint* desc = (cint*)(p.plan + kHdrWords + p.num_seqs + 1);
-  int32_t* task_out = p.plan + kHdrWords + p.num_seqs + 1 + 4 * p.range_cap;
-  const int R = hdr[kHdrRanges];
-  const int T_ = hdr[kHdrTiles];
-  const int total = hdr[kHdrTotal];
-  for (int r = blockIdx.x; r < R; r += gridDim.x) {
-    int kvg = desc[4 * r + 0];
-    int s = desc[4 * r + 1];
-    int t0 = desc[4 * r + 2];
-    int remaining = min(T_, total - r * T_);
-    int task = -1;
-    // The range holds `remaining` tiles of the flattened space; the walk can
-    // never pass the last KV-head group, which bounds the loop for any input.
-    while (remaining > 0 && kvg < p.kvg_count) {
+  const int C = hdr[kHdrClaims];
+  __shared__ int next_lds[2];
+  int parity = 0;
+  for (int c = blockIdx.x; c < C;) {
+    int next = 0;
+    if (threadIdx.x == 0) next = atomicAdd(p.plan + kHdrNext, 1) + (int)gridDim.x;
+    int qd = desc[4 * c + 0];
+    int s = desc[4 * c + 1];
+    int t0 = desc[4 * c + 2];
+    int remaining = desc[4 * c + 3];
+    // The claim holds `remaining` tiles of the flattened space; the walk can
+    // never pass the last quad, which bounds the loop for any input.
+    while (remaining > 0 && qd < p.kvq_count) {
       const int nt = cum[s + 1] - cum[s];
       const int take = min(nt - t0, remaining);
       if (take > 0) {
         Segment sg;
-        sg.kvg = kvg;
-        sg.kvh = kvg / p.head_groups;
-        const int hg = kvg - sg.kvh * p.head_groups;
-        sg.h0 = sg.kvh * p.group + hg * G;
-        sg.nh = min(G, p.group - hg * G);
+        sg.qd = qd;
         sg.s = s;
         sg.L = ((cint*)p.lens)[s];
         sg.t0 = t0;
         sg.take = take;
         sg.final = (t0 == 0 && take == nt);
-        sg.pair = r + kvg * p.num_seqs + s;
-        if (t0 == 0 && !sg.final) task = kvg * p.num_seqs + s;
+        // Unique: along the walk both c and qd * S + s never decrease and
+        // one of them grows from one segment to the next.
+        sg.pair = c + qd * p.num_seqs + s;
         process(sg);
         remaining -= take;
       }
       t0 = 0;
       if (++s == p.num_seqs) {
         s = 0;
-        ++kvg;
+        ++qd;
       }
     }
-    if (threadIdx.x == 0) task_out[r] = task;
+    if (threadIdx.x == 0) next_lds[parity] = next;
+    // One barrier suffices: a slot is written again two claims later, after
+    // every thread has passed the barrier that follows its read.
+    lds_barrier();
+    c = __builtin_amdgcn_readfirstlane(next_lds[parity]);
+    parity ^= 1;
   }
 }
 
-// Combine the per-wave (m, l, o) states held in LDS and store the result:
-// the final output when the segment is the whole sequence, else its partial
-// state (M, weighted l, weighted o) in slot sg.pair.
+// The KV-head group a wave serves in a segment: quad qd, member kw.
+struct WaveKv {
+  bool live;   // kvg < kvg_count (the last quad may be short)
+  int kvg, kvh, h0, nh;
+};
+__device__ __forceinline__ WaveKv wave_kv(const AttnParams& p, int qd, int kw) {
+  WaveKv r;
+  r.kvg = qd * p.kw + kw;
+  r.live = r.kvg < p.kvg_count;
+  r.kvh = r.kvg / p.head_groups;
+  const int hg = r.kvg - r.kvh * p.head_groups;
+  r.h0 = r.kvh * p.group + hg * p.gsize;
+  r.nh = r.live ? min(p.gsize, p.group - hg * p.gsize) : 0;
+  return r;
+}
+
+// One output item: channels d .. d+3 of head h of KV-head group kw, from the
+// (m, l, o) states of waves w0 .. w0+n-1 held in LDS.  Writes the final
+// output when the segment is the whole sequence, else the partial state
+// (M, weighted l, weighted o) of slot (pair, kw, h).
 template <typename T, int D, int G>
-__device__ void combine_waves(const AttnParams& p, const Segment& sg, int bad,
-                              const float (*red_m)[G], const float (*red_l)[G],
-                              const float (*red_acc)[G][D]) {
+__device__ __forceinline__ void emit_item(const AttnParams& p, const Segment& sg, const WaveKv& kv,
+                                          int kw, int w0, int n, int h, int d, int bad,
+                                          const float (*red_m)[G], const float (*red_l)[G],
+                                          const float (*red_acc)[G][D]) {
   using S = typename T::storage;
-  for (int idx = threadIdx.x; idx < sg.nh * D; idx += kThreads) {
-    const int h = idx / D, d = idx % D;
-    float big_m = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) big_m = fmaxf(big_m, red_m[w][h]);
-    float num = 0.f, den = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = red_m[w][h];
-      const float wgt = mw == -INFINITY ? 0.f : fast_exp2(mw - big_m);
-      num += wgt * red_acc[w][h][d];
-      den += wgt * red_l[w][h];
+  float big_m = -INFINITY;
+  for (int j = 0; j < n; ++j) big_m = fmaxf(big_m, red_m[w0 + j][h]);
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  for (int j = 0; j < n; ++j) {
+    const float mw = red_m[w0 + j][h];
+    const float wgt = mw == -INFINITY ? 0.f : fast_exp2(mw - big_m);
+    const float4 a = *reinterpret_cast<const float4*>(&red_acc[w0 + j][h][d]);
+    num.x += wgt * a.x;
+    num.y += wgt * a.y;
+    num.z += wgt * a.z;
+    num.w += wgt * a.w;
+    den += wgt * red_l[w0 + j][h];
+  }
+  const float nan = __builtin_nanf("");
+  if (sg.final) {
+    S* o = (S*)p.out + ((size_t)sg.s * p.num_q_heads + kv.h0 + h) * D + d;
+    const float inv = 1.f / den;
+    Cvt<T>::store(o + 0, bad ? nan : num.x * inv);
+    Cvt<T>::store(o + 1, bad ? nan : num.y * inv);
+    Cvt<T>::store(o + 2, bad ? nan : num.z * inv);
+    Cvt<T>::store(o + 3, bad ? nan : num.w * inv);
+  } else {
+    const size_t slot = ((size_t)sg.pair * p.kw + kw) * G + h;
+    *reinterpret_cast<float4*>(p.ws_acc + slot * D + d) =
+        bad ? make_float4(nan, nan, nan, nan) : num;
+    if (d == 0) {
+      p.ws_m[slot] = bad ? 0.f : big_m;
+      p.ws_l[slot] = bad ? nan : den;
     }
-    if (sg.final) {
-      const size_t row = (size_t)sg.s * p.num_q_heads + sg.h0 + h;
-      Cvt<T>::store((S*)p.out + row * D + d, bad ? __builtin_nanf("") : num / den);
-    } else {
-      const size_t slot = (size_t)sg.pair * G + h;
-      p.ws_acc[slot * D + d] = bad ? __builtin_nanf("") : num;
-      if (d == 0) {
-        p.ws_m[slot] = bad ? 0.f : big_m;
-        p.ws_l[slot] = bad ? __builtin_nanf("") : den;
+  }
+}
+
+// End of a segment, after each wave has put its (m, l, o) in LDS slot w.
+// One wave per KV-head group: the wave writes its own results, no barrier.
+// Several waves per group: the workgroup combines them after a barrier.
+template <typename T, int D, int G>
+__device__ __forceinline__ void finish_segment(const AttnParams& p, const Segment& sg, int w,
+                                               int bad, const float (*red_m)[G],
+                                               const float (*red_l)[G],
+                                               const float (*red_acc)[G][D]) {
+  constexpr int D4 = D / 4;
+  if (p.wpk == 1) {
+    wave_lds_sync();
+    const WaveKv kv = wave_kv(p, sg.qd, w);
+    const int any_bad = __any(bad) ? 1 : 0;
+    if (kv.live) {
+      for (int it = threadIdx.x & 63; it < kv.nh * D4; it += 64) {
+        const int h = it / D4;
+        emit_item<T, D, G>(p, sg, kv, w, w, 1, h, (it - h * D4) * 4, any_bad, red_m, red_l, red_acc);
       }
     }
+    wave_lds_sync();   // the wave's LDS slot is rewritten by its next segment
+  } else {
+    __shared__ int bad_lds[kWaves];
+    if ((threadIdx.x & 63) == 0) bad_lds[w] = 0;
+    wave_lds_sync();
+    if (bad) bad_lds[w] = 1;
+    lds_barrier();
+    int any_bad = 0;
+#pragma unroll
+    for (int j = 0; j < kWaves; ++j) any_bad |= bad_lds[j];
+    for (int it = threadIdx.x; it < p.kw * G * D4; it += kThreads) {
+      const int kw = it / (G * D4);
+      const int r = it - kw * G * D4;
+      const int h = r / D4;
+      const WaveKv kv = wave_kv(p, sg.qd, kw);
+      if (h < kv.nh)
+        emit_item<T, D, G>(p, sg, kv, kw, kw * p.wpk, p.wpk, h, (r - h * D4) * 4, any_bad, red_m,
+                           red_l, red_acc);
+    }
+    lds_barrier();   // the LDS buffers (and bad_lds) are reused by the next segment
   }
 }
 
@@ -386,10 +592,18 @@ __device__ __forceinline__ int tile_block_ids(const AttnParams& p, cint* trow, i
   return v;
 }
 
+// K/V cache load: streamed (non-temporal) when every block is read once per
+// call, cache-retaining when blocks are shared between sequences.
+template <bool kStream>
+__device__ __forceinline__ uint4 load_kv(const char* p) {
+  if constexpr (kStream) return load16_stream(p);
+  else return load16(p);
+}
+
 // ---------------------------------------------------------------------------
 // MFMA partition kernel (fp16 / bf16).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool kStream>
 __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnParams p) {
   using S = typename T::storage;
   constexpr int KCH = D / 32;        // MFMA k-chunks of 32 channels
@@ -411,7 +625,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
   __shared__ float red_m[kWaves][G];
   __shared__ float red_l[kWaves][G];
   __shared__ __align__(16) float red_acc[kWaves][G][D];
+  // K tile of each wave, 16 rows of LPR 16-byte chunks; chunk c of row r
+  // sits at position c ^ kswz(r), which keeps both the row-wise writes and
+  // the operand-wise reads free of bank conflicts.
+  __shared__ __align__(16) uint4 k_lds[kWaves][kTile * LPR];
   uint32_t (*p2_lds)[G][kTile / 2] = reinterpret_cast<uint32_t (*)[G][kTile / 2]>(p_lds);
+  auto kswz = [](int r) {
+    if constexpr (LPR >= 16) return r & 15;          // rows of >= 256 bytes
+    else if constexpr (LPR == 8) return (r >> 1) & 7; // 128-byte rows: two per 256 bytes
+    else return (r >> 2) & 3;                         // 64-byte rows: four per 256 bytes
+  };
 
   const int lane = threadIdx.x & 63;
   // The wave index is uniform across the wave; saying so lets the tile loop
@@ -422,26 +645,31 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
   const int vc = lane % LPR;     // V: 16-byte chunk within the row
   const int vr = lane / LPR;     // V: row group, tokens TPR*vr .. TPR*vr+TPR-1
   const size_t bytes = T::bytes;
+  // KV-head group kw of the quad; with several waves per group, sub-wave sw
+  // takes every wpk-th tile.
+  const int kw = w / p.wpk;
+  const int sw = w - kw * p.wpk;
 
-  walk_ranges<G>(p, [&](const Segment& sg) {
+  walk_claims(p, [&](const Segment& sg) {
     cint* trow = (cint*)(p.tables + (size_t)sg.s * p.max_blocks);
     const int L = sg.L;
     const int last = L - 1;
+    const WaveKv kv = wave_kv(p, sg.qd, kw);
 
     // B operand: query head `col` of this group, channels 32j + 8*kgrp .. +7.
     uint4 qop[KCH];
     {
-      const S* qrow = (const S*)p.q + ((size_t)sg.s * p.num_q_heads + sg.h0 + col) * D + kgrp * 8;
+      const S* qrow = (const S*)p.q + ((size_t)sg.s * p.num_q_heads + kv.h0 + col) * D + kgrp * 8;
 #pragma unroll
       for (int j = 0; j < KCH; ++j)
-        qop[j] = col < sg.nh ? load16(qrow + 32 * j) : make_uint4(0, 0, 0, 0);
+        qop[j] = col < kv.nh ? load16(qrow + 32 * j) : make_uint4(0, 0, 0, 0);
     }
 
     int bad = 0;
     const int tile_end = sg.t0 + sg.take;
     // Register ring: while one tile is consumed the next kSlots - 1 are in
     // flight.  Loads past the segment's last tile repeat that tile.
-    uint4 kb[kSlots][KCH], vb[kSlots][TPR];
+    uint4 kb[kSlots][TPR], vb[kSlots][TPR];
     auto issue = [&](auto slot, int tile) {
       constexpr int SL = decltype(slot)::value;
       const int tc = min(tile, tile_end - 1);
@@ -453,27 +681,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
         // The whole tile lies in one block: one scalar base per pool, and
         // per-lane 32-bit offsets of rows (clamped to the last valid token).
         const int rlim = last - tb;
-        const size_t base = row_offset(id0, tb, p.log2_b, p.num_kv_heads, sg.kvh, D) * bytes;
+        const size_t base = row_offset(id0, tb, p.log2_b, p.num_kv_heads, kv.kvh, D) * bytes;
         const char* kbase = p.k_pool + base;
         const char* vbase = p.v_pool + base;
         const uint32_t rstride = (uint32_t)(p.num_kv_heads * D * bytes);
-        const uint32_t ko = (uint32_t)min(col, rlim) * rstride + kgrp * 8 * bytes;
+        // K and V alike: lane (vr, vc) reads chunk vc of rows TPR*vr + i, so
+        // every load instruction covers whole rows.
 #pragma unroll
-        for (int j = 0; j < KCH; ++j) kb[SL][j] = load16(kbase + ko + 32 * j * bytes);
-#pragma unroll
-        for (int i = 0; i < TPR; ++i)
-          vb[SL][i] = load16(vbase + (uint32_t)min(TPR * vr + i, rlim) * rstride + vc * 8 * bytes);
+        for (int i = 0; i < TPR; ++i) {
+          const uint32_t o = (uint32_t)min(TPR * vr + i, rlim) * rstride + vc * 8 * bytes;
+          kb[SL][i] = load_kv<kStream>(kbase + o);
+          vb[SL][i] = load_kv<kStream>(vbase + o);
+        }
       } else {
         auto row = [&](int t, int ch) -> size_t {
           const int tt = min(t, last);
           const int blk = __shfl(ids, (tt >> p.log2_b) - first);
-          return (row_offset(blk, tt, p.log2_b, p.num_kv_heads, sg.kvh, D) + ch) * bytes;
+          return (row_offset(blk, tt, p.log2_b, p.num_kv_heads, kv.kvh, D) + ch) * bytes;
         };
-        const size_t ko = row(tb + col, kgrp * 8);
 #pragma unroll
-        for (int j = 0; j < KCH; ++j) kb[SL][j] = load16(p.k_pool + ko + 32 * j * bytes);
-#pragma unroll
-        for (int i = 0; i < TPR; ++i) vb[SL][i] = load16(p.v_pool + row(tb + TPR * vr + i, vc * 8));
+        for (int i = 0; i < TPR; ++i) {
+          const size_t o = row(tb + TPR * vr + i, vc * 8);
+          kb[SL][i] = load_kv<kStream>(p.k_pool + o);
+          vb[SL][i] = load_kv<kStream>(p.v_pool + o);
+        }
       }
     };
 
@@ -487,9 +718,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
 
     auto consume = [&](auto slot, int tile) {
       constexpr int SL = decltype(slot)::value;
+      // K rows to LDS, then each lane takes its operand: row `col`, channels
+      // 32j + 8*kgrp .. +7 = chunk 4j + kgrp.  (The previous tile's reads of
+      // k_lds are ordered before these writes by the syncs that follow them.)
+#pragma unroll
+      for (int i = 0; i < TPR; ++i) {
+        const int r = TPR * vr + i;
+        k_lds[w][r * LPR + (vc ^ kswz(r))] = kb[SL][i];
+      }
+      wave_lds_sync();
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < KCH; ++j) sc = Mfma<T>::run(kb[SL][j], qop[j], sc);
+      for (int j = 0; j < KCH; ++j)
+        sc = Mfma<T>::run(k_lds[w][col * LPR + ((4 * j + kgrp) ^ kswz(col))], qop[j], sc);
       const int tb = tile * kTile;
       float sv[4];
       float mt = -INFINITY;
@@ -579,35 +820,36 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    int tile = sg.t0 + w;
-    if (tile < tile_end) {
+    const int step = p.wpk;
+    int tile = sg.t0 + sw;
+    if (kv.live && tile < tile_end) {
       if constexpr (kSlots == 3) {
         issue(I0{}, tile);
-        issue(I1{}, tile + kWaves);
+        issue(I1{}, tile + step);
         while (true) {
-          issue(I2{}, tile + 2 * kWaves);
+          issue(I2{}, tile + 2 * step);
           consume(I0{}, tile);
-          tile += kWaves;
+          tile += step;
           if (tile >= tile_end) break;
-          issue(I0{}, tile + 2 * kWaves);
+          issue(I0{}, tile + 2 * step);
           consume(I1{}, tile);
-          tile += kWaves;
+          tile += step;
           if (tile >= tile_end) break;
-          issue(I1{}, tile + 2 * kWaves);
+          issue(I1{}, tile + 2 * step);
           consume(I2{}, tile);
-          tile += kWaves;
+          tile += step;
           if (tile >= tile_end) break;
         }
       } else {
         issue(I0{}, tile);
         while (true) {
-          issue(I1{}, tile + kWaves);
+          issue(I1{}, tile + step);
           consume(I0{}, tile);
-          tile += kWaves;
+          tile += step;
           if (tile >= tile_end) break;
-          issue(I0{}, tile + kWaves);
+          issue(I0{}, tile + step);
           consume(I1{}, tile);
-          tile += kWaves;
+          tile += step;
           if (tile >= tile_end) break;
         }
       }
@@ -635,16 +877,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
       red_m[w][col] = m_run;
       red_l[w][col] = l_run;
     }
-    const int any_bad = __syncthreads_or(bad);
-    combine_waves<T, D, G>(p, sg, any_bad, red_m, red_l, red_acc);
-    __syncthreads();   // the LDS buffers are reused by the next segment
+    finish_segment<T, D, G>(p, sg, w, bad, red_m, red_l, red_acc);
   });
 }
 
 // ---------------------------------------------------------------------------
 // Vector-ALU partition kernel (any dtype).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool kStream>
 __global__ __launch_bounds__(kThreads, 2) void attn_partition_valu(const AttnParams p) {
   using S = typename T::storage;
   constexpr int E = 16 / T::bytes;   // elements per 16-byte chunk
@@ -661,14 +901,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_valu(const AttnPar
   const int c = lane % LPR;   // chunk of the row
   const int r = lane / LPR;   // token slot within the wave step
   const size_t bytes = T::bytes;
+  const int kw = w / p.wpk;
+  const int sw = w - kw * p.wpk;
 
-  walk_ranges<G>(p, [&](const Segment& sg) {
+  walk_claims(p, [&](const Segment& sg) {
     const int32_t* trow = p.tables + (size_t)sg.s * p.max_blocks;
+    const WaveKv kv = wave_kv(p, sg.qd, kw);
     float qf[G][E];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      if (h < sg.nh) {
-        const S* qrow = (const S*)p.q + ((size_t)sg.s * p.num_q_heads + sg.h0 + h) * D + c * E;
+      if (h < kv.nh) {
+        const S* qrow = (const S*)p.q + ((size_t)sg.s * p.num_q_heads + kv.h0 + h) * D + c * E;
         Cvt<T>::unpack(load16(qrow), qf[h]);
 #pragma unroll
         for (int e = 0; e < E; ++e) qf[h][e] *= p.scale_log2;
@@ -689,8 +932,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_valu(const AttnPar
 
     int bad = 0;
     const int tok0 = sg.t0 * kTile;
-    const int tok_end = min(sg.L, (sg.t0 + sg.take) * kTile);
-    for (int base = tok0 + w * RPL; base < tok_end; base += RPL * kWaves) {
+    const int tok_end = kv.live ? min(sg.L, (sg.t0 + sg.take) * kTile) : tok0;
+    for (int base = tok0 + sw * RPL; base < tok_end; base += RPL * p.wpk) {
       const int t = base + r;
       const bool valid = t < tok_end;
       const int tt = valid ? t : tok_end - 1;
@@ -699,10 +942,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_valu(const AttnPar
         bad = 1;
         blk = 0;
       }
-      const size_t off = (row_offset(blk, tt, p.log2_b, p.num_kv_heads, sg.kvh, D) + c * E) * bytes;
+      const size_t off = (row_offset(blk, tt, p.log2_b, p.num_kv_heads, kv.kvh, D) + c * E) * bytes;
       float kf[E], vf[E];
-      Cvt<T>::unpack(load16(p.k_pool + off), kf);
-      Cvt<T>::unpack(load16(p.v_pool + off), vf);
+      Cvt<T>::unpack(load_kv<kStream>(p.k_pool + off), kf);
+      Cvt<T>::unpack(load_kv<kStream>(p.v_pool + off), vf);
       float sh[G];
       bool grow = false;
 #pragma unroll
@@ -764,104 +1007,190 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_valu(const AttnPar
         red_l[w][h] = l[h];
       }
     }
-    const int any_bad = __syncthreads_or(bad);
-    combine_waves<T, D, G>(p, sg, any_bad, red_m, red_l, red_acc);
-    __syncthreads();
+    finish_segment<T, D, G>(p, sg, w, bad, red_m, red_l, red_acc);
   });
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge: the range where a split sequence starts combines the
-// partial states of all ranges the sequence covers.
+// Log-sum-exp merge of the partial states of split sequences,
+//     M = max_i m_i,  l = sum_i e^(m_i - M) l_i,  o = sum_i e^(m_i - M) o_i,
+// out = o / l, for each (task, KV-head group of the quad).  Short tasks (at
+// most kMergeBlock partials) take one wave with all of its loads in flight
+// together; long tasks take a workgroup whose waves combine chunks of
+// kMergeBlock in turn and then merge their four states through LDS.
 // ---------------------------------------------------------------------------
+struct MergeState {
+  float run_m;              // running maximum of head lh (per lane)
+  float den;                // weighted l of partial (li, lh); summed over li by the caller
+  float4 acc[kMaxGD / 256]; // weighted o, channels 4 * lane + 256 * j
+};
+
+__device__ __forceinline__ void merge_init(MergeState& st) {
+  st.run_m = -INFINITY;
+  st.den = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxGD / 256; ++j) st.acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// Adds the states of pairs first .. first + count - 1 (count <= kMergeBlock)
+// of KV-head group kw_i to st.  Slot of pair q, head h: (q * kw + kw_i) * G + h.
+__device__ __forceinline__ void merge_block(const AttnParams& p, size_t first, int count,
+                                            int kw_i, int nh, MergeState& st) {
+  constexpr int kF4 = kMaxGD / 256;
+  const int G = p.gsize, D = p.head_dim, KW = p.kw;
+  const int lane = threadIdx.x & 63;
+  const int lh = lane & (G - 1);
+  const int li = lane / G;
+  const int nf = nh * D;
+  const bool ok = li < count && lh < nh;
+  const size_t slot = ((first + li) * KW + kw_i) * G + lh;
+  const float mi = ok ? p.ws_m[slot] : -INFINITY;
+  const float lv = ok ? p.ws_l[slot] : 0.f;
+  float4 x[kMergeBlock][kF4];
+#pragma unroll
+  for (int i = 0; i < kMergeBlock; ++i)
+#pragma unroll
+    for (int j = 0; j < kF4; ++j) {
+      const int f = 4 * lane + 256 * j;
+      x[i][j] = (i < count && f < nf)
+                    ? *reinterpret_cast<const float4*>(p.ws_acc + ((first + i) * KW + kw_i) * G * D + f)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  float cm = mi;
+  for (int o = G; o < 64; o <<= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
+  const float mn = fmaxf(st.run_m, cm);
+  const float so = st.run_m == -INFINITY ? 0.f : fast_exp2(st.run_m - mn);
+  st.run_m = mn;
+  const float wi = mi == -INFINITY ? 0.f : fast_exp2(mi - mn);
+  st.den = st.den * so + wi * lv;
+#pragma unroll
+  for (int j = 0; j < kF4; ++j) {
+    const int f = 4 * lane + 256 * j;
+    const int h = min(f / D, G - 1);
+    const float sj = __shfl(so, h);
+    float4 a = st.acc[j];
+    a.x *= sj; a.y *= sj; a.z *= sj; a.w *= sj;
+#pragma unroll
+    for (int i = 0; i < kMergeBlock; ++i) {
+      const float wj = __shfl(wi, i * G + h);
+      a.x += wj * x[i][j].x;
+      a.y += wj * x[i][j].y;
+      a.z += wj * x[i][j].z;
+      a.w += wj * x[i][j].w;
+    }
+    st.acc[j] = a;
+  }
+}
+
+// Sum of den over the partials of each head (lanes with the same lh).
+__device__ __forceinline__ float head_den(const MergeState& st, int G) {
+  float d = st.den;
+  for (int o = G; o < 64; o <<= 1) d += __shfl_xor(d, o);
+  return d;
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(const AttnParams& p, int s, int head, int d, float4 v) {
+  using S = typename T::storage;
+  S* o = (S*)p.out + ((size_t)s * p.num_q_heads + head) * p.head_dim + d;
+  Cvt<T>::store(o + 0, v.x);
+  Cvt<T>::store(o + 1, v.y);
+  Cvt<T>::store(o + 2, v.z);
+  Cvt<T>::store(o + 3, v.w);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
-  using S = typename T::storage;
-  constexpr int kChunk = 64;                    // partial states staged per pass
-  constexpr int kItems = kMaxGD / kThreads;     // (head, channel) outputs per thread
-  __shared__ float w_lds[kChunk][kMaxGroup];    // m of each partial, then its weight
-  __shared__ float l_lds[kChunk][kMaxGroup];
-  __shared__ float run_m[kMaxGroup], run_den[kMaxGroup], rescale[kMaxGroup];
+  constexpr int kF4 = kMaxGD / 256;
+  __shared__ float m_lds[kWaves][kMaxGroup];
+  __shared__ float l_lds[kWaves][kMaxGroup];
+  __shared__ __align__(16) float acc_lds[kWaves][kMaxGD];
   cint* hdr = (cint*)p.plan;
-  cint* cum = (cint*)(p.plan + kHdrWords);
-  cint* task_in = (cint*)(p.plan + kHdrWords + p.num_seqs + 1 + 4 * p.range_cap);
-  const int tot = hdr[kHdrTot];
-  const int R = hdr[kHdrRanges];
-  const int T_ = hdr[kHdrTiles];
-  const int G = p.gsize, D = p.head_dim;
-  const int tid = threadIdx.x;
-  for (int r = blockIdx.x; r < R; r += gridDim.x) {
-    const int task = task_in[r];
-    if (task < 0) continue;
-    const int kvg = task / p.num_seqs;
-    const int s = task - kvg * p.num_seqs;
-    const int n = (kvg * tot + cum[s + 1] - 1) / T_ - r + 1;   // ranges covered
-    const int kvh = kvg / p.head_groups;
-    const int hg = kvg - kvh * p.head_groups;
-    const int h0 = kvh * p.group + hg * G;
-    const int nh = min(G, p.group - hg * G);
-    const size_t first_slot = (size_t)(r + task) * G;          // slot of (range r, head 0)
-    float num[kItems];
-#pragma unroll
-    for (int k = 0; k < kItems; ++k) num[k] = 0.f;
-    if (tid < nh) {
-      run_m[tid] = -INFINITY;
-      run_den[tid] = 0.f;
-    }
-    for (int c0 = 0; c0 < n; c0 += kChunk) {
-      const int cn = min(kChunk, n - c0);
-      __syncthreads();
-      for (int t = tid; t < cn * nh; t += kThreads) {
-        const int i = t / nh, h = t - i * nh;
-        const size_t slot = first_slot + (size_t)(c0 + i) * G + h;
-        w_lds[i][h] = p.ws_m[slot];
-        l_lds[i][h] = p.ws_l[slot];
-      }
-      __syncthreads();
-      if (tid < nh) {
-        const int h = tid;
-        float cm = -INFINITY;
-        for (int i = 0; i < cn; ++i) cm = fmaxf(cm, w_lds[i][h]);
-        const float mn = fmaxf(run_m[h], cm);
-        const float so = run_m[h] == -INFINITY ? 0.f : fast_exp2(run_m[h] - mn);
-        float den = run_den[h] * so;
-        for (int i = 0; i < cn; ++i) {
-          const float wt = fast_exp2(w_lds[i][h] - mn);
-          w_lds[i][h] = wt;
-          den += wt * l_lds[i][h];
-        }
-        run_m[h] = mn;
-        run_den[h] = den;
-        rescale[h] = so;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int k = 0; k < kItems; ++k) {
-        const int idx = tid + k * kThreads;
-        if (idx < nh * D) {
-          const int h = idx / D, d = idx - (idx / D) * D;
-          const float* src = p.ws_acc + (first_slot + (size_t)c0 * G + h) * D + d;
-          float a = num[k] * rescale[h];
-          int i = 0;
-          for (; i + 4 <= cn; i += 4) {
-            const float x0 = src[(size_t)(i + 0) * G * D], x1 = src[(size_t)(i + 1) * G * D];
-            const float x2 = src[(size_t)(i + 2) * G * D], x3 = src[(size_t)(i + 3) * G * D];
-            a += w_lds[i][h] * x0 + w_lds[i + 1][h] * x1 + w_lds[i + 2][h] * x2 + w_lds[i + 3][h] * x3;
-          }
-          for (; i < cn; ++i) a += w_lds[i][h] * src[(size_t)i * G * D];
-          num[k] = a;
-        }
-      }
+  cint* short_list = (cint*)(p.plan + p.off_short);
+  cint* long_list = (cint*)(p.plan + p.off_long);
+  const int G = p.gsize, D = p.head_dim, KW = p.kw;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+
+  // Long tasks: one workgroup per (task, KV-head group).
+  const int n_long = hdr[kHdrLong] * KW;
+  for (int u = blockIdx.x; u < n_long; u += gridDim.x) {
+    const int ti = u / KW;
+    const int kw_i = u - ti * KW;
+    const int t = long_list[4 * ti + 0];
+    const int c0 = long_list[4 * ti + 1];
+    const int n = long_list[4 * ti + 2];
+    const int qd = t / p.num_seqs;
+    const int s = t - qd * p.num_seqs;
+    const WaveKv kv = wave_kv(p, qd, kw_i);
+    if (!kv.live) continue;   // uniform over the workgroup
+    const size_t pair0 = (size_t)c0 + t;
+    MergeState st;
+    merge_init(st);
+    for (int i0 = wv * kMergeBlock; i0 < n; i0 += kWaves * kMergeBlock)
+      merge_block(p, pair0 + i0, min(kMergeBlock, n - i0), kw_i, kv.nh, st);
+    const float den = head_den(st, G);
+    if (lane < kv.nh) {
+      m_lds[wv][lane] = st.run_m;
+      l_lds[wv][lane] = den;
     }
 #pragma unroll
-    for (int k = 0; k < kItems; ++k) {
-      const int idx = tid + k * kThreads;
-      if (idx < nh * D) {
-        const int h = idx / D, d = idx - (idx / D) * D;
-        Cvt<T>::store((S*)p.out + ((size_t)s * p.num_q_heads + h0 + h) * D + d, num[k] / run_den[h]);
-      }
+    for (int j = 0; j < kF4; ++j) {
+      const int f = 4 * lane + 256 * j;
+      if (f < kv.nh * D) *reinterpret_cast<float4*>(&acc_lds[wv][f]) = st.acc[j];
     }
-    __syncthreads();   // LDS is reused by the next task
+    lds_barrier();
+    for (int f = 4 * threadIdx.x; f < kv.nh * D; f += 4 * kThreads) {
+      const int h = f / D;
+      float big = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) big = fmaxf(big, m_lds[w][h]);
+      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+      float dsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = m_lds[w][h];
+        const float wt = mw == -INFINITY ? 0.f : fast_exp2(mw - big);
+        const float4 a = *reinterpret_cast<const float4*>(&acc_lds[w][f]);
+        num.x += wt * a.x;
+        num.y += wt * a.y;
+        num.z += wt * a.z;
+        num.w += wt * a.w;
+        dsum += wt * l_lds[w][h];
+      }
+      const float inv = 1.f / dsum;
+      store4<T>(p, s, kv.h0 + h, f - h * D,
+                make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv));
+    }
+    lds_barrier();   // the LDS buffers are reused by the next task
+  }
+
+  // Short tasks: one wave per (task, KV-head group).
+  const int n_short = hdr[kHdrShort] * KW;
+  for (int it = blockIdx.x * kWaves + wv; it < n_short; it += gridDim.x * kWaves) {
+    const int ti = it / KW;
+    const int kw_i = it - ti * KW;
+    const int t = short_list[4 * ti + 0];
+    const int c0 = short_list[4 * ti + 1];
+    const int n = short_list[4 * ti + 2];
+    const int qd = t / p.num_seqs;
+    const int s = t - qd * p.num_seqs;
+    const WaveKv kv = wave_kv(p, qd, kw_i);
+    if (!kv.live) continue;
+    MergeState st;
+    merge_init(st);
+    merge_block(p, (size_t)c0 + t, n, kw_i, kv.nh, st);
+    const float den = head_den(st, G);
+#pragma unroll
+    for (int j = 0; j < kF4; ++j) {
+      const int f = 4 * lane + 256 * j;
+      const int h = min(f / D, G - 1);
+      const float inv = 1.f / __shfl(den, h);
+      if (f < kv.nh * D)
+        store4<T>(p, s, kv.h0 + h, f - h * D,
+                  make_float4(st.acc[j].x * inv, st.acc[j].y * inv, st.acc[j].z * inv,
+                              st.acc[j].w * inv));
+    }
   }
 }
 
@@ -871,20 +1200,27 @@ __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t m_off, l_off, acc_off, total;
+  size_t off_short, off_long, plan_words;   // plan-area words
+  size_t m_off, l_off, acc_off, total;         // bytes
 };
 
 // Workspace of a call: the plan words, then the partial states.  Pair slots:
-// one per (range, sequence slot) along the monotone walk, at most
-// range_cap + kvg_count * S of them, G heads each.
-inline WsLayout ws_layout(int num_seqs, int kvg_count, int gsize, int head_dim, int range_cap) {
+// one per (claim, quad-sequence) along the monotone walk, at most
+// range_cap + kvq_count * S of them, kw * G heads each.  The two merge task
+// lists hold at most kvq_count * S entries each (16-byte aligned).
+inline WsLayout ws_layout(int num_seqs, int kvq_count, int pair_heads, int head_dim,
+                          int range_cap) {
   WsLayout w;
-  const size_t plan_words = kHdrWords + (size_t)num_seqs + 1 + 5 * (size_t)range_cap;
-  const size_t pairs = (size_t)range_cap + (size_t)kvg_count * num_seqs;
+  const size_t pairs_q = (size_t)kvq_count * num_seqs;
+  w.off_short = (kHdrWords + (size_t)num_seqs + 1 + 4 * (size_t)range_cap + 3) & ~(size_t)3;
+  w.off_long = w.off_short + 4 * pairs_q;
+  const size_t plan_words = w.off_long + 4 * pairs_q;
+  w.plan_words = plan_words;
+  const size_t heads = ((size_t)range_cap + pairs_q) * pair_heads;
   w.m_off = align256(plan_words * 4);
-  w.l_off = w.m_off + align256(pairs * gsize * 4);
-  w.acc_off = w.l_off + align256(pairs * gsize * 4);
-  w.total = w.acc_off + align256(pairs * gsize * head_dim * 4);
+  w.l_off = w.m_off + align256(heads * 4);
+  w.acc_off = w.l_off + align256(heads * 4);
+  w.total = w.acc_off + align256(heads * head_dim * 4);
   return w;
 }
 
@@ -936,45 +1272,51 @@ inline int pow2_at_least(int x) {
   return r;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool kStream>
 const void* partition_fn(int family) {
   if (family == kFamilyMfma) {
     if constexpr (!std::is_same<T, F32>::value && D >= 32 && G * D <= kMaxGD && (D < 256 || G <= 2))
-      return reinterpret_cast<const void*>(&attn_partition_mfma<T, D, G>);
+      return reinterpret_cast<const void*>(&attn_partition_mfma<T, D, G, kStream>);
   } else {
     if constexpr (G * D <= kMaxGD && (std::is_same<T, F32>::value || G <= 4))
-      return reinterpret_cast<const void*>(&attn_partition_valu<T, D, G>);
+      return reinterpret_cast<const void*>(&attn_partition_valu<T, D, G, kStream>);
   }
   return nullptr;
 }
 
-template <typename T, int D>
+template <typename T, int D, bool kStream>
 const void* partition_fn_g(int family, int G) {
   switch (G) {
-    case 1: return partition_fn<T, D, 1>(family);
-    case 2: return partition_fn<T, D, 2>(family);
-    case 4: return partition_fn<T, D, 4>(family);
-    default: return partition_fn<T, D, 8>(family);
+    case 1: return partition_fn<T, D, 1, kStream>(family);
+    case 2: return partition_fn<T, D, 2, kStream>(family);
+    case 4: return partition_fn<T, D, 4, kStream>(family);
+    default: return partition_fn<T, D, 8, kStream>(family);
   }
 }
 
-template <typename T>
+template <typename T, bool kStream>
 const void* partition_fn_d(int family, int D, int G) {
   switch (D) {
-    case 16: return partition_fn_g<T, 16>(family, G);
-    case 32: return partition_fn_g<T, 32>(family, G);
-    case 64: return partition_fn_g<T, 64>(family, G);
-    case 128: return partition_fn_g<T, 128>(family, G);
-    default: return partition_fn_g<T, 256>(family, G);
+    case 16: return partition_fn_g<T, 16, kStream>(family, G);
+    case 32: return partition_fn_g<T, 32, kStream>(family, G);
+    case 64: return partition_fn_g<T, 64, kStream>(family, G);
+    case 128: return partition_fn_g<T, 128, kStream>(family, G);
+    default: return partition_fn_g<T, 256, kStream>(family, G);
   }
 }
 
-inline const void* pick_partition(int family, int dtype, int D, int G) {
+template <bool kStream>
+const void* pick_partition_s(int family, int dtype, int D, int G) {
   switch (dtype) {
-    case PKV_F32: return partition_fn_d<F32>(family, D, G);
-    case PKV_F16: return partition_fn_d<F16>(family, D, G);
-    default: return partition_fn_d<BF16>(family, D, G);
+    case PKV_F32: return partition_fn_d<F32, kStream>(family, D, G);
+    case PKV_F16: return partition_fn_d<F16, kStream>(family, D, G);
+    default: return partition_fn_d<BF16, kStream>(family, D, G);
   }
+}
+
+inline const void* pick_partition(int family, int dtype, int D, int G, bool stream) {
+  return stream ? pick_partition_s<true>(family, dtype, D, G)
+                : pick_partition_s<false>(family, dtype, D, G);
 }
 
 enum Phase { kPhasePlan = 1, kPhasePartitions = 2, kPhaseMerge = 4, kPhaseAll = 7 };
@@ -996,7 +1338,10 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
       num_q_heads % num_kv_heads != 0 || !(scale == scale) || scale == INFINITY ||
       scale == -INFINITY)
     return PKV_ERR_INVALID_ARG;
-  if (kernel < PKV_ATTN_AUTO || kernel > PKV_ATTN_MFMA) return PKV_ERR_INVALID_ARG;
+  if ((kernel & ~(PKV_ATTN_KERNEL_MASK | PKV_ATTN_CACHE_KV)) != 0) return PKV_ERR_INVALID_ARG;
+  const bool cache_kv = (kernel & PKV_ATTN_CACHE_KV) != 0;
+  kernel &= PKV_ATTN_KERNEL_MASK;
+  if (kernel > PKV_ATTN_MFMA) return PKV_ERR_INVALID_ARG;
   if (partition_tokens < 0 || (partition_tokens > 0 && partition_tokens % kTile != 0))
     return PKV_ERR_INVALID_ARG;
   const long long max_len = (long long)max_blocks_per_seq * block_size;
@@ -1020,17 +1365,22 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
 
-  const void* fn = pick_partition(family, dtype, head_dim, G);
+  const void* fn = pick_partition(family, dtype, head_dim, G, !cache_kv);
   if (!fn) return PKV_ERR_UNSUPPORTED;
-  // The merge and plan must size the same layout whichever kernel runs, so
-  // the grid is the largest one the device holds of any partition kernel.
   const int grid = device_cu_count() * resident_per_cu(fn);
+  // Streamed K/V: the four waves of a workgroup take turns on the tiles of
+  // one KV-head group.  Shared (cached) K/V: they serve four KV-head groups
+  // of the same tokens when there are that many, so the rows a workgroup
+  // reads are adjacent and a block read by several sequences stays hot.
+  const int kw = !cache_kv ? 1 : kvg >= kWaves ? kWaves : (kvg >= 2 ? 2 : 1);
+  const long long kvq = (kvg + kw - 1) / kw;
   const int cap_tiles = partition_tokens / kTile;
-  long long range_cap = (long long)device_cu_count() * kMaxWgPerCu;
+  long long range_cap = (long long)device_cu_count() * kClaimsPerCu;
   if (cap_tiles > 0)
-    range_cap += kvg * num_seqs * ((max_len + partition_tokens - 1) / partition_tokens);
+    range_cap += kvq * num_seqs * ((max_len + partition_tokens - 1) / partition_tokens);
   if (range_cap >= (1LL << 30)) return PKV_ERR_INVALID_ARG;
-  const WsLayout ws = ws_layout(num_seqs, (int)kvg, G, head_dim, (int)range_cap);
+  const WsLayout ws = ws_layout(num_seqs, (int)kvq, kw * G, head_dim, (int)range_cap);
+  if (ws.plan_words >= (1ULL << 31)) return PKV_ERR_INVALID_ARG;   // 32-bit word offsets
   if (!workspace || workspace_bytes < ws.total || ((uintptr_t)workspace & 255) != 0)
     return PKV_ERR_WORKSPACE;
 
@@ -1057,9 +1407,14 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
   p.gsize = G;
   p.head_groups = head_groups;
   p.kvg_count = (int)kvg;
+  p.kw = kw;
+  p.wpk = kWaves / kw;
+  p.kvq_count = (int)kvq;
   p.cap_tiles = cap_tiles;
   p.grid = grid;
   p.range_cap = (int)range_cap;
+  p.off_short = (int)ws.off_short;
+  p.off_long = (int)ws.off_long;
   p.scale_log2 = scale * kLog2e;
   L->part_fn = fn;
   return PKV_OK;
@@ -1116,17 +1471,22 @@ extern "C" size_t paged_decode_workspace_bytes(int num_seqs, int num_q_heads, in
   if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_context_len < 0 ||
       partition_tokens < 0)
     return 0;
-  // Bounds that hold for every KV head count: G <= 8 and kvg_count * G <= 2 * Hq.
-  long long range_cap = (long long)pkv::device_cu_count() * pkv::kMaxWgPerCu;
-  const long long kvg_bound = 2LL * num_q_heads;
-  if (partition_tokens > 0)
-    range_cap += kvg_bound * num_seqs *
-                 (((long long)max_context_len + partition_tokens - 1) / partition_tokens);
+  // Bounds that hold for every KV head count: kvq_count <= kvg_count <= Hq,
+  // kw * G <= 4 * 8 and kvq_count * kw * G <= (kvg_count + 3) * G <= 2 * Hq + 24.
+  const long long parts = partition_tokens > 0
+      ? ((long long)max_context_len + partition_tokens - 1) / partition_tokens : 0;
+  const long long range_cap = (long long)pkv::device_cu_count() * pkv::kClaimsPerCu +
+                              (long long)num_q_heads * num_seqs * parts;
   if (range_cap >= (1LL << 30)) return 0;
-  const size_t plan_words = pkv::kHdrWords + (size_t)num_seqs + 1 + 5 * (size_t)range_cap;
-  const size_t pair_heads = (size_t)range_cap * pkv::kMaxGroup + (size_t)kvg_bound * num_seqs;
-  return pkv::align256(plan_words * 4) + 2 * pkv::align256(pair_heads * 4) +
-         pkv::align256(pair_heads * head_dim * 4);
+  // Plan words: header, cum, descriptors, then the two merge task lists of
+  // at most kvq_count * S <= Hq * S entries each.
+  const size_t plan_words = pkv::kHdrWords + (size_t)num_seqs + 4 + 4 * (size_t)range_cap +
+                            8 * (size_t)num_q_heads * num_seqs;
+  const size_t heads = (size_t)pkv::device_cu_count() * pkv::kClaimsPerCu * pkv::kWaves *
+                           pkv::kMaxGroup +
+                       (size_t)(2LL * num_q_heads + 24) * num_seqs * (size_t)(1 + parts);
+  return pkv::align256(plan_words * 4) + 2 * pkv::align256(heads * 4) +
+         pkv::align256(heads * head_dim * 4);
 }
 
 #define PKV_ATTN_ARGS                                                                      \
@@ -1148,14 +1508,14 @@ extern "C" int paged_decode_attention_with(int kernel, PKV_ATTN_ARGS) {
   return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, PKV_ATTN_PASS);
 }
 
-extern "C" int paged_decode_attention_plan(PKV_ATTN_ARGS) {
-  return pkv::decode_attention_impl(pkv::kPhasePlan, PKV_ATTN_AUTO, PKV_ATTN_PASS);
+extern "C" int paged_decode_attention_plan(int kernel, PKV_ATTN_ARGS) {
+  return pkv::decode_attention_impl(pkv::kPhasePlan, kernel, PKV_ATTN_PASS);
 }
 
 extern "C" int paged_decode_attention_partitions(int kernel, PKV_ATTN_ARGS) {
   return pkv::decode_attention_impl(pkv::kPhasePartitions, kernel, PKV_ATTN_PASS);
 }
 
-extern "C" int paged_decode_attention_merge(PKV_ATTN_ARGS) {
-  return pkv::decode_attention_impl(pkv::kPhaseMerge, PKV_ATTN_AUTO, PKV_ATTN_PASS);
+extern "C" int paged_decode_attention_merge(int kernel, PKV_ATTN_ARGS) {
+  return pkv::decode_attention_impl(pkv::kPhaseMerge, kernel, PKV_ATTN_PASS);
 }

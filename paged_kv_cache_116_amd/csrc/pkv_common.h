@@ -101,6 +101,14 @@ template <> struct Cvt<F16> {
 };
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+// Streaming load (non-temporal hint): for data read once per call, such as
+// the K/V cache in decode attention; it keeps the caches for reused data and
+// lets the memory system run closer to peak.
+__device__ __forceinline__ uint4 load16_stream(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 inline int log2_exact(int x) {

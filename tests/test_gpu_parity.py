@@ -215,7 +215,10 @@ def test_attention_matches_oracle(cid, seed_off):
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
 @pytest.mark.parametrize("kernel", ["valu", "mfma"])
 @pytest.mark.parametrize("part", [0, 16, 48, 512])
-def test_attention_kernels_and_partitions(cid, kernel, part):
+@pytest.mark.parametrize("cache_kv", [False, True])
+def test_attention_kernels_and_partitions(cid, kernel, part, cache_kv):
+    # cache_kv selects the cache-retaining loads and the four-groups-per-
+    # workgroup layout; without it K/V are streamed and waves share a group.
     kw = dict(SMALL[cid])
     if cid == 5:
         kw["block_size"] = {0: 8, 16: 32, 48: 8, 512: 32}[part]
@@ -223,8 +226,40 @@ def test_attention_kernels_and_partitions(cid, kernel, part):
     dev = to_dev(w)
     ref = oracle_step(w, w.k_pool, w.v_pool)
     k = pkv.PKV_ATTN_VALU if kernel == "valu" else pkv.PKV_ATTN_MFMA
+    if cache_kv:
+        k |= pkv.PKV_ATTN_CACHE_KV
     out = run_step(w, dev, partition_tokens=part, kernel=k)
-    check_close(out, ref, w.dtype, f"config{cid} {kernel} P={part} B={w.block_size}")
+    check_close(out, ref, w.dtype,
+                f"config{cid} {kernel} P={part} B={w.block_size} cache_kv={cache_kv}")
+
+
+@pytest.mark.parametrize("kernel", ["auto", "valu", "mfma", "mfma_cached"])
+@pytest.mark.parametrize("part", [0, 48])
+def test_phased_entry_points_match_oracle(kernel, part):
+    # The plan, partition and merge launches called one by one, as a caller
+    # that times or schedules them does.  g = 8 query heads per KV head: the
+    # vector-ALU kernel groups 4 of them, the matrix-core kernel 8, so a phase
+    # given another kernel's grouping would read the wrong plan.
+    w = workloads.make_workload(3, **SMALL[3])
+    dev = to_dev(w)
+    ref = oracle_step(w, w.k_pool, w.v_pool)
+    k = {"auto": pkv.PKV_ATTN_AUTO, "valu": pkv.PKV_ATTN_VALU, "mfma": pkv.PKV_ATTN_MFMA,
+         "mfma_cached": pkv.PKV_ATTN_MFMA | pkv.PKV_ATTN_CACHE_KV}[kernel]
+    pkv.paged_kv_append(dev["k_pool"], dev["v_pool"], dev["k_new"], dev["v_new"], dev["tables"],
+                        dev["lens_pre"])
+    out = torch.empty_like(dev["q"])
+    ws = torch.empty(pkv.paged_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim,
+                                                      w.max_blocks * w.block_size, part),
+                     dtype=torch.uint8, device="cuda")
+    args = (out, dev["q"], dev["k_pool"], dev["v_pool"], dev["tables"], dev["lens"])
+    kw = dict(scale=w.scale, partition_tokens=part, workspace=ws)
+    for _ in range(2):   # a second round reuses the workspace
+        out.fill_(7.0)
+        pkv.paged_decode_attention_plan(k, *args, **kw)
+        pkv.paged_decode_attention_partitions(k, *args, **kw)
+        pkv.paged_decode_attention_merge(k, *args, **kw)
+        torch.cuda.synchronize()
+        check_close(out, ref, w.dtype, f"phased {kernel} P={part}")
 
 
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64, 128])
@@ -364,10 +399,12 @@ def test_deterministic_and_relabelling_invariant():
     assert torch.equal(a.view(torch.int16), c.view(torch.int16))
 
 
-def test_shared_prefix_equals_private_copies_bitwise():
+@pytest.mark.parametrize("cache_kv", [False, True])
+def test_shared_prefix_equals_private_copies_bitwise(cache_kv):
+    k = pkv.PKV_ATTN_AUTO | (pkv.PKV_ATTN_CACHE_KV if cache_kv else 0)
     w = workloads.make_workload(4, batch=4, len_range=(1, 100), prefix_tokens=256)
     dev = to_dev(w)
-    a = run_step(w, dev)
+    a = run_step(w, dev, kernel=k)
     # Give sequence 2 private copies of the shared prefix blocks.
     pb = len(w.shared_blocks)
     extra = torch.arange(w.num_blocks, w.num_blocks + pb)
@@ -377,7 +414,7 @@ def test_shared_prefix_equals_private_copies_bitwise():
     tables[2, :pb] = extra.numpy()
     dev2 = to_dev(w)
     dev2.update(k_pool=kp.cuda(), v_pool=vp.cuda(), tables=torch.as_tensor(tables, device="cuda"))
-    b = run_step(w, dev2)
+    b = run_step(w, dev2, kernel=k)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
@@ -397,9 +434,11 @@ def compact_inputs(w, seqs):
     return kp, vp, tables
 
 
-@pytest.mark.parametrize("cid,block_size,nsample", [(2, None, 4), (3, None, 6), (4, None, 4),
-                                                    (5, 16, 2)])
-def test_full_size_sampled(cid, block_size, nsample):
+@pytest.mark.parametrize("cid,block_size,nsample,cache_kv",
+                         [(2, None, 4, False), (3, None, 6, False), (4, None, 4, True),
+                          (4, None, 4, False), (5, 16, 2, False)])
+def test_full_size_sampled(cid, block_size, nsample, cache_kv):
+    # Config 4 shares a prefix: the bench runs it with PKV_ATTN_CACHE_KV.
     kw = {} if block_size is None else dict(block_size=block_size)
     w = workloads.make_workload(cid, device="cuda", **kw)
     rng = np.random.default_rng(cid)
@@ -417,6 +456,7 @@ def test_full_size_sampled(cid, block_size, nsample):
                tables=torch.as_tensor(w.tables, device="cuda"),
                lens=torch.as_tensor(w.lens, device="cuda"),
                lens_pre=torch.as_tensor(w.lens_pre, device="cuda"))
-    out = run_step(w, dev, partition_tokens=w.partition_tokens)
-    check_close(out[sel.cuda()], ref, w.dtype, f"full config{cid} seqs={seqs}")
+    k = pkv.PKV_ATTN_CACHE_KV if cache_kv else pkv.PKV_ATTN_AUTO
+    out = run_step(w, dev, partition_tokens=w.partition_tokens, kernel=k)
+    check_close(out[sel.cuda()], ref, w.dtype, f"full config{cid} seqs={seqs} cache_kv={cache_kv}")
     assert torch.isfinite(out.float()).all()

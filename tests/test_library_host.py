@@ -90,6 +90,10 @@ def test_fp32_rejects_matrix_core_kernel():
     a[-2] = 2
     assert lib.paged_decode_attention_with(pkv.PKV_ATTN_MFMA, *a) == pkv.PKV_ERR_UNSUPPORTED
     assert lib.paged_decode_attention_with(9, *a) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.paged_decode_attention_with(32, *a) == pkv.PKV_ERR_INVALID_ARG   # unknown flag
+    a[12], a[-2] = 128, 0
+    assert lib.paged_decode_attention_with(pkv.PKV_ATTN_MFMA | pkv.PKV_ATTN_CACHE_KV, *a) \
+        == pkv.PKV_ERR_UNSUPPORTED   # the flag does not change which kernels exist
 
 
 def test_cache_ops_reject_bad_arguments():
