@@ -88,24 +88,26 @@ constexpr int kPlanThreads = 1024;
 constexpr int kPlanLdsCum = 8192;   // prefix sums kept in LDS up to this many sequences
 
 // Plan area (int32 words): header | cum[S + 1] | desc[range_cap][4] |
-// short tasks[kvq * S][4] | long tasks[kvq * S][4]
+// short tasks[kvq * S][4] | long tasks[kvq * S][4]; plan workgroup b writes
+// its tasks from entry b * task_seg of each list.
 // Header: totals, the claim counter and the stage table; stage k covers
 // claims [C_k, C_k+1) and tiles [X_k, X_k+1), every claim z_k tiles long but
 // the last of the final stage.  Entry ns (= number of stages) is a sentinel.
-constexpr int kHdrWords = 64;
+constexpr int kPlanGroups = 16;     // workgroups of the plan launch
+constexpr int kHdrWords = 128;
 enum Hdr {
   kHdrTot = 0,      // tiles of one KV-head quad (sum over sequences)
   kHdrClaims = 1,   // number of claims
   kHdrStages = 2,   // number of stages
   kHdrTotal = 3,    // tiles of the whole space
   kHdrNext = 4,     // claim counter
-  kHdrShort = 5,    // split (quad, sequence) pairs of at most kMergeBlock partials
-  kHdrLong = 6,     // split pairs of more partials
   kHdrX = 8,        // X_k, kMaxStages + 1 entries
   kHdrC = 8 + kMaxStages + 1,
   kHdrZ = 8 + 2 * (kMaxStages + 1),
+  kHdrShort = 64,   // per plan workgroup: split pairs of at most kMergeBlock partials
+  kHdrLong = 64 + kPlanGroups,   // per plan workgroup: split pairs of more partials
 };
-static_assert(kHdrZ + kMaxStages + 1 <= kHdrWords, "header");
+static_assert(kHdrZ + kMaxStages + 1 <= kHdrShort && kHdrLong + kPlanGroups <= kHdrWords, "header");
 
 typedef const __attribute__((address_space(4))) int32_t cint;   // read with scalar loads
 
@@ -137,8 +139,10 @@ struct AttnParams {
   int cap_tiles;    // 0 = no cap, else at most this many tiles per claim
   int grid;         // workgroups of the partition and merge launches
   int range_cap;    // claim descriptor slots
-  int off_short;    // plan-area word offsets of the merge task lists
+  int off_desc;     // plan-area word offsets of the claim descriptors
+  int off_short;    // and of the merge task lists
   int off_long;
+  int task_seg;     // task-list entries per plan workgroup
   float scale_log2;  // scale * log2(e): scores live in log2 units
 };
 
@@ -226,7 +230,9 @@ __device__ __forceinline__ int live_tiles(int L, int max_len) {
 }
 
 // ---------------------------------------------------------------------------
-// Plan: one workgroup.
+// Plan: kPlanGroups workgroups.  Each one prefix-sums the tile counts and
+// builds the claim schedule for itself (a few microseconds of LDS work), then
+// writes its share of the claim descriptors, merge tasks and empty-row fills.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
@@ -236,16 +242,23 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
   __shared__ int dead_list[kPlanThreads];
   __shared__ int wave_sum[kPlanThreads / 64];
   __shared__ int cum_lds[kPlanLdsCum + 1];
+  __shared__ int st_x[kMaxStages + 1], st_c[kMaxStages + 1], st_z[kMaxStages + 1];
+  __shared__ int n_stages, n_claims, n_short, n_long;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
+  const int b = blockIdx.x;
   const int S_ = p.num_seqs;
   const int max_len = p.max_blocks << p.log2_b;
   const size_t row_elems = (size_t)p.num_q_heads * p.head_dim;
+  // Past kPlanLdsCum sequences the prefix sums live in memory only (every
+  // workgroup writes the same values and reads back its own).
+  const bool in_lds = S_ <= kPlanLdsCum;
   int32_t* cum = p.plan + kHdrWords;
 
   // Exclusive prefix sum of tile counts, kPlanThreads sequences per pass.
-  // Sequences with nothing to attend get their rows filled on the way:
-  // zeros for L <= 0, NaN for a length the table row cannot hold.
+  // Sequences with nothing to attend get their rows filled on the way, each
+  // by workgroup s % kPlanGroups: zeros for L <= 0, NaN for a length the
+  // table row cannot hold.
   if (tid == 0) carry_lds = 0;
   for (int base = 0; base < S_; base += kPlanThreads) {
     if (tid == 0) dead_count = 0;
@@ -253,7 +266,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
     const int s = base + tid;
     const int L = s < S_ ? p.lens[s] : 1;
     const int nt = s < S_ ? live_tiles(L, max_len) : 0;
-    if (s < S_ && nt == 0) dead_list[atomicAdd(&dead_count, 1)] = s;
+    if (s < S_ && nt == 0 && s % kPlanGroups == b) dead_list[atomicAdd(&dead_count, 1)] = s;
     int incl = nt;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -266,14 +279,14 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
     for (int i = 0; i < wv; ++i) before += wave_sum[i];
     const int excl = before + incl - nt;
     if (s < S_) {
-      cum[s] = excl;
-      if (s < kPlanLdsCum) cum_lds[s] = excl;
+      if (in_lds) cum_lds[s] = excl;
+      else cum[s] = excl;
+      if (in_lds && b == 0) cum[s] = excl;
     }
     const int ndead = dead_count;
     for (int k = 0; k < ndead; ++k) {
       const int sd = dead_list[k];
-      const int Ld = p.lens[sd];
-      const float fill = Ld <= 0 ? 0.f : __builtin_nanf("");
+      const float fill = p.lens[sd] <= 0 ? 0.f : __builtin_nanf("");
       S* row = (S*)p.out + (size_t)sd * row_elems;
       for (size_t i = tid; i < row_elems; i += kPlanThreads) Cvt<T>::store(row + i, fill);
     }
@@ -283,11 +296,11 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
   }
   const int tot = carry_lds;
   if (tid == 0) {
-    cum[S_] = tot;
-    if (S_ <= kPlanLdsCum) cum_lds[S_] = tot;
+    if (in_lds) cum_lds[S_] = tot;
+    if (!in_lds || b == 0) cum[S_] = tot;
   }
-  // Past kPlanLdsCum sequences the prefix sums are read back from memory.
-  if (S_ > kPlanLdsCum) __syncthreads(); else lds_barrier();
+  if (in_lds) lds_barrier(); else __syncthreads();
+  auto cum_at = [&](int i) { return in_lds ? cum_lds[i] : cum[i]; };
 
   // Claim schedule.  Stage 0 hands every workgroup one claim of half its
   // share; each later stage halves the claim size, down to
@@ -295,55 +308,68 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
   // A workgroup claims its next piece when it finishes one, so faster units
   // take more pieces and the last ones are short.  The descriptor budget
   // range_cap always leaves room for the rest at the cap size (when capped).
-  __shared__ int st_x[kMaxStages + 1], st_c[kMaxStages + 1], st_z[kMaxStages + 1];
-  __shared__ int n_stages, n_claims;
+  // All counts stay below 2^31 (the host checks the tile total).
   const int total = tot * p.kvq_count;
   if (tid == 0) {
-    const int g = p.grid;
-    const int zmin = kMinClaimWaveTiles * p.wpk;
-    const int cap = p.cap_tiles;
-    int x = 0, c = 0, ns = 0;
-    long long z = ((long long)total + 2LL * g - 1) / (2LL * g);
-    while (x < total) {
-      const int rem = total - x;
-      int zz = (int)(z > zmin ? z : zmin);
+    const unsigned g = (unsigned)p.grid;
+    const unsigned zmin = kMinClaimWaveTiles * p.wpk;
+    const unsigned cap = (unsigned)p.cap_tiles;
+    const unsigned budget_all = (unsigned)p.range_cap;
+    unsigned x = 0, c = 0, z = ((unsigned)total + 2 * g - 1) / (2 * g);
+    int ns = 0;
+    while (x < (unsigned)total) {
+      const unsigned rem = (unsigned)total - x;
+      unsigned zz = z > zmin ? z : zmin;
       if (cap > 0 && zz > cap) zz = cap;
-      const long long count_all = ((long long)rem + zz - 1) / zz;
+      const unsigned count_all = rem / zz + (rem % zz != 0);
       bool final_stage = count_all <= g || zz <= zmin || ns == kMaxStages - 1;
       if (!final_stage) {
-        const long long rest = (long long)rem - (long long)g * zz;
-        const long long need_after = cap > 0 ? (rest + cap - 1) / cap : 1;
-        if ((long long)c + g + need_after > p.range_cap) final_stage = true;
+        const unsigned rest = rem - g * zz;
+        const unsigned need_after = cap > 0 ? rest / cap + (rest % cap != 0) : 1;
+        if (c + g + need_after > budget_all) final_stage = true;
       }
-      int count;
+      unsigned count;
       if (final_stage) {
-        const int budget = p.range_cap - c;   // >= 1 by construction
-        if (count_all > budget) zz = (int)(((long long)rem + budget - 1) / budget);
-        count = (rem + zz - 1) / zz;
+        const unsigned budget = budget_all - c;   // >= 1 by construction
+        if (count_all > budget) zz = rem / budget + (rem % budget != 0);
+        count = rem / zz + (rem % zz != 0);
       } else {
         count = g;
       }
-      st_x[ns] = x;
-      st_c[ns] = c;
-      st_z[ns] = zz;
+      st_x[ns] = (int)x;
+      st_c[ns] = (int)c;
+      st_z[ns] = (int)zz;
       ++ns;
       c += count;
-      x = final_stage ? total : x + g * zz;
+      x = final_stage ? (unsigned)total : x + g * zz;
       z = (z + 1) / 2;
     }
     st_x[ns] = total;
-    st_c[ns] = c;
+    st_c[ns] = (int)c;
     st_z[ns] = 0;
     n_stages = ns;
-    n_claims = c;
+    n_claims = (int)c;
+    n_short = 0;
+    n_long = 0;
   }
   lds_barrier();
   const int ns = n_stages;
   const int C = n_claims;
-  int32_t* desc = p.plan + kHdrWords + S_ + 1;
-  for (int c = tid; c < C; c += kPlanThreads) {
+  auto stage_of_claim = [&](int c) {
     int k = 0;
     while (k + 1 < ns && st_c[k + 1] <= c) ++k;
+    return k;
+  };
+  auto claim_at = [&](int x) {
+    int k = 0;
+    while (k + 1 < ns && st_x[k + 1] <= x) ++k;
+    return st_c[k] + (x - st_x[k]) / st_z[k];
+  };
+
+  // Claim descriptors (qd, sequence, first tile, tiles), this workgroup's share.
+  int32_t* desc = p.plan + p.off_desc;
+  for (int c = b * kPlanThreads + tid; c < C; c += kPlanGroups * kPlanThreads) {
+    const int k = stage_of_claim(c);
     const int x = st_x[k] + (c - st_c[k]) * st_z[k];
     const int size = min(st_z[k], st_x[k + 1] - x);
     const int qd = x / tot;
@@ -352,60 +378,55 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
     int lo = 0, hi = S_;   // cum[lo] <= rem < cum[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      const int cm = S_ <= kPlanLdsCum ? cum_lds[mid] : cum[mid];
-      if (cm <= rem) lo = mid; else hi = mid;
+      if (cum_at(mid) <= rem) lo = mid; else hi = mid;
     }
-    const int c_lo = S_ <= kPlanLdsCum ? cum_lds[lo] : cum[lo];
-    desc[4 * c + 0] = qd;
-    desc[4 * c + 1] = lo;
-    desc[4 * c + 2] = rem - c_lo;
-    desc[4 * c + 3] = size;
+    *reinterpret_cast<int4*>(desc + 4 * c) = make_int4(qd, lo, rem - cum_at(lo), size);
   }
 
-  // Merge lists.  A (quad, sequence) pair whose tiles span claims c0 .. c1
+  // Merge tasks.  A (quad, sequence) pair whose tiles span claims c0 .. c1
   // with c0 < c1 is a task: its partial states sit in pairs c0 + t .. c1 + t
   // (t = quad * S + sequence).  Tasks of at most kMergeBlock partials go to
   // the short list (one wave each), longer ones to the long list (one
-  // workgroup each).
-  __shared__ int n_short, n_long;
-  if (tid == 0) {
-    n_short = 0;
-    n_long = 0;
-  }
-  lds_barrier();
-  auto claim_at = [&](int x) {
-    int k = 0;
-    while (k + 1 < ns && st_x[k + 1] <= x) ++k;
-    return st_c[k] + (x - st_x[k]) / st_z[k];
-  };
-  for (int t = tid; t < p.kvq_count * S_; t += kPlanThreads) {
+  // workgroup each).  This workgroup takes pairs [t_begin, t_end) and writes
+  // its own segment of each list.
+  const int pairs = p.kvq_count * S_;
+  const int t_begin = b * p.task_seg;
+  const int t_end = min(pairs, t_begin + p.task_seg);
+  int32_t* short_list = p.plan + p.off_short + 4 * t_begin;
+  int32_t* long_list = p.plan + p.off_long + 4 * t_begin;
+  for (int t = t_begin + tid; t < t_end; t += kPlanThreads) {
     const int qd = t / S_;
     const int sq = t - qd * S_;
-    const int c_a = S_ <= kPlanLdsCum ? cum_lds[sq] : cum[sq];
-    const int c_b = S_ <= kPlanLdsCum ? cum_lds[sq + 1] : cum[sq + 1];
-    if (c_b == c_a) continue;
+    const int c_a = cum_at(sq);
+    const int c_b = cum_at(sq + 1);
+    if (c_b == c_a) continue;   // empty: its rows were filled above
     const int c0 = claim_at(qd * tot + c_a);
     const int c1 = claim_at(qd * tot + c_b - 1);
     if (c0 == c1) continue;
     const int n = c1 - c0 + 1;
-    int32_t* list = p.plan + (n <= kMergeBlock ? p.off_short : p.off_long);
-    const int ti = atomicAdd(n <= kMergeBlock ? &n_short : &n_long, 1);
-    *reinterpret_cast<int4*>(list + 4 * ti) = make_int4(t, c0, n, 0);
+    const bool is_short = n <= kMergeBlock;
+    const int ti = atomicAdd(is_short ? &n_short : &n_long, 1);
+    *reinterpret_cast<int4*>((is_short ? short_list : long_list) + 4 * ti) =
+        make_int4(t, c0, n, 0);
   }
   lds_barrier();
-  if (tid <= ns) {
-    p.plan[kHdrX + tid] = st_x[tid];
-    p.plan[kHdrC + tid] = st_c[tid];
-    p.plan[kHdrZ + tid] = st_z[tid];
-  }
   if (tid == 0) {
-    p.plan[kHdrTot] = tot;
-    p.plan[kHdrClaims] = C;
-    p.plan[kHdrStages] = ns;
-    p.plan[kHdrTotal] = total;
-    p.plan[kHdrNext] = 0;
-    p.plan[kHdrShort] = n_short;
-    p.plan[kHdrLong] = n_long;
+    p.plan[kHdrShort + b] = n_short;
+    p.plan[kHdrLong + b] = n_long;
+  }
+  if (b == 0) {
+    if (tid <= ns) {
+      p.plan[kHdrX + tid] = st_x[tid];
+      p.plan[kHdrC + tid] = st_c[tid];
+      p.plan[kHdrZ + tid] = st_z[tid];
+    }
+    if (tid == 0) {
+      p.plan[kHdrTot] = tot;
+      p.plan[kHdrClaims] = C;
+      p.plan[kHdrStages] = ns;
+      p.plan[kHdrTotal] = total;
+      p.plan[kHdrNext] = 0;
+    }
   }
 }
 
@@ -426,7 +447,7 @@ template <typename Fn>
 __device__ __forceinline__ void walk_claims(const AttnParams& p, Fn&& process) {
   cint* hdr = (cint*)p.plan;
   cint* cum = (cint*)(p.plan + kHdrWords);
-  cint* desc = (cint*)(p.plan + kHdrWords + p.num_seqs + 1);
+  cint* desc = (cint*)(p.plan + p.off_desc);
   const int C = hdr[kHdrClaims];
   __shared__ int next_lds[2];
   int parity = 0;
@@ -1105,21 +1126,37 @@ __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
   __shared__ float m_lds[kWaves][kMaxGroup];
   __shared__ float l_lds[kWaves][kMaxGroup];
   __shared__ __align__(16) float acc_lds[kWaves][kMaxGD];
-  cint* hdr = (cint*)p.plan;
-  cint* short_list = (cint*)(p.plan + p.off_short);
-  cint* long_list = (cint*)(p.plan + p.off_long);
   const int G = p.gsize, D = p.head_dim, KW = p.kw;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
+  // The task lists come in kPlanGroups segments.  Lanes 0..15 hold the
+  // inclusive prefix of the short-list counts, lanes 16..31 that of the
+  // long-list counts; entry i of a list is then found with one ballot.
+  static_assert(kPlanGroups == 16, "two 16-lane prefix groups");
+  int pre = lane < 2 * kPlanGroups ? p.plan[kHdrShort + lane] : 0;   // kHdrLong = kHdrShort + 16
+#pragma unroll
+  for (int o = 1; o < kPlanGroups; o <<= 1) {
+    const int v = __shfl_up(pre, o);
+    if ((lane & (kPlanGroups - 1)) >= o) pre += v;
+  }
+  auto entry = [&](int list_off, int group0, int i) {
+    const unsigned long long below = __ballot(lane >= group0 && lane < group0 + kPlanGroups && pre <= i);
+    const int seg = __builtin_amdgcn_readfirstlane(__popcll(below));
+    const int start =
+        seg > 0 ? __builtin_amdgcn_readfirstlane(__shfl(pre, group0 + seg - 1)) : 0;
+    // Uniform address: the entry comes through scalar loads.
+    cint* e = (cint*)(p.plan + list_off) + 4 * ((size_t)seg * p.task_seg + (i - start));
+    return make_int4(e[0], e[1], e[2], 0);
+  };
+
   // Long tasks: one workgroup per (task, KV-head group).
-  const int n_long = hdr[kHdrLong] * KW;
+  const int n_long = __builtin_amdgcn_readfirstlane(__shfl(pre, 2 * kPlanGroups - 1)) * KW;
   for (int u = blockIdx.x; u < n_long; u += gridDim.x) {
     const int ti = u / KW;
     const int kw_i = u - ti * KW;
-    const int t = long_list[4 * ti + 0];
-    const int c0 = long_list[4 * ti + 1];
-    const int n = long_list[4 * ti + 2];
+    const int4 e = entry(p.off_long, kPlanGroups, ti);
+    const int t = e.x, c0 = e.y, n = e.z;
     const int qd = t / p.num_seqs;
     const int s = t - qd * p.num_seqs;
     const WaveKv kv = wave_kv(p, qd, kw_i);
@@ -1165,14 +1202,16 @@ __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
     lds_barrier();   // the LDS buffers are reused by the next task
   }
 
-  // Short tasks: one wave per (task, KV-head group).
-  const int n_short = hdr[kHdrShort] * KW;
-  for (int it = blockIdx.x * kWaves + wv; it < n_short; it += gridDim.x * kWaves) {
+  // Short tasks: one wave per (task, KV-head group), counted from the last
+  // workgroup down so that they land on workgroups without a long task
+  // whenever the grid has room for both.
+  const int n_short = __builtin_amdgcn_readfirstlane(__shfl(pre, kPlanGroups - 1)) * KW;
+  for (int it = (gridDim.x - 1 - blockIdx.x) * kWaves + wv; it < n_short;
+       it += gridDim.x * kWaves) {
     const int ti = it / KW;
     const int kw_i = it - ti * KW;
-    const int t = short_list[4 * ti + 0];
-    const int c0 = short_list[4 * ti + 1];
-    const int n = short_list[4 * ti + 2];
+    const int4 e = entry(p.off_short, 0, ti);
+    const int t = e.x, c0 = e.y, n = e.z;
     const int qd = t / p.num_seqs;
     const int s = t - qd * p.num_seqs;
     const WaveKv kv = wave_kv(p, qd, kw_i);
@@ -1200,7 +1239,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t off_short, off_long, plan_words;   // plan-area words
+  size_t off_desc, off_short, off_long, task_seg, plan_words;   // plan-area words
   size_t m_off, l_off, acc_off, total;         // bytes
 };
 
@@ -1212,9 +1251,11 @@ inline WsLayout ws_layout(int num_seqs, int kvq_count, int pair_heads, int head_
                           int range_cap) {
   WsLayout w;
   const size_t pairs_q = (size_t)kvq_count * num_seqs;
-  w.off_short = (kHdrWords + (size_t)num_seqs + 1 + 4 * (size_t)range_cap + 3) & ~(size_t)3;
-  w.off_long = w.off_short + 4 * pairs_q;
-  const size_t plan_words = w.off_long + 4 * pairs_q;
+  w.task_seg = (pairs_q + kPlanGroups - 1) / kPlanGroups;
+  w.off_desc = (kHdrWords + (size_t)num_seqs + 1 + 3) & ~(size_t)3;
+  w.off_short = w.off_desc + 4 * (size_t)range_cap;
+  w.off_long = w.off_short + 4 * w.task_seg * kPlanGroups;
+  const size_t plan_words = w.off_long + 4 * w.task_seg * kPlanGroups;
   w.plan_words = plan_words;
   const size_t heads = ((size_t)range_cap + pairs_q) * pair_heads;
   w.m_off = align256(plan_words * 4);
@@ -1413,8 +1454,10 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
   p.cap_tiles = cap_tiles;
   p.grid = grid;
   p.range_cap = (int)range_cap;
+  p.off_desc = (int)ws.off_desc;
   p.off_short = (int)ws.off_short;
   p.off_long = (int)ws.off_long;
+  p.task_seg = (int)ws.task_seg;
   p.scale_log2 = scale * kLog2e;
   L->part_fn = fn;
   return PKV_OK;
@@ -1422,7 +1465,7 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
 
 template <typename T>
 hipError_t launch_plan(const AttnParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(attn_plan<T>, dim3(1), dim3(kPlanThreads), 0, st, p);
+  hipLaunchKernelGGL(attn_plan<T>, dim3(kPlanGroups), dim3(kPlanThreads), 0, st, p);
   return hipGetLastError();
 }
 
@@ -1479,9 +1522,10 @@ extern "C" size_t paged_decode_workspace_bytes(int num_seqs, int num_q_heads, in
                               (long long)num_q_heads * num_seqs * parts;
   if (range_cap >= (1LL << 30)) return 0;
   // Plan words: header, cum, descriptors, then the two merge task lists of
-  // at most kvq_count * S <= Hq * S entries each.
+  // at most kvq_count * S <= Hq * S entries each (rounded up per plan
+  // workgroup).
   const size_t plan_words = pkv::kHdrWords + (size_t)num_seqs + 4 + 4 * (size_t)range_cap +
-                            8 * (size_t)num_q_heads * num_seqs;
+                            8 * ((size_t)num_q_heads * num_seqs + pkv::kPlanGroups);
   const size_t heads = (size_t)pkv::device_cu_count() * pkv::kClaimsPerCu * pkv::kWaves *
                            pkv::kMaxGroup +
                        (size_t)(2LL * num_q_heads + 24) * num_seqs * (size_t)(1 + parts);
