@@ -689,12 +689,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
     int bad = 0;
     const int tile_end = sg.t0 + sg.take;
     // Register ring: while one tile is consumed the next kSlots - 1 are in
-    // flight.  Loads past the segment's last tile repeat that tile.
+    // flight.
     uint4 kb[kSlots][TPR], vb[kSlots][TPR];
     auto issue = [&](auto slot, int tile) {
       constexpr int SL = decltype(slot)::value;
-      const int tc = min(tile, tile_end - 1);
-      const int tb = tc * kTile;
+      // Past the segment's last tile the slot is never consumed: load nothing.
+      if (tile >= tile_end) return;
+      const int tb = tile * kTile;
       int first, nid;
       const int ids = tile_block_ids(p, trow, tb, L, first, nid, bad);
       const int id0 = __builtin_amdgcn_readfirstlane(ids);
