@@ -2,11 +2,13 @@
 """Paged decode benchmark on one MI355X.
 
 A step is one pass of the whole decode hot path over one batch: the cache
-append of one new token per sequence (paged_kv_append), then the three
-launches of paged decode attention: the work plan, the partition kernel and
-the log-sum-exp merge (paged_decode_attention_plan / _partitions / _merge).  Host slot allocation is done once before
-timing (the tables already list the slot), and the append rewrites the same
-bytes every step, so the timed steps are identical.
+append of one new token per sequence, then paged decode attention
+(paged_decode_step: the append rides in the work-plan launch, followed by the
+partition kernel and the log-sum-exp merge).  A second pass times the phases
+one by one (paged_kv_append, paged_decode_attention_plan / _partitions /
+_merge).  Host slot allocation is done once before timing (the tables already
+list the slot), and the append rewrites the same bytes every step, so the
+timed steps are identical.
 
 Default workload: the 70B-shaped GQA decode batch (64 query / 8 KV heads of
 128, bf16, B = 16, 256 sequences with log-uniform lengths in [512, 8192],
@@ -178,21 +180,22 @@ def main(argv=None) -> int:
                                          scale=w.scale, partition_tokens=P, workspace=ws,
                                          stream=stream)
 
+    def step():
+        # Append + attention; the append rides in the plan launch.
+        pkv.paged_decode_step(out, w.q, w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens,
+                              kernel=kernel, scale=w.scale, partition_tokens=P, workspace=ws,
+                              stream=stream)
+
     for _ in range(args.warmup):
         append()
         plan()
         partitions()
         merge()
+        step()
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-
-    def step():
-        append()
-        plan()
-        partitions()
-        merge()
 
     # The timed region: K whole steps back to back, events only around them.
     start, end = ev(), ev()
@@ -204,9 +207,10 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
 
-    # Phase breakdown, a separate pass with an event between launches (event
-    # records add a few microseconds of gap each, so the phases sum to more
-    # than ms_step).  The partition kernel's time here is the roofline's.
+    # Phase breakdown, a separate pass with an event between launches, the
+    # append as its own launch (event records add a few microseconds of gap
+    # each, so the phases sum to more than ms_step).  The partition kernel's
+    # time here is the roofline's.
     marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for m in marks:

@@ -248,6 +248,33 @@ int paged_decode_attention_merge(int kernel, void* out, const void* q, const voi
                                  int partition_tokens, void* workspace, size_t workspace_bytes,
                                  int dtype, void* stream);
 
+/*
+ * paged_decode_step - one decode step: cache append, then attention.
+ *
+ * [pofe] "How it works", decode step: the new token's k and v are written to
+ * the cache (slot (L-1) % B of block table[(L-1) / B], as paged_kv_append
+ * with context_lens_pre = L - 1), then attention runs over all L tokens, as
+ * paged_decode_attention_with(kernel, ...).  The append rides in the plan
+ * launch, so the step is three launches instead of four.
+ *   k_pool, v_pool : device, writable (the append writes them)
+ *   k_new, v_new   : device, [num_seqs, num_kv_heads, head_dim], dtype; must
+ *                    not be NULL when num_seqs > 0 (else PKV_ERR_INVALID_ARG)
+ *   context_lens   : device int32 [num_seqs], lengths AFTER the append; a
+ *                    sequence with L <= 0 or L > max_blocks_per_seq *
+ *                    block_size writes nothing (its output is as attention
+ *                    defines: zeros, NaN), nor does one whose block id for
+ *                    slot L-1 lies outside the pool (its output is NaN).
+ * Other arguments, results and workspace as paged_decode_attention_with.
+ * Equivalent bit for bit to paged_kv_append followed by
+ * paged_decode_attention_with on the same stream.
+ */
+int paged_decode_step(int kernel, void* out, const void* q, void* k_pool, void* v_pool,
+                      const void* k_new, const void* v_new, const int32_t* block_tables,
+                      int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                      int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
+                      int head_dim, float scale, int partition_tokens, void* workspace,
+                      size_t workspace_bytes, int dtype, void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Host block manager (CPU only; no device calls)                            */
 /* ------------------------------------------------------------------------- */

@@ -66,6 +66,7 @@ _sig("paged_decode_attention_with", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_attention_plan", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_attention_partitions", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_attention_merge", _i32, [_i32] + _ATTN_ARGS)
+_sig("paged_decode_step", _i32, [_i32, _p, _p, _p, _p, _p, _p] + _ATTN_ARGS[4:])
 _sig("pkv_validate_tables", _i32, [_p, _i32, _p, _i32, _i32, _i32, _intp])
 _sig("pkv_bm_create", _i32, [_i32, _i32, ctypes.POINTER(_p)])
 _sig("pkv_bm_destroy", None, [_p])
@@ -262,6 +263,22 @@ def paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens, *
 
 def paged_decode_attention_with(kernel, out, q, k_pool, v_pool, block_tables, context_lens, **kw):
     paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens, kernel=kernel, **kw)
+
+
+def paged_decode_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, *,
+                      kernel=0, scale=None, partition_tokens=0, workspace=None, stream=None):
+    """One decode step: append token L-1 (k_new, v_new [num_seqs, H_kv, D]) to
+    each sequence's cache, then attention over L tokens (context_lens are the
+    lengths after the append).  Same as paged_kv_append + paged_decode_attention_with."""
+    args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                      partition_tokens, workspace, stream)
+    s, h, d = q.shape[0], k_pool.shape[2], k_pool.shape[3]
+    if k_new.shape != (s, h, d) or v_new.shape != (s, h, d):
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    _check(_lib.paged_decode_step(int(kernel), args[0], args[1], args[2], args[3],
+                                  _dev(k_new, "k_new", k_pool.dtype),
+                                  _dev(v_new, "v_new", k_pool.dtype), *args[4:]),
+           "paged_decode_step")
 
 
 def pkv_validate_tables(block_tables, context_lens, num_blocks: int, block_size: int):

@@ -81,7 +81,7 @@ constexpr int kMaxGD = 1024;    // G * D bound: the cross-wave LDS buffer is 16 
 constexpr int kMaxGroup = 8;    // query heads per workgroup (larger groups are split)
 constexpr int kMaxWgPerCu = 8;  // 2048 threads per CU / 256
 constexpr int kClaimsPerCu = 16;    // claim descriptors per compute unit
-constexpr int kMinClaimWaveTiles = 4;  // smallest claim: tiles per wave
+constexpr int kMinClaimWaveTiles = 6;  // smallest claim: tiles per wave
 constexpr int kMaxStages = 16;      // claim-size stages (sizes halve stage to stage)
 constexpr int kMergeBlock = 8;      // partial states one merge item combines
 constexpr int kPlanThreads = 1024;
@@ -118,6 +118,8 @@ struct AttnParams {
   const char* v_pool;
   const int32_t* tables;
   const int32_t* lens;
+  const char* k_new;  // decode step: token L-1 of each sequence, written by the plan
+  const char* v_new;  // (null: attention only)
   int32_t* plan;     // header, cum, desc, task
   float* ws_m;       // [pairs][G]
   float* ws_l;       // [pairs][G]
@@ -254,6 +256,28 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
   // workgroup writes the same values and reads back its own).
   const bool in_lds = S_ <= kPlanLdsCum;
   int32_t* cum = p.plan + kHdrWords;
+
+  // Decode step: append token L-1 of every sequence with 0 < L <= max_len
+  // (the cache append of [pofe] "How it works"), one 16-byte chunk per
+  // thread, spread over the plan workgroups.  The partition launch that
+  // follows on the stream reads it from the pool.
+  if (p.k_new) {
+    const int row_chunks = p.num_kv_heads * p.head_dim * T::bytes / 16;
+    for (long long i = (long long)b * kPlanThreads + tid; i < (long long)S_ * row_chunks;
+         i += kPlanGroups * kPlanThreads) {
+      const int s = (int)(i / row_chunks);
+      const int ch = (int)(i - (long long)s * row_chunks);
+      const int L = p.lens[s];
+      if (L <= 0 || L > max_len) continue;
+      const int blk = p.tables[(size_t)s * p.max_blocks + ((L - 1) >> p.log2_b)];
+      if (!valid_block(blk, p.num_blocks)) continue;
+      const size_t dst = row_offset(blk, L - 1, p.log2_b, p.num_kv_heads, 0, p.head_dim) * T::bytes +
+                         16 * (size_t)ch;
+      const size_t src = (size_t)s * row_chunks * 16 + 16 * (size_t)ch;
+      store16((char*)p.k_pool + dst, load16(p.k_new + src));
+      store16((char*)p.v_pool + dst, load16(p.v_new + src));
+    }
+  }
 
   // Exclusive prefix sum of tile counts, kPlanThreads sequences per pass.
   // Sequences with nothing to attend get their rows filled on the way, each
@@ -1481,13 +1505,16 @@ int decode_attention_impl(int phase, int kernel, void* out, const void* q, const
                           const int32_t* context_lens, int num_seqs, int num_blocks,
                           int block_size, int num_q_heads, int num_kv_heads, int head_dim,
                           float scale, int partition_tokens, void* workspace,
-                          size_t workspace_bytes, int dtype, void* stream) {
+                          size_t workspace_bytes, int dtype, void* stream,
+                          const void* k_new = nullptr, const void* v_new = nullptr) {
   Launch L;
   const int st = prepare(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                          context_lens, num_seqs, num_blocks, block_size, num_q_heads,
                          num_kv_heads, head_dim, scale, partition_tokens, workspace,
                          workspace_bytes, dtype, &L);
   if (st != PKV_OK || num_seqs == 0) return st;
+  L.p.k_new = (const char*)k_new;
+  L.p.v_new = (const char*)v_new;
   hipStream_t hs = (hipStream_t)stream;
   if (phase & kPhasePlan) {
     hipError_t e = dtype == PKV_F32 ? launch_plan<F32>(L.p, hs)
@@ -1563,4 +1590,19 @@ extern "C" int paged_decode_attention_partitions(int kernel, PKV_ATTN_ARGS) {
 
 extern "C" int paged_decode_attention_merge(int kernel, PKV_ATTN_ARGS) {
   return pkv::decode_attention_impl(pkv::kPhaseMerge, kernel, PKV_ATTN_PASS);
+}
+
+extern "C" int paged_decode_step(int kernel, void* out, const void* q, void* k_pool, void* v_pool,
+                                 const void* k_new, const void* v_new,
+                                 const int32_t* block_tables, int max_blocks_per_seq,
+                                 const int32_t* context_lens, int num_seqs, int num_blocks,
+                                 int block_size, int num_q_heads, int num_kv_heads, int head_dim,
+                                 float scale, int partition_tokens, void* workspace,
+                                 size_t workspace_bytes, int dtype, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_INVALID_ARG;
+  return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, out, q, k_pool, v_pool, block_tables,
+                                    max_blocks_per_seq, context_lens, num_seqs, num_blocks,
+                                    block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                                    partition_tokens, workspace, workspace_bytes, dtype, stream,
+                                    k_new, v_new);
 }

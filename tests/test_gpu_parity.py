@@ -379,6 +379,54 @@ def test_zero_length_gives_zeros_and_bad_ids_give_nan():
         assert torch.isfinite(o[s]).all()
 
 
+@pytest.mark.parametrize("cid,kernel", [(2, "auto"), (3, "auto"), (3, "valu"), (4, "cached"),
+                                        (5, "auto"), (1, "auto")])
+def test_decode_step_equals_append_then_attention(cid, kernel):
+    # paged_decode_step fuses the append into the plan launch; it must give
+    # the same pools and the same outputs, bit for bit, as the two calls.
+    k = {"auto": pkv.PKV_ATTN_AUTO, "valu": pkv.PKV_ATTN_VALU,
+         "cached": pkv.PKV_ATTN_CACHE_KV}[kernel]
+    w = workloads.make_workload(cid, **SMALL[cid])
+    a = to_dev(w)
+    b = to_dev(w)
+    ref_out = run_step(w, a, kernel=k)
+    out = torch.empty_like(b["q"])
+    pkv.paged_decode_step(out, b["q"], b["k_pool"], b["v_pool"], b["k_new"], b["v_new"],
+                          b["tables"], b["lens"], kernel=k, scale=w.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(a["k_pool"]), bits(b["k_pool"]))
+    assert np.array_equal(bits(a["v_pool"]), bits(b["v_pool"]))
+    assert np.array_equal(bits(ref_out), bits(out))
+    check_close(out, oracle_step(w, w.k_pool, w.v_pool), w.dtype, f"decode step config{cid}")
+
+
+def test_decode_step_edge_rows():
+    # Zero length: nothing appended, zeros out.  A block id outside the pool at
+    # the append slot: nothing written there, NaN out.  Others as usual.
+    w = workloads.make_workload(3, batch=5, len_range=(20, 900))
+    dev = to_dev(w)
+    lens = w.lens.copy()
+    lens[1] = 0
+    tables = w.tables.copy()
+    tables[3, (int(lens[3]) - 1) // w.block_size] = w.num_blocks + 5
+    before = dev["k_pool"].clone()
+    out = torch.full_like(dev["q"], 7.0)
+    pkv.paged_decode_step(out, dev["q"], dev["k_pool"], dev["v_pool"], dev["k_new"],
+                          dev["v_new"], torch.as_tensor(tables, device="cuda"),
+                          torch.as_tensor(lens, device="cuda"), scale=w.scale)
+    torch.cuda.synchronize()
+    o = out.float().cpu()
+    assert (o[1] == 0).all()
+    assert torch.isnan(o[3]).all()
+    for s in (0, 2, 4):
+        assert torch.isfinite(o[s]).all()
+    # Only the three live sequences' append slots changed.
+    changed = (bits(dev["k_pool"]) != bits(before)).reshape(w.num_blocks * w.block_size, -1).any(1)
+    slots = sorted(int(tables[s, (int(lens[s]) - 1) // w.block_size]) * w.block_size +
+                   (int(lens[s]) - 1) % w.block_size for s in (0, 2, 4))
+    assert np.nonzero(changed)[0].tolist() == slots
+
+
 def test_deterministic_and_relabelling_invariant():
     w = workloads.make_workload(3, batch=4, len_range=(100, 1500))
     dev = to_dev(w)

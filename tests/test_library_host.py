@@ -78,6 +78,16 @@ def test_attention_rejects_bad_arguments(kw, code):
     assert attn(**kw) == code
 
 
+def test_decode_step_needs_the_new_tokens():
+    a = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 16, 16, 8, 2, 128, 0.1, 0, FAKE, 1 << 30, 2, None]
+    lib_step = lib.paged_decode_step
+    # kernel, out, q, k_pool, v_pool, k_new, v_new, tables, ...
+    assert lib_step(0, a[0], a[1], a[2], a[3], None, FAKE, *a[4:]) == pkv.PKV_ERR_INVALID_ARG
+    assert lib_step(0, a[0], a[1], a[2], a[3], FAKE, None, *a[4:]) == pkv.PKV_ERR_INVALID_ARG
+    a[7] = 0   # no sequences: nothing to do, nothing checked
+    assert lib_step(0, a[0], a[1], a[2], a[3], None, None, *a[4:]) == pkv.PKV_OK
+
+
 def test_zero_sequences_is_a_noop():
     assert attn(s=0) == pkv.PKV_OK
     assert lib.paged_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, 16, 16, 2, 128, 2, None) == 0
