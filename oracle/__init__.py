@@ -29,6 +29,7 @@ Modules:
                 the block-wise online-softmax recurrence and the
                 log-sum-exp merge of partition states
   cache_ops     cache append and block copy on pool copies
+  fp8           E4M3FN codes for FP8 cache blocks: encode, decode, append
   block_manager free list, reference counts, fork and copy-on-write
   allocator_toy contiguous-reservation vs paged accounting of a toy workload
 
@@ -37,4 +38,4 @@ values printed on the pages, closed forms, brute force or an independent
 library routine; none is "parity unpinned".
 """
 
-from . import paging, attention, cache_ops, block_manager, allocator_toy  # noqa: F401
+from . import paging, attention, cache_ops, block_manager, allocator_toy, fp8  # noqa: F401
