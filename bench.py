@@ -56,6 +56,8 @@ def parse_args(argv=None):
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="0 = balanced ranges; > 0 = also cap each range at this many tokens")
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
+    ap.add_argument("--kv-dtype", choices=["native", "fp8"], default="native",
+                    help="fp8: E4M3FN pools with per-pool scales (q / out keep the config dtype)")
     ap.add_argument("--cache-kv", choices=["auto", "on", "off"], default="auto",
                     help="PKV_ATTN_CACHE_KV: auto = on when the tables share blocks")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -123,7 +125,8 @@ def main(argv=None) -> int:
     if args.block_size:
         kw["block_size"] = args.block_size
     t0 = time.time()
-    w = workloads.make_workload(args.config, device=dev, **kw)
+    fp8 = args.kv_dtype == "fp8"
+    w = workloads.make_workload(args.config, device=dev, kv_fp8=fp8, **kw)
     torch.cuda.synchronize()
     print(f"# workload {w.name}: {w.num_seqs} seqs, tokens={int(w.lens.sum())}, "
           f"blocks={w.num_blocks}, drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -137,12 +140,13 @@ def main(argv=None) -> int:
     cpu_inputs = (workloads.extract_sequences(w, cpu_sample, dtype=np.float32)
                   if args.cpu_seconds > 0 else None)
 
-    esize = w.k_pool.element_size()
+    esize = w.k_pool.element_size()     # 1 for FP8 pools
+    qsize = w.q.element_size()
     S, Hq, Hkv, D, B = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     lens64 = w.lens.astype(np.int64)
     kv_bytes = int(lens64.sum()) * Hkv * D * 2 * esize
     table_bytes = int(sum(-(-int(L) // B) for L in lens64)) * 4
-    alg_bytes = kv_bytes + 2 * S * Hq * D * esize + table_bytes + S * 4
+    alg_bytes = kv_bytes + 2 * S * Hq * D * qsize + table_bytes + S * 4
 
     tables = torch.as_tensor(w.tables, device=dev)
     lens = torch.as_tensor(w.lens, device=dev)
@@ -163,7 +167,17 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream()
 
     def append():
-        pkv.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens_pre, stream=stream)
+        if fp8:
+            pkv.paged_kv_append_fp8(w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens_pre,
+                                    w.k_scale, w.v_scale, stream=stream)
+        else:
+            pkv.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens_pre,
+                                stream=stream)
+
+    def attention_fp8():
+        pkv.paged_decode_attention_fp8(out, w.q, w.k_pool, w.v_pool, tables, lens, w.k_scale,
+                                       w.v_scale, kernel=kernel, scale=w.scale,
+                                       partition_tokens=P, workspace=ws, stream=stream)
 
     def plan():
         pkv.paged_decode_attention_plan(kernel, out, w.q, w.k_pool, w.v_pool, tables, lens,
@@ -182,15 +196,22 @@ def main(argv=None) -> int:
 
     def step():
         # Append + attention; the append rides in the plan launch.
-        pkv.paged_decode_step(out, w.q, w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens,
-                              kernel=kernel, scale=w.scale, partition_tokens=P, workspace=ws,
-                              stream=stream)
+        if fp8:
+            pkv.paged_decode_step_fp8(out, w.q, w.k_pool, w.v_pool, w.k_new, w.v_new, tables,
+                                      lens, w.k_scale, w.v_scale, kernel=kernel, scale=w.scale,
+                                      partition_tokens=P, workspace=ws, stream=stream)
+        else:
+            pkv.paged_decode_step(out, w.q, w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens,
+                                  kernel=kernel, scale=w.scale, partition_tokens=P,
+                                  workspace=ws, stream=stream)
+
+    # FP8 pools have no phase-by-phase entry points: their breakdown times the
+    # whole attention call as one phase (so its roofline is conservative).
+    phases = [append, attention_fp8] if fp8 else [append, plan, partitions, merge]
 
     for _ in range(args.warmup):
-        append()
-        plan()
-        partitions()
-        merge()
+        for ph in phases:
+            ph()
         step()
     torch.cuda.synchronize()
     print(f"# warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
@@ -211,23 +232,22 @@ def main(argv=None) -> int:
     # append as its own launch (event records add a few microseconds of gap
     # each, so the phases sum to more than ms_step).  The partition kernel's
     # time here is the roofline's.
-    marks = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    marks = [[ev() for _ in range(len(phases) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for m in marks:
         m[0].record(stream)
-        append()
-        m[1].record(stream)
-        plan()
-        m[2].record(stream)
-        partitions()
-        m[3].record(stream)
-        merge()
-        m[4].record(stream)
+        for i, ph in enumerate(phases):
+            ph()
+            m[i + 1].record(stream)
     torch.cuda.synchronize()
     t_app = [m[0].elapsed_time(m[1]) for m in marks]
-    t_plan = [m[1].elapsed_time(m[2]) for m in marks]
-    t_part = [m[2].elapsed_time(m[3]) for m in marks]
-    t_merge = [m[3].elapsed_time(m[4]) for m in marks]
+    if fp8:
+        t_part = [m[1].elapsed_time(m[2]) for m in marks]
+        t_plan = t_merge = [0.0]
+    else:
+        t_plan = [m[1].elapsed_time(m[2]) for m in marks]
+        t_part = [m[2].elapsed_time(m[3]) for m in marks]
+        t_merge = [m[3].elapsed_time(m[4]) for m in marks]
     part_ms = statistics.mean(t_part)
     print(f"# timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, partition {part_ms * 1e3:.1f} us",
           file=sys.stderr, flush=True)
@@ -259,13 +279,23 @@ def main(argv=None) -> int:
               file=sys.stderr, flush=True)
         del calib, calib_out
 
+    def oracle_append(c):
+        """Oracle append on host copies; FP8 pools are appended as codes and
+        decoded (value = code * scale)."""
+        from oracle import cache_ops as o_cache
+        from oracle import fp8 as o_fp8
+        if not fp8:
+            return o_cache.append_token(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
+                                        c["tables"], c["lens_pre"], B)
+        kc, vc = o_fp8.append_token_fp8(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
+                                        c["tables"], c["lens_pre"], B, w.k_scale, w.v_scale)
+        return o_fp8.dequantise(kc, w.k_scale), o_fp8.dequantise(vc, w.v_scale)
+
     parity = None
     if check_inputs is not None:
         from oracle import attention as o_attn
-        from oracle import cache_ops as o_cache
         c = check_inputs
-        kp, vp = o_cache.append_token(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
-                                      c["tables"], c["lens_pre"], B)
+        kp, vp = oracle_append(c)
         ref = o_attn.decode_attention(c["q"], kp, vp, c["tables"], c["lens"], B, w.scale)
         got = out[torch.as_tensor(check_seqs, device=dev)].double().cpu().numpy()
         err = np.abs(got - ref)
@@ -281,15 +311,13 @@ def main(argv=None) -> int:
     if cpu_inputs is not None:
         import threadpoolctl
         from oracle import attention as o_attn
-        from oracle import cache_ops as o_cache
         c = cpu_inputs
         sample_kv = int(c["lens"].astype(np.int64).sum()) * Hkv * D * 2 * esize
         passes, spent = 0, 0.0
         with threadpoolctl.threadpool_limits(1):
             while spent < args.cpu_seconds:
                 t = time.perf_counter()
-                kp, vp = o_cache.append_token(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
-                                              c["tables"], c["lens_pre"], B)
+                kp, vp = oracle_append(c)
                 o_attn.decode_attention(c["q"], kp, vp, c["tables"], c["lens"], B, w.scale)
                 spent += time.perf_counter() - t
                 passes += 1
@@ -305,7 +333,8 @@ def main(argv=None) -> int:
     attn_ms = statistics.mean(t_plan) + statistics.mean(t_part) + statistics.mean(t_merge)
     achieved = alg_bytes / (part_ms * 1e-3) / 1e9
     kname = {"auto": "mfma" if w.dtype != "f32" and D >= 32 else "valu"}.get(args.kernel, args.kernel)
-    traffic = measured_traffic(w.name + (f"_B{B}" if args.config == 5 else ""), kname)
+    traffic = (None if fp8 else
+               measured_traffic(w.name + (f"_B{B}" if args.config == 5 else ""), kname))
     result = {
         "metric": "paged decode attention KV GB/s (% of HBM peak) + seq-layer steps/s",
         "value": round(kv_gbps_step, 2),
@@ -323,7 +352,7 @@ def main(argv=None) -> int:
                    "name": w.name, "batch": S, "block_size": B, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "tokens": int(lens64.sum()),
                    "partition_tokens": P, "kernel": kname, "shared_blocks": shared,
-                   "cache_kv": cache_kv},
+                   "cache_kv": cache_kv, "kv_dtype": "fp8_e4m3" if fp8 else w.dtype},
         "pct_of_hbm_peak": round(100 * kv_gbps_step / HBM_PEAK_GBPS, 2),
         "seq_layer_steps_per_s": round(S / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
@@ -337,7 +366,8 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": f"attn_partition_{kname}",
+                     "kernel": ("attention launches (plan + partitions + merge)" if fp8
+                                else f"attn_partition_{kname}"),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "copy_gbps": round(copy_gbps, 1) if copy_gbps else None,
         "parity": parity,

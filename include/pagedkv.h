@@ -54,7 +54,9 @@
 extern "C" {
 #endif
 
-typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 } pkv_dtype;
+/* PKV_FP8_E4M3: pool element type only (the FP8 entry points below, and the
+ * byte moves append / copy / gather): OCP E4M3FN codes, one byte each. */
+typedef enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2, PKV_FP8_E4M3 = 3 } pkv_dtype;
 
 enum pkv_status {
   PKV_OK = 0,
@@ -274,6 +276,64 @@ int paged_decode_step(int kernel, void* out, const void* q, void* k_pool, void* 
                       int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
                       int head_dim, float scale, int partition_tokens, void* workspace,
                       size_t workspace_bytes, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------- */
+/* FP8 cache blocks                                                           */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [pofe] "Fine-tuned models and adapters": an FP8 cache halves the bytes per
+ * block and nothing else about paging changes; [pofe] "Failure modes": once
+ * the cache dominates step time, fewer bytes per token is the lever.  The
+ * pages fix no format or scale; this library uses:
+ *   - codes: OCP E4M3FN (bias 7, 3 mantissa bits, no infinities,
+ *     S.1111.111 = NaN, largest finite 448), PKV_FP8_E4M3 pools;
+ *   - one float32 scale per pool (k_scale for K, v_scale for V): a code c
+ *     stands for decode(c) * scale, and a value x is stored as
+ *     encode(fp32(x) / fp32(scale)), nearest with ties to even, magnitudes
+ *     >= 448 saturating to +-448, NaN kept (0x7F, or 0xFF for a negative
+ *     sign bit).
+ * Scales must be finite and > 0 (else PKV_ERR_INVALID_ARG).  Pools are laid
+ * out as the 16-bit pools, one byte per element; copy and gather move FP8
+ * pools like any other (dtype PKV_FP8_E4M3).
+ */
+
+/* paged_kv_append_fp8 - paged_kv_append into FP8 pools: k_new, v_new
+ * [num_seqs, num_kv_heads, head_dim] of new_dtype (F32, F16 or BF16) are
+ * quantised as above.  Same slot rules and padding rows as paged_kv_append. */
+int paged_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                        const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* context_lens_pre, int num_seqs, int num_blocks,
+                        int block_size, int num_kv_heads, int head_dim, int new_dtype,
+                        float k_scale, float v_scale, void* stream);
+
+/* paged_decode_attention_fp8 - paged_decode_attention_with over FP8 pools:
+ * the key of token t is decode(code) * k_scale, its value decode(code) *
+ * v_scale.  q and out have element type dtype (F16 or BF16; F32 gives
+ * PKV_ERR_UNSUPPORTED), head_dim >= 32, and the matrix-core kernel runs
+ * (PKV_ATTN_VALU gives PKV_ERR_UNSUPPORTED).  Codes are decoded exactly into
+ * the 16-bit operands; k_scale is folded into the softmax scale and v_scale
+ * applied to the weighted sum, both in fp32.  Workspace as
+ * paged_decode_workspace_bytes. */
+int paged_decode_attention_fp8(int kernel, void* out, const void* q, const void* k_pool,
+                               const void* v_pool, const int32_t* block_tables,
+                               int max_blocks_per_seq, const int32_t* context_lens,
+                               int num_seqs, int num_blocks, int block_size, int num_q_heads,
+                               int num_kv_heads, int head_dim, float scale, float k_scale,
+                               float v_scale, int partition_tokens, void* workspace,
+                               size_t workspace_bytes, int dtype, void* stream);
+
+/* paged_decode_step_fp8 - paged_decode_step over FP8 pools: token L-1 (k_new,
+ * v_new in dtype) is quantised into its slot as paged_kv_append_fp8 does,
+ * then paged_decode_attention_fp8 runs; equivalent bit for bit to the two
+ * calls on one stream. */
+int paged_decode_step_fp8(int kernel, void* out, const void* q, void* k_pool, void* v_pool,
+                          const void* k_new, const void* v_new, const int32_t* block_tables,
+                          int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                          int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
+                          int head_dim, float scale, float k_scale, float v_scale,
+                          int partition_tokens, void* workspace, size_t workspace_bytes,
+                          int dtype, void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Host block manager (CPU only; no device calls)                            */

@@ -32,11 +32,12 @@ PKV_ERR_NO_FREE_BLOCK = -3
 PKV_ERR_WORKSPACE = -4
 PKV_ERR_HIP = -5
 
-PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 PKV_ATTN_AUTO, PKV_ATTN_VALU, PKV_ATTN_MFMA = 0, 1, 2
 PKV_ATTN_CACHE_KV = 16   # flag: blocks shared between sequences (see include/pagedkv.h)
 
-_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+_DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
+               torch.float8_e4m3fn: PKV_FP8_E4M3}   # FP8: pools only (E4M3FN codes)
 
 _i32 = ctypes.c_int
 _p = ctypes.c_void_p
@@ -67,6 +68,13 @@ _sig("paged_decode_attention_plan", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_attention_partitions", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_attention_merge", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_step", _i32, [_i32, _p, _p, _p, _p, _p, _p] + _ATTN_ARGS[4:])
+_f32 = ctypes.c_float
+_sig("paged_kv_append_fp8", _i32,
+     [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _p])
+# FP8 attention: the 16-bit argument list with k_scale, v_scale after scale.
+_ATTN_ARGS_FP8 = _ATTN_ARGS[:14] + [_f32, _f32] + _ATTN_ARGS[14:]
+_sig("paged_decode_attention_fp8", _i32, [_i32] + _ATTN_ARGS_FP8)
+_sig("paged_decode_step_fp8", _i32, [_i32, _p, _p, _p, _p, _p, _p] + _ATTN_ARGS_FP8[4:])
 _sig("pkv_validate_tables", _i32, [_p, _i32, _p, _i32, _i32, _i32, _intp])
 _sig("pkv_bm_create", _i32, [_i32, _i32, ctypes.POINTER(_p)])
 _sig("pkv_bm_destroy", None, [_p])
@@ -198,8 +206,12 @@ def paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_le
 
 
 def _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partition_tokens,
-               workspace, stream):
+               workspace, stream, io_dtype=None):
     n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    io_dtype = k_pool.dtype if io_dtype is None else io_dtype
+    if io_dtype not in _DTYPE_CODE or _DTYPE_CODE[io_dtype] == PKV_FP8_E4M3:
+        raise TypeError(f"q / out dtype {io_dtype} is not supported")
+    dt = _DTYPE_CODE[io_dtype]
     s, hq, dq = q.shape
     if dq != d or out.shape != q.shape:
         raise ValueError("q and out must be [num_seqs, num_q_heads, head_dim]")
@@ -212,7 +224,7 @@ def _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partit
         need = paged_decode_workspace_bytes(s, hq, d, mb * b, partition_tokens)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace", torch.uint8)
-    return (_dev(out, "out", k_pool.dtype), _dev(q, "q", k_pool.dtype), _dev(k_pool, "k_pool"),
+    return (_dev(out, "out", io_dtype), _dev(q, "q", io_dtype), _dev(k_pool, "k_pool"),
             _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32), mb,
             _dev(context_lens, "context_lens", torch.int32), s, n, b, hq, h, d, float(scale),
             int(partition_tokens), ws_ptr, workspace.numel(), dt, _stream(stream))
@@ -399,3 +411,61 @@ class BlockManager:
         _check(_lib.pkv_bm_export_tables(self._h, ids.data_ptr(), n, out.data_ptr(), ld,
                                          lens.data_ptr()), "pkv_bm_export_tables")
         return out, lens
+
+
+# --- FP8 (E4M3FN) pools -----------------------------------------------------------
+
+def _fp8_pools(k_pool, v_pool):
+    if k_pool.dtype != torch.float8_e4m3fn or v_pool.dtype != torch.float8_e4m3fn:
+        raise TypeError("FP8 entry points take torch.float8_e4m3fn pools")
+
+
+def paged_kv_append_fp8(k_pool, v_pool, k_new, v_new, block_tables, context_lens_pre, k_scale,
+                        v_scale, *, stream=None):
+    """Quantise one new token per sequence, code = e4m3(x / scale) (nearest,
+    ties to even, saturating), into slot len % B of block table[len / B] of
+    FP8 pools.  k_new / v_new: float32, float16 or bfloat16 [S, H_kv, D]."""
+    _fp8_pools(k_pool, v_pool)
+    n, b, h, d, _ = _pool_dims(k_pool, v_pool)
+    s = k_new.shape[0]
+    if k_new.shape != (s, h, d) or v_new.shape != (s, h, d) or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must be [num_seqs, kv_heads, head_dim] of one dtype")
+    if k_new.dtype not in _DTYPE_CODE or _DTYPE_CODE[k_new.dtype] == PKV_FP8_E4M3:
+        raise TypeError(f"new-token dtype {k_new.dtype} is not supported")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens_pre.shape != (s,):
+        raise ValueError("block_tables [num_seqs, max_blocks] and context_lens_pre [num_seqs]")
+    _check(_lib.paged_kv_append_fp8(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+        _dev(v_new, "v_new"), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens_pre, "context_lens_pre", torch.int32), s, n, b,
+        h, d, _DTYPE_CODE[k_new.dtype], float(k_scale), float(v_scale), _stream(stream)),
+        "paged_kv_append_fp8")
+
+
+def paged_decode_attention_fp8(out, q, k_pool, v_pool, block_tables, context_lens, k_scale,
+                               v_scale, *, kernel=0, scale=None, partition_tokens=0,
+                               workspace=None, stream=None):
+    """Decode attention over FP8 pools (value = code * scale); q and out are
+    float16 or bfloat16.  Other arguments as paged_decode_attention."""
+    _fp8_pools(k_pool, v_pool)
+    a = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partition_tokens,
+                   workspace, stream, io_dtype=q.dtype)
+    _check(_lib.paged_decode_attention_fp8(int(kernel), *a[:14], float(k_scale), float(v_scale),
+                                           *a[14:]), "paged_decode_attention_fp8")
+
+
+def paged_decode_step_fp8(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens,
+                          k_scale, v_scale, *, kernel=0, scale=None, partition_tokens=0,
+                          workspace=None, stream=None):
+    """paged_decode_step for FP8 pools: the append quantises token L-1 (k_new,
+    v_new in q's dtype) as paged_kv_append_fp8 does, then FP8 attention."""
+    _fp8_pools(k_pool, v_pool)
+    a = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partition_tokens,
+                   workspace, stream, io_dtype=q.dtype)
+    s, h, d = q.shape[0], k_pool.shape[2], k_pool.shape[3]
+    if k_new.shape != (s, h, d) or v_new.shape != (s, h, d):
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    _check(_lib.paged_decode_step_fp8(int(kernel), a[0], a[1], a[2], a[3],
+                                      _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype),
+                                      *a[4:14], float(k_scale), float(v_scale), *a[14:]),
+           "paged_decode_step_fp8")

@@ -145,7 +145,10 @@ struct AttnParams {
   int off_short;    // and of the merge task lists
   int off_long;
   int task_seg;     // task-list entries per plan workgroup
-  float scale_log2;  // scale * log2(e): scores live in log2 units
+  float scale_log2;  // scale * log2(e) (* k_scale for FP8 pools): scores in log2 units
+  int kv_fp8;        // pools hold E4M3FN codes
+  float k_scale;     // FP8 pools: value = code * scale (the decode-step append divides)
+  float v_scale;     // multiplies the weighted V sum (1 unless FP8)
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -262,7 +265,10 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
   // thread, spread over the plan workgroups.  The partition launch that
   // follows on the stream reads it from the pool.
   if (p.k_new) {
-    const int row_chunks = p.num_kv_heads * p.head_dim * T::bytes / 16;
+    // One 16-byte chunk of the new row (16 / sizeof(T) elements) per thread;
+    // FP8 pools get its codes, encode(x / scale), as in paged_kv_append_fp8.
+    constexpr int E = 16 / T::bytes;
+    const int row_chunks = p.num_kv_heads * p.head_dim / E;
     for (long long i = (long long)b * kPlanThreads + tid; i < (long long)S_ * row_chunks;
          i += kPlanGroups * kPlanThreads) {
       const int s = (int)(i / row_chunks);
@@ -271,11 +277,30 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
       if (L <= 0 || L > max_len) continue;
       const int blk = p.tables[(size_t)s * p.max_blocks + ((L - 1) >> p.log2_b)];
       if (!valid_block(blk, p.num_blocks)) continue;
-      const size_t dst = row_offset(blk, L - 1, p.log2_b, p.num_kv_heads, 0, p.head_dim) * T::bytes +
-                         16 * (size_t)ch;
-      const size_t src = (size_t)s * row_chunks * 16 + 16 * (size_t)ch;
-      store16((char*)p.k_pool + dst, load16(p.k_new + src));
-      store16((char*)p.v_pool + dst, load16(p.v_new + src));
+      const size_t elem = row_offset(blk, L - 1, p.log2_b, p.num_kv_heads, 0, p.head_dim) +
+                          (size_t)E * ch;
+      const size_t src = ((size_t)s * row_chunks + ch) * 16;
+      if (p.kv_fp8) {
+        if constexpr (E == 8) {
+          float kf[8], vf[8];
+          Cvt<T>::unpack(load16(p.k_new + src), kf);
+          Cvt<T>::unpack(load16(p.v_new + src), vf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kf[e] = kf[e] / p.k_scale;
+            vf[e] = vf[e] / p.v_scale;
+          }
+          *reinterpret_cast<uint2*>((char*)p.k_pool + elem) =
+              make_uint2(e4m3_encode4(kf[0], kf[1], kf[2], kf[3]),
+                         e4m3_encode4(kf[4], kf[5], kf[6], kf[7]));
+          *reinterpret_cast<uint2*>((char*)p.v_pool + elem) =
+              make_uint2(e4m3_encode4(vf[0], vf[1], vf[2], vf[3]),
+                         e4m3_encode4(vf[4], vf[5], vf[6], vf[7]));
+        }
+      } else {
+        store16((char*)p.k_pool + elem * T::bytes, load16(p.k_new + src));
+        store16((char*)p.v_pool + elem * T::bytes, load16(p.v_new + src));
+      }
     }
   }
 
@@ -536,7 +561,7 @@ __device__ __forceinline__ WaveKv wave_kv(const AttnParams& p, int qd, int kw) {
 // (m, l, o) states of waves w0 .. w0+n-1 held in LDS.  Writes the final
 // output when the segment is the whole sequence, else the partial state
 // (M, weighted l, weighted o) of slot (pair, kw, h).
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool kScaleV>
 __device__ __forceinline__ void emit_item(const AttnParams& p, const Segment& sg, const WaveKv& kv,
                                           int kw, int w0, int n, int h, int d, int bad,
                                           const float (*red_m)[G], const float (*red_l)[G],
@@ -557,6 +582,12 @@ __device__ __forceinline__ void emit_item(const AttnParams& p, const Segment& sg
     den += wgt * red_l[w0 + j][h];
   }
   const float nan = __builtin_nanf("");
+  if constexpr (kScaleV) {   // FP8 pools: the V codes' scale
+    num.x *= p.v_scale;
+    num.y *= p.v_scale;
+    num.z *= p.v_scale;
+    num.w *= p.v_scale;
+  }
   if (sg.final) {
     S* o = (S*)p.out + ((size_t)sg.s * p.num_q_heads + kv.h0 + h) * D + d;
     const float inv = 1.f / den;
@@ -578,7 +609,7 @@ __device__ __forceinline__ void emit_item(const AttnParams& p, const Segment& sg
 // End of a segment, after each wave has put its (m, l, o) in LDS slot w.
 // One wave per KV-head group: the wave writes its own results, no barrier.
 // Several waves per group: the workgroup combines them after a barrier.
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool kScaleV = false>
 __device__ __forceinline__ void finish_segment(const AttnParams& p, const Segment& sg, int w,
                                                int bad, const float (*red_m)[G],
                                                const float (*red_l)[G],
@@ -591,7 +622,8 @@ __device__ __forceinline__ void finish_segment(const AttnParams& p, const Segmen
     if (kv.live) {
       for (int it = threadIdx.x & 63; it < kv.nh * D4; it += 64) {
         const int h = it / D4;
-        emit_item<T, D, G>(p, sg, kv, w, w, 1, h, (it - h * D4) * 4, any_bad, red_m, red_l, red_acc);
+        emit_item<T, D, G, kScaleV>(p, sg, kv, w, w, 1, h, (it - h * D4) * 4, any_bad, red_m,
+                                    red_l, red_acc);
       }
     }
     wave_lds_sync();   // the wave's LDS slot is rewritten by its next segment
@@ -610,8 +642,8 @@ __device__ __forceinline__ void finish_segment(const AttnParams& p, const Segmen
       const int h = r / D4;
       const WaveKv kv = wave_kv(p, sg.qd, kw);
       if (h < kv.nh)
-        emit_item<T, D, G>(p, sg, kv, kw, kw * p.wpk, p.wpk, h, (r - h * D4) * 4, any_bad, red_m,
-                           red_l, red_acc);
+        emit_item<T, D, G, kScaleV>(p, sg, kv, kw, kw * p.wpk, p.wpk, h, (r - h * D4) * 4,
+                                    any_bad, red_m, red_l, red_acc);
     }
     lds_barrier();   // the LDS buffers (and bad_lds) are reused by the next segment
   }
@@ -644,22 +676,45 @@ __device__ __forceinline__ uint4 load_kv(const char* p) {
   if constexpr (kStream) return load16_stream(p);
   else return load16(p);
 }
+template <bool kStream>
+__device__ __forceinline__ uint2 load_kv8(const char* p) {
+  if constexpr (kStream) return load8_stream(p);
+  else return load8(p);
+}
+
+// 8 pool elements as 8 elements of T: the identity for 16-bit pools; for FP8
+// pools the exact decode of 8 codes, each value representable in T.
+template <typename T>
+__device__ __forceinline__ uint4 expand8(const uint4& v) { return v; }
+template <typename T>
+__device__ __forceinline__ uint4 expand8(const uint2& c) {
+  float f[8];
+  e4m3_decode4(c.x, f);
+  e4m3_decode4(c.y, f + 4);
+  return make_uint4(Pair<T>::pack(f[0], f[1]), Pair<T>::pack(f[2], f[3]),
+                    Pair<T>::pack(f[4], f[5]), Pair<T>::pack(f[6], f[7]));
+}
 
 // ---------------------------------------------------------------------------
 // MFMA partition kernel (fp16 / bf16).
 // ---------------------------------------------------------------------------
-template <typename T, int D, int G, bool kStream>
+template <typename T, int D, int G, bool kStream, bool kF8>
 __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnParams p) {
   using S = typename T::storage;
+  // A lane loads 8 elements of a K or V row at a time: 16 bytes of a 16-bit
+  // pool, 8 bytes of an FP8 pool (decoded to T on use).
+  using KvReg = typename std::conditional<kF8, uint2, uint4>::type;
+  constexpr int KVB = kF8 ? 1 : T::bytes;   // bytes per pool element
   constexpr int KCH = D / 32;        // MFMA k-chunks of 32 channels
-  constexpr int LPR = D / 8;         // lanes per V row (16 bytes each)
-  constexpr int RPL = 64 / LPR;      // V rows per load instruction
-  constexpr int TPR = kTile / RPL;   // tokens per V row group per tile
+  constexpr int LPR = D / 8;         // lanes per K/V row (8 elements each)
+  constexpr int RPL = 64 / LPR;      // rows per load instruction
+  constexpr int TPR = kTile / RPL;   // tokens per row group per tile
   // Tiles in flight per wave: three when the accumulator is large (G >= 4:
   // occupancy is register bound at two waves per SIMD anyway) and a slot
   // costs <= 32 registers; otherwise two, which keeps small groups at a
   // higher occupancy.
-  constexpr int kSlots = ((KCH + TPR) * 4 <= 32 && G >= 4) ? 3 : 2;
+  constexpr int kSlotRegs = 2 * TPR * (int)(sizeof(KvReg) / 4);
+  constexpr int kSlots = (kSlotRegs <= 32 && G >= 4) ? 3 : 2;
   static_assert(D % 32 == 0 && TPR >= 1 && G <= kMaxGroup && G * D <= kMaxGD, "shape");
 
   // Probabilities of the current tile per head: fp32 for the FMA form,
@@ -687,9 +742,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;     // A row (token of tile) / B and C column (head)
   const int kgrp = lane >> 4;    // k group of A and B; C rows 4*kgrp .. 4*kgrp+3
-  const int vc = lane % LPR;     // V: 16-byte chunk within the row
-  const int vr = lane / LPR;     // V: row group, tokens TPR*vr .. TPR*vr+TPR-1
-  const size_t bytes = T::bytes;
+  const int vc = lane % LPR;     // K/V: 8-element chunk within the row
+  const int vr = lane / LPR;     // K/V: row group, tokens TPR*vr .. TPR*vr+TPR-1
+  const size_t bytes = KVB;
   // KV-head group kw of the quad; with several waves per group, sub-wave sw
   // takes every wpk-th tile.
   const int kw = w / p.wpk;
@@ -714,7 +769,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
     const int tile_end = sg.t0 + sg.take;
     // Register ring: while one tile is consumed the next kSlots - 1 are in
     // flight.
-    uint4 kb[kSlots][TPR], vb[kSlots][TPR];
+    KvReg kb[kSlots][TPR], vb[kSlots][TPR];
+    auto ld = [&](const char* a) {
+      if constexpr (kF8) return load_kv8<kStream>(a);
+      else return load_kv<kStream>(a);
+    };
     auto issue = [&](auto slot, int tile) {
       constexpr int SL = decltype(slot)::value;
       // Past the segment's last tile the slot is never consumed: load nothing.
@@ -736,8 +795,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
 #pragma unroll
         for (int i = 0; i < TPR; ++i) {
           const uint32_t o = (uint32_t)min(TPR * vr + i, rlim) * rstride + vc * 8 * bytes;
-          kb[SL][i] = load_kv<kStream>(kbase + o);
-          vb[SL][i] = load_kv<kStream>(vbase + o);
+          kb[SL][i] = ld(kbase + o);
+          vb[SL][i] = ld(vbase + o);
         }
       } else {
         auto row = [&](int t, int ch) -> size_t {
@@ -748,8 +807,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
 #pragma unroll
         for (int i = 0; i < TPR; ++i) {
           const size_t o = row(tb + TPR * vr + i, vc * 8);
-          kb[SL][i] = load_kv<kStream>(p.k_pool + o);
-          vb[SL][i] = load_kv<kStream>(p.v_pool + o);
+          kb[SL][i] = ld(p.k_pool + o);
+          vb[SL][i] = ld(p.v_pool + o);
         }
       }
     };
@@ -770,7 +829,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
 #pragma unroll
       for (int i = 0; i < TPR; ++i) {
         const int r = TPR * vr + i;
-        k_lds[w][r * LPR + (vc ^ kswz(r))] = kb[SL][i];
+        k_lds[w][r * LPR + (vc ^ kswz(r))] = expand8<T>(kb[SL][i]);
       }
       wave_lds_sync();
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -830,11 +889,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
         uint32_t vp[NP][8];           // channel e of tokens (2k, 2k+1)
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-          const uint4 a = vb[SL][2 * k], b = vb[SL][2 * k + 1];
-          vp[k][0] = pair_lo(a.x, b.x); vp[k][1] = pair_hi(a.x, b.x);
-          vp[k][2] = pair_lo(a.y, b.y); vp[k][3] = pair_hi(a.y, b.y);
-          vp[k][4] = pair_lo(a.z, b.z); vp[k][5] = pair_hi(a.z, b.z);
-          vp[k][6] = pair_lo(a.w, b.w); vp[k][7] = pair_hi(a.w, b.w);
+          if constexpr (kF8) {
+            // Decode both tokens' codes and pack the pairs directly.
+            float fa[8], fb[8];
+            e4m3_decode4(vb[SL][2 * k].x, fa);
+            e4m3_decode4(vb[SL][2 * k].y, fa + 4);
+            e4m3_decode4(vb[SL][2 * k + 1].x, fb);
+            e4m3_decode4(vb[SL][2 * k + 1].y, fb + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) vp[k][e] = Pair<T>::pack(fa[e], fb[e]);
+          } else {
+            const uint4 a = vb[SL][2 * k], b = vb[SL][2 * k + 1];
+            vp[k][0] = pair_lo(a.x, b.x); vp[k][1] = pair_hi(a.x, b.x);
+            vp[k][2] = pair_lo(a.y, b.y); vp[k][3] = pair_hi(a.y, b.y);
+            vp[k][4] = pair_lo(a.z, b.z); vp[k][5] = pair_hi(a.z, b.z);
+            vp[k][6] = pair_lo(a.w, b.w); vp[k][7] = pair_hi(a.w, b.w);
+          }
         }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
@@ -849,7 +919,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
       } else {
         float vf[TPR][8];
 #pragma unroll
-        for (int i = 0; i < TPR; ++i) Cvt<T>::unpack(vb[SL][i], vf[i]);
+        for (int i = 0; i < TPR; ++i) Cvt<T>::unpack(expand8<T>(vb[SL][i]), vf[i]);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float ph[TPR];
@@ -923,7 +993,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
       red_m[w][col] = m_run;
       red_l[w][col] = l_run;
     }
-    finish_segment<T, D, G>(p, sg, w, bad, red_m, red_l, red_acc);
+    finish_segment<T, D, G, kF8>(p, sg, w, bad, red_m, red_l, red_acc);
   });
 }
 
@@ -1338,51 +1408,56 @@ inline int pow2_at_least(int x) {
   return r;
 }
 
-template <typename T, int D, int G, bool kStream>
+template <typename T, int D, int G, bool kStream, bool kF8>
 const void* partition_fn(int family) {
   if (family == kFamilyMfma) {
     if constexpr (!std::is_same<T, F32>::value && D >= 32 && G * D <= kMaxGD && (D < 256 || G <= 2))
-      return reinterpret_cast<const void*>(&attn_partition_mfma<T, D, G, kStream>);
-  } else {
+      return reinterpret_cast<const void*>(&attn_partition_mfma<T, D, G, kStream, kF8>);
+  } else if constexpr (!kF8) {
     if constexpr (G * D <= kMaxGD && (std::is_same<T, F32>::value || G <= 4))
       return reinterpret_cast<const void*>(&attn_partition_valu<T, D, G, kStream>);
   }
   return nullptr;
 }
 
-template <typename T, int D, bool kStream>
+template <typename T, int D, bool kStream, bool kF8>
 const void* partition_fn_g(int family, int G) {
   switch (G) {
-    case 1: return partition_fn<T, D, 1, kStream>(family);
-    case 2: return partition_fn<T, D, 2, kStream>(family);
-    case 4: return partition_fn<T, D, 4, kStream>(family);
-    default: return partition_fn<T, D, 8, kStream>(family);
+    case 1: return partition_fn<T, D, 1, kStream, kF8>(family);
+    case 2: return partition_fn<T, D, 2, kStream, kF8>(family);
+    case 4: return partition_fn<T, D, 4, kStream, kF8>(family);
+    default: return partition_fn<T, D, 8, kStream, kF8>(family);
   }
 }
 
-template <typename T, bool kStream>
+template <typename T, bool kStream, bool kF8>
 const void* partition_fn_d(int family, int D, int G) {
   switch (D) {
-    case 16: return partition_fn_g<T, 16, kStream>(family, G);
-    case 32: return partition_fn_g<T, 32, kStream>(family, G);
-    case 64: return partition_fn_g<T, 64, kStream>(family, G);
-    case 128: return partition_fn_g<T, 128, kStream>(family, G);
-    default: return partition_fn_g<T, 256, kStream>(family, G);
+    case 16: return partition_fn_g<T, 16, kStream, kF8>(family, G);
+    case 32: return partition_fn_g<T, 32, kStream, kF8>(family, G);
+    case 64: return partition_fn_g<T, 64, kStream, kF8>(family, G);
+    case 128: return partition_fn_g<T, 128, kStream, kF8>(family, G);
+    default: return partition_fn_g<T, 256, kStream, kF8>(family, G);
   }
 }
 
-template <bool kStream>
+template <bool kStream, bool kF8>
 const void* pick_partition_s(int family, int dtype, int D, int G) {
   switch (dtype) {
-    case PKV_F32: return partition_fn_d<F32, kStream>(family, D, G);
-    case PKV_F16: return partition_fn_d<F16, kStream>(family, D, G);
-    default: return partition_fn_d<BF16, kStream>(family, D, G);
+    case PKV_F32: return kF8 ? nullptr : partition_fn_d<F32, kStream, false>(family, D, G);
+    case PKV_F16: return partition_fn_d<F16, kStream, kF8>(family, D, G);
+    default: return partition_fn_d<BF16, kStream, kF8>(family, D, G);
   }
 }
 
-inline const void* pick_partition(int family, int dtype, int D, int G, bool stream) {
-  return stream ? pick_partition_s<true>(family, dtype, D, G)
-                : pick_partition_s<false>(family, dtype, D, G);
+// The partition kernel for a call: family, q/out dtype, head size, group,
+// streamed or cached loads, 16-bit or FP8 pools; nullptr if none exists.
+inline const void* pick_partition(int family, int dtype, int D, int G, bool stream, bool fp8) {
+  if (fp8)
+    return stream ? pick_partition_s<true, true>(family, dtype, D, G)
+                  : pick_partition_s<false, true>(family, dtype, D, G);
+  return stream ? pick_partition_s<true, false>(family, dtype, D, G)
+                : pick_partition_s<false, false>(family, dtype, D, G);
 }
 
 enum Phase { kPhasePlan = 1, kPhasePartitions = 2, kPhaseMerge = 4, kPhaseAll = 7 };
@@ -1397,9 +1472,14 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
             const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
             int num_seqs, int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
             int head_dim, float scale, int partition_tokens, void* workspace,
-            size_t workspace_bytes, int dtype, Launch* L) {
+            size_t workspace_bytes, int dtype, Launch* L, bool kv_fp8 = false,
+            float k_scale = 1.f, float v_scale = 1.f) {
   int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, dtype);
   if (st != PKV_OK) return st;
+  if (!supported_dtype(dtype)) return PKV_ERR_UNSUPPORTED;   // q / out element type
+  if (kv_fp8 && (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == INFINITY ||
+                 v_scale == INFINITY))
+    return PKV_ERR_INVALID_ARG;
   if (num_seqs < 0 || max_blocks_per_seq < 1 || num_q_heads < 1 ||
       num_q_heads % num_kv_heads != 0 || !(scale == scale) || scale == INFINITY ||
       scale == -INFINITY)
@@ -1418,6 +1498,12 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
   else
     family = kernel == PKV_ATTN_MFMA ? kFamilyMfma : kFamilyValu;
   if (family == kFamilyMfma && (dtype == PKV_F32 || head_dim < 32)) return PKV_ERR_UNSUPPORTED;
+  // FP8 pools: the matrix-core kernel only (it decodes codes into its
+  // 16-bit operands).
+  if (kv_fp8 && family != kFamilyMfma) {
+    if (kernel != PKV_ATTN_AUTO || dtype == PKV_F32 || head_dim < 32) return PKV_ERR_UNSUPPORTED;
+    family = kFamilyMfma;
+  }
 
   const int g = num_q_heads / num_kv_heads;
   const int gmax = max_group(head_dim, family, dtype);
@@ -1431,7 +1517,7 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
 
-  const void* fn = pick_partition(family, dtype, head_dim, G, !cache_kv);
+  const void* fn = pick_partition(family, dtype, head_dim, G, !cache_kv, kv_fp8);
   if (!fn) return PKV_ERR_UNSUPPORTED;
   const int grid = device_cu_count() * resident_per_cu(fn);
   // Streamed K/V: the four waves of a workgroup take turns on the tiles of
@@ -1483,7 +1569,10 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
   p.off_short = (int)ws.off_short;
   p.off_long = (int)ws.off_long;
   p.task_seg = (int)ws.task_seg;
-  p.scale_log2 = scale * kLog2e;
+  p.scale_log2 = scale * kLog2e * (kv_fp8 ? k_scale : 1.f);
+  p.kv_fp8 = kv_fp8 ? 1 : 0;
+  p.k_scale = kv_fp8 ? k_scale : 1.f;
+  p.v_scale = kv_fp8 ? v_scale : 1.f;
   L->part_fn = fn;
   return PKV_OK;
 }
@@ -1506,12 +1595,13 @@ int decode_attention_impl(int phase, int kernel, void* out, const void* q, const
                           int block_size, int num_q_heads, int num_kv_heads, int head_dim,
                           float scale, int partition_tokens, void* workspace,
                           size_t workspace_bytes, int dtype, void* stream,
-                          const void* k_new = nullptr, const void* v_new = nullptr) {
+                          const void* k_new = nullptr, const void* v_new = nullptr,
+                          bool kv_fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
   Launch L;
   const int st = prepare(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                          context_lens, num_seqs, num_blocks, block_size, num_q_heads,
                          num_kv_heads, head_dim, scale, partition_tokens, workspace,
-                         workspace_bytes, dtype, &L);
+                         workspace_bytes, dtype, &L, kv_fp8, k_scale, v_scale);
   if (st != PKV_OK || num_seqs == 0) return st;
   L.p.k_new = (const char*)k_new;
   L.p.v_new = (const char*)v_new;
@@ -1605,4 +1695,36 @@ extern "C" int paged_decode_step(int kernel, void* out, const void* q, void* k_p
                                     block_size, num_q_heads, num_kv_heads, head_dim, scale,
                                     partition_tokens, workspace, workspace_bytes, dtype, stream,
                                     k_new, v_new);
+}
+
+extern "C" int paged_decode_attention_fp8(int kernel, void* out, const void* q,
+                                          const void* k_pool, const void* v_pool,
+                                          const int32_t* block_tables, int max_blocks_per_seq,
+                                          const int32_t* context_lens, int num_seqs,
+                                          int num_blocks, int block_size, int num_q_heads,
+                                          int num_kv_heads, int head_dim, float scale,
+                                          float k_scale, float v_scale, int partition_tokens,
+                                          void* workspace, size_t workspace_bytes, int dtype,
+                                          void* stream) {
+  return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, out, q, k_pool, v_pool, block_tables,
+                                    max_blocks_per_seq, context_lens, num_seqs, num_blocks,
+                                    block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                                    partition_tokens, workspace, workspace_bytes, dtype, stream,
+                                    nullptr, nullptr, true, k_scale, v_scale);
+}
+
+extern "C" int paged_decode_step_fp8(int kernel, void* out, const void* q, void* k_pool,
+                                     void* v_pool, const void* k_new, const void* v_new,
+                                     const int32_t* block_tables, int max_blocks_per_seq,
+                                     const int32_t* context_lens, int num_seqs, int num_blocks,
+                                     int block_size, int num_q_heads, int num_kv_heads,
+                                     int head_dim, float scale, float k_scale, float v_scale,
+                                     int partition_tokens, void* workspace,
+                                     size_t workspace_bytes, int dtype, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_INVALID_ARG;
+  return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, out, q, k_pool, v_pool, block_tables,
+                                    max_blocks_per_seq, context_lens, num_seqs, num_blocks,
+                                    block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                                    partition_tokens, workspace, workspace_bytes, dtype, stream,
+                                    k_new, v_new, true, k_scale, v_scale);
 }

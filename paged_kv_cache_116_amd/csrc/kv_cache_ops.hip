@@ -41,6 +41,50 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
   }
 }
 
+// FP8 pools: one workgroup per sequence; each thread quantises 8 elements of
+// the new token's row, code = e4m3(fp32(x) / fp32(scale)), and stores them
+// as 8 bytes.  T is the element type of k_new / v_new.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void append_fp8_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, const char* __restrict__ k_new,
+    const char* __restrict__ v_new, const int32_t* __restrict__ tables, int max_blocks,
+    const int32_t* __restrict__ lens_pre, int num_blocks, int log2_b, int num_kv_heads,
+    int head_dim, float k_scale, float v_scale) {
+  const int s = blockIdx.x;
+  const int len = lens_pre[s];
+  if (len < 0) return;
+  const int lb = logical_block(len, log2_b);
+  if (lb >= max_blocks) return;
+  const int blk = tables[(size_t)s * max_blocks + lb];
+  if (!valid_block(blk, num_blocks)) return;
+  const int row = num_kv_heads * head_dim;          // elements, a multiple of 16
+  const size_t dst = row_offset(blk, len, log2_b, num_kv_heads, 0, head_dim);
+  for (int c = threadIdx.x; c < row / 8; c += kThreads) {
+    float kf[8], vf[8];
+    const size_t src = ((size_t)s * row + 8 * c) * T::bytes;
+    if constexpr (T::bytes == 4) {
+      Cvt<T>::unpack(load16(k_new + src), kf);
+      Cvt<T>::unpack(load16(k_new + src + 16), kf + 4);
+      Cvt<T>::unpack(load16(v_new + src), vf);
+      Cvt<T>::unpack(load16(v_new + src + 16), vf + 4);
+    } else {
+      Cvt<T>::unpack(load16(k_new + src), kf);
+      Cvt<T>::unpack(load16(v_new + src), vf);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      kf[e] = kf[e] / k_scale;
+      vf[e] = vf[e] / v_scale;
+    }
+    const uint2 kc = make_uint2(e4m3_encode4(kf[0], kf[1], kf[2], kf[3]),
+                                e4m3_encode4(kf[4], kf[5], kf[6], kf[7]));
+    const uint2 vc = make_uint2(e4m3_encode4(vf[0], vf[1], vf[2], vf[3]),
+                                e4m3_encode4(vf[4], vf[5], vf[6], vf[7]));
+    *reinterpret_cast<uint2*>(k_pool + dst + 8 * c) = kc;
+    *reinterpret_cast<uint2*>(v_pool + dst + 8 * c) = vc;
+  }
+}
+
 // blockIdx.x = pair, blockIdx.y = slice of the block's chunks.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     char* __restrict__ k_pool, char* __restrict__ v_pool, const int32_t* __restrict__ src,
@@ -106,6 +150,36 @@ extern "C" int paged_kv_append(void* k_pool, void* v_pool, const void* k_new, co
                      (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new,
                      block_tables, max_blocks_per_seq, context_lens_pre, num_blocks,
                      log2_exact(block_size), num_kv_heads, head_dim, dtype_bytes(dtype));
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" int paged_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new,
+                                   const void* v_new, const int32_t* block_tables,
+                                   int max_blocks_per_seq, const int32_t* context_lens_pre,
+                                   int num_seqs, int num_blocks, int block_size, int num_kv_heads,
+                                   int head_dim, int new_dtype, float k_scale, float v_scale,
+                                   void* stream) {
+  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, PKV_FP8_E4M3);
+  if (st != PKV_OK) return st;
+  if (!supported_dtype(new_dtype)) return PKV_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == INFINITY || v_scale == INFINITY)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs < 0 || max_blocks_per_seq < 1) return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !context_lens_pre)
+    return PKV_ERR_INVALID_ARG;
+  const int log2_b = log2_exact(block_size);
+  auto launch = [&](auto tag) {
+    using T = decltype(tag);
+    hipLaunchKernelGGL(append_fp8_kernel<T>, dim3(num_seqs), dim3(kThreads), 0,
+                       (hipStream_t)stream, (uint8_t*)k_pool, (uint8_t*)v_pool,
+                       (const char*)k_new, (const char*)v_new, block_tables, max_blocks_per_seq,
+                       context_lens_pre, num_blocks, log2_b, num_kv_heads, head_dim, k_scale,
+                       v_scale);
+  };
+  if (new_dtype == PKV_F32) launch(F32{});
+  else if (new_dtype == PKV_F16) launch(F16{});
+  else launch(BF16{});
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

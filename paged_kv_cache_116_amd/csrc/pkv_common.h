@@ -23,6 +23,7 @@ inline int dtype_bytes(int dtype) {
     case PKV_F32: return 4;
     case PKV_F16: return 2;
     case PKV_BF16: return 2;
+    case PKV_FP8_E4M3: return 1;
     default: return 0;
   }
 }
@@ -108,6 +109,46 @@ __device__ __forceinline__ uint4 load16_stream(const void* p) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 load8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+__device__ __forceinline__ uint2 load8_stream(const void* p) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+// ---------------------------------------------------------------------------
+// FP8 cache codes: E4M3FN of the OCP 8-bit floating point format (bias 7,
+// 3 mantissa bits, no infinities, S.1111.111 = NaN, largest finite 448).
+// gfx950's v_cvt_pk_f32_fp8 decodes this format exactly; its encoder rounds
+// to nearest even but turns magnitudes past the largest rounding boundary
+// into NaN, so the encoder below saturates first and keeps NaN explicitly.
+// ---------------------------------------------------------------------------
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Four codes (one 32-bit word, code i in byte i) -> four floats.
+__device__ __forceinline__ void e4m3_decode4(uint32_t w, float* out) {
+  const f32x2_t a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_t b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  out[0] = a.x; out[1] = a.y; out[2] = b.x; out[3] = b.y;
+}
+
+// Four floats -> four codes: nearest, ties to even, |v| >= 448 -> +-448,
+// NaN -> 0x7F or 0xFF by the sign bit.
+__device__ __forceinline__ uint32_t e4m3_encode4(float v0, float v1, float v2, float v3) {
+  auto sat = [](float v) { return fminf(fmaxf(v, -448.f), 448.f); };   // NaN: fixed below
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v0), sat(v1), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(v2), sat(v3), w, true);
+  uint32_t u = (uint32_t)w;
+  const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (v[i] != v[i]) {
+      const uint32_t nan_code = (__float_as_uint(v[i]) >> 31) ? 0xFFu : 0x7Fu;
+      u = (u & ~(0xFFu << (8 * i))) | (nan_code << (8 * i));
+    }
+  }
+  return u;
 }
 __device__ __forceinline__ void store16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 

@@ -18,6 +18,8 @@ inline bool supported_head_dim(int d) {
 }
 
 inline bool supported_dtype(int dt) { return dt == PKV_F32 || dt == PKV_F16 || dt == PKV_BF16; }
+// Pools may also hold FP8 codes (byte moves and the FP8 entry points).
+inline bool supported_pool_dtype(int dt) { return supported_dtype(dt) || dt == PKV_FP8_E4M3; }
 
 // Shape checks every pool operation shares.  Sizes must be positive; block
 // size, head size and dtype must be in the supported lists.
@@ -26,7 +28,7 @@ inline int check_pool_shape(int num_blocks, int block_size, int num_kv_heads, in
   if (num_blocks < 1 || num_kv_heads < 1 || block_size < 1 || head_dim < 1)
     return PKV_ERR_INVALID_ARG;
   if (!supported_block_size(block_size) || !supported_head_dim(head_dim) ||
-      !supported_dtype(dtype))
+      !supported_pool_dtype(dtype))
     return PKV_ERR_UNSUPPORTED;
   return PKV_OK;
 }

@@ -88,6 +88,34 @@ def test_decode_step_needs_the_new_tokens():
     assert lib_step(0, a[0], a[1], a[2], a[3], None, None, *a[4:]) == pkv.PKV_OK
 
 
+def test_fp8_entry_points_validate_arguments():
+    # out, q, k, v, tables, mb, lens, S, N, B, Hq, Hkv, D, scale | k_scale, v_scale | part, ws, wsb, dt, st
+    head = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 16, 16, 8, 2, 128, 0.1]
+    tail = [0, FAKE, 1 << 30, pkv.PKV_BF16, None]
+    f = lib.paged_decode_attention_fp8
+    assert f(0, *head, 0.0, 1.0, *tail) == pkv.PKV_ERR_INVALID_ARG          # scale > 0
+    assert f(0, *head, 1.0, float("nan"), *tail) == pkv.PKV_ERR_INVALID_ARG
+    assert f(0, *head, 1.0, float("inf"), *tail) == pkv.PKV_ERR_INVALID_ARG
+    assert f(pkv.PKV_ATTN_VALU, *head, 1.0, 1.0, *tail) == pkv.PKV_ERR_UNSUPPORTED
+    t32 = tail[:3] + [pkv.PKV_F32, None]
+    assert f(0, *head, 1.0, 1.0, *t32) == pkv.PKV_ERR_UNSUPPORTED       # q / out fp32
+    t8 = tail[:3] + [pkv.PKV_FP8_E4M3, None]
+    assert f(0, *head, 1.0, 1.0, *t8) == pkv.PKV_ERR_UNSUPPORTED        # q / out cannot be FP8
+    h32 = head[:12] + [16, 0.1]
+    assert f(0, *h32, 1.0, 1.0, *tail) == pkv.PKV_ERR_UNSUPPORTED       # head_dim < 32
+    # plain attention never takes FP8 as its element type
+    a = head + tail[:3] + [pkv.PKV_FP8_E4M3, None]
+    assert lib.paged_decode_attention(*a) == pkv.PKV_ERR_UNSUPPORTED
+    ap = lib.paged_kv_append_fp8
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 3, 16, 16, 2, 128]
+    assert ap(*base, pkv.PKV_FP8_E4M3, 1.0, 1.0, None) == pkv.PKV_ERR_UNSUPPORTED
+    assert ap(*base, pkv.PKV_BF16, -1.0, 1.0, None) == pkv.PKV_ERR_INVALID_ARG
+    assert ap(*base[:7], 0, *base[8:], pkv.PKV_BF16, 1.0, 1.0, None) == pkv.PKV_OK
+    step = lib.paged_decode_step_fp8
+    assert step(0, FAKE, FAKE, FAKE, FAKE, None, FAKE, *head[4:], 1.0, 1.0, *tail) == \
+        pkv.PKV_ERR_INVALID_ARG
+
+
 def test_zero_sequences_is_a_noop():
     assert attn(s=0) == pkv.PKV_OK
     assert lib.paged_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, 16, 16, 2, 128, 2, None) == 0

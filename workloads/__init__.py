@@ -24,6 +24,12 @@ remaining entries are -1.  Every slot that holds no token before the append
 (unallocated blocks, the tail of each sequence's last block, including the
 append slot) is NaN when ``poison`` is set, so any read of it shows up in the
 result.
+
+FP8 pools (``kv_fp8=True``) hold E4M3FN codes drawn field by field: a random
+sign, exponent field 3..10 and mantissa field 0..7 (magnitudes 2^-4 .. 15,
+never NaN), with per-pool scales ``k_scale`` / ``v_scale``; empty slots hold
+the NaN code 0x7F.  No quantisation is done here.  q and the new tokens keep
+the config's 16-bit type.
 """
 
 from __future__ import annotations
@@ -64,6 +70,9 @@ class Workload:
     partition_tokens: int = 512
     shared_blocks: list = field(default_factory=list)
     seed: int = 0
+    kv_fp8: bool = False             # pools are torch.float8_e4m3fn codes
+    k_scale: float = 1.0
+    v_scale: float = 1.0
 
     @property
     def num_seqs(self) -> int:
@@ -115,7 +124,8 @@ def make_workload(config_id: int, seed: int | None = None, *, batch: int | None 
                   len_range=None, block_size: int | None = None, prefix_tokens: int = 1024,
                   device="cpu", poison: bool = True, dtype: str | None = None,
                   num_q_heads: int | None = None, num_kv_heads: int | None = None,
-                  head_dim: int | None = None, shuffle: bool = True) -> Workload:
+                  head_dim: int | None = None, shuffle: bool = True,
+                  kv_fp8: bool = False) -> Workload:
     """Draw config ``config_id`` (1-5).  Keyword overrides shrink a config for
     tests while keeping its structure (length law, sharing, shuffled ids).
     ``shuffle=False`` hands out physical ids in order (identity-like tables)."""
@@ -191,13 +201,30 @@ def make_workload(config_id: int, seed: int | None = None, *, batch: int | None 
     def randn(*shape):
         return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(tdtype)
 
+    def codes(*shape):
+        sign = torch.randint(0, 2, shape, generator=gen, device=dev, dtype=torch.int32)
+        expo = torch.randint(3, 11, shape, generator=gen, device=dev, dtype=torch.int32)
+        mant = torch.randint(0, 8, shape, generator=gen, device=dev, dtype=torch.int32)
+        return ((sign << 7) | (expo << 3) | mant).to(torch.uint8).view(torch.float8_e4m3fn)
+
     q = randn(S, Hq, D)
     k_new = randn(S, Hkv, D)
     v_new = randn(S, Hkv, D)
-    k_pool = randn(num_blocks, B, Hkv, D)
-    v_pool = randn(num_blocks, B, Hkv, D)
+    if kv_fp8:
+        if dtype == "f32":
+            raise ValueError("FP8 pools pair with 16-bit queries")
+        k_pool = codes(num_blocks, B, Hkv, D)
+        v_pool = codes(num_blocks, B, Hkv, D)
+    else:
+        k_pool = randn(num_blocks, B, Hkv, D)
+        v_pool = randn(num_blocks, B, Hkv, D)
     if poison:
+        # NaN, or for FP8 pools the NaN code 0x7F.
         nan = float("nan")
+        if kv_fp8:
+            k_pool = k_pool.view(torch.uint8)
+            v_pool = v_pool.view(torch.uint8)
+            nan = 0x7F
         if len(unused_ids):
             idx = torch.as_tensor(unused_ids, device=dev, dtype=torch.long)
             k_pool[idx] = nan
@@ -216,11 +243,16 @@ def make_workload(config_id: int, seed: int | None = None, *, batch: int | None 
             oi = torch.as_tensor(off_idx, device=dev, dtype=torch.long)
             k_pool[bi, oi] = nan
             v_pool[bi, oi] = nan
+        if kv_fp8:
+            k_pool = k_pool.view(torch.float8_e4m3fn)
+            v_pool = v_pool.view(torch.float8_e4m3fn)
     del used_ids
     return Workload(name=CONFIG_NAMES[config_id], dtype=dtype, block_size=B,
                     num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, num_blocks=num_blocks,
                     lens=lens.astype(np.int32), tables=tables, q=q, k_new=k_new, v_new=v_new,
-                    k_pool=k_pool, v_pool=v_pool, shared_blocks=shared, seed=seed)
+                    k_pool=k_pool, v_pool=v_pool, shared_blocks=shared, seed=seed,
+                    kv_fp8=kv_fp8, k_scale=0.0625 if kv_fp8 else 1.0,
+                    v_scale=0.125 if kv_fp8 else 1.0)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
@@ -245,6 +277,11 @@ def extract_sequences(w: Workload, seqs, dtype=np.float64):
     def host(t):   # exact: every element type here widens exactly to float32/64
         return t.detach().to("cpu").to(torch.float64).numpy().astype(dtype)
 
-    return dict(k_pool=host(w.k_pool[idx]), v_pool=host(w.v_pool[idx]), tables=tables,
+    def pool(t):   # FP8 pools come back as their uint8 codes, undecoded
+        if w.kv_fp8:
+            return t.detach().view(torch.uint8).to("cpu").numpy().copy()
+        return host(t)
+
+    return dict(k_pool=pool(w.k_pool[idx]), v_pool=pool(w.v_pool[idx]), tables=tables,
                 lens=w.lens[seqs].copy(), lens_pre=w.lens_pre[seqs].copy(),
                 q=host(w.q[sel]), k_new=host(w.k_new[sel]), v_new=host(w.v_new[sel]))
