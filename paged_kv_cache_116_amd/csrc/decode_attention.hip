@@ -64,6 +64,7 @@
 
 #include <mutex>
 #include <type_traits>
+#include <utility>
 #include <unordered_map>
 
 #include "pkv_common.h"
@@ -170,6 +171,16 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1 in order.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -713,8 +724,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
   // occupancy is register bound at two waves per SIMD anyway) and a slot
   // costs <= 32 registers; otherwise two, which keeps small groups at a
   // higher occupancy.
+  // FP8 slots cost half the registers and carry half the bytes, so the FP8
+  // kernel keeps more tiles in flight for the same bytes in flight.
   constexpr int kSlotRegs = 2 * TPR * (int)(sizeof(KvReg) / 4);
-  constexpr int kSlots = (kSlotRegs <= 32 && G >= 4) ? 3 : 2;
+  constexpr int kSlots = (kF8 && G >= 4 && kSlotRegs <= 16) ? 5
+                       : (kSlotRegs <= 32 && G >= 4) ? 3 : 2;
   static_assert(D % 32 == 0 && TPR >= 1 && G <= kMaxGroup && G * D <= kMaxGD, "shape");
 
   // Probabilities of the current tile per head: fp32 for the FMA form,
@@ -933,41 +947,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
       }
     };
 
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
+    // The ring: slots 0 .. kSlots-2 are filled first; then each step issues
+    // the tile kSlots-1 steps ahead into the slot freed last and consumes the
+    // oldest one (slot indices are compile-time constants).
     const int step = p.wpk;
     int tile = sg.t0 + sw;
     if (kv.live && tile < tile_end) {
-      if constexpr (kSlots == 3) {
-        issue(I0{}, tile);
-        issue(I1{}, tile + step);
-        while (true) {
-          issue(I2{}, tile + 2 * step);
-          consume(I0{}, tile);
-          tile += step;
-          if (tile >= tile_end) break;
-          issue(I0{}, tile + 2 * step);
-          consume(I1{}, tile);
-          tile += step;
-          if (tile >= tile_end) break;
-          issue(I1{}, tile + 2 * step);
-          consume(I2{}, tile);
-          tile += step;
-          if (tile >= tile_end) break;
-        }
-      } else {
-        issue(I0{}, tile);
-        while (true) {
-          issue(I1{}, tile + step);
-          consume(I0{}, tile);
-          tile += step;
-          if (tile >= tile_end) break;
-          issue(I0{}, tile + step);
-          consume(I1{}, tile);
-          tile += step;
-          if (tile >= tile_end) break;
-        }
+      static_for<kSlots - 1>([&](auto k) { issue(k, tile + decltype(k)::value * step); });
+      bool done = false;
+      while (!done) {
+        static_for<kSlots>([&](auto k) {
+          constexpr int K = decltype(k)::value;
+          if (!done) {
+            issue(std::integral_constant<int, (K + kSlots - 1) % kSlots>{},
+                  tile + (kSlots - 1) * step);
+            consume(k, tile);
+            tile += step;
+            done = tile >= tile_end;
+          }
+        });
       }
     }
 
