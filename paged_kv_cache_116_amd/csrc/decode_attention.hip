@@ -47,9 +47,12 @@
 //     v_mfma_f32_16x16x32 ops.  K and V rows are loaded whole (every load
 //     instruction covers complete rows); K goes through a per-wave swizzled
 //     LDS tile to reach the MFMA operand layout (lane: row l % 16, channels
-//     8 * (l / 16) .. +7 of each 32-channel chunk).  P.V runs on the vector
-//     ALU as packed dot2 over token pairs: each lane owns 8 channels of one
-//     V row group and reads the probabilities of its tokens from LDS.
+//     8 * (l / 16) .. +7 of each 32-channel chunk).  P.V is O^T = V^T . P^T,
+//     D/16 v_mfma_f32_16x16x16 ops per tile: a lane's four probabilities
+//     (four tokens of one head, straight from the score tile) are its B
+//     operand, and V goes through a per-wave LDS tile read back with
+//     transposing reads (ds_read_b64_tr_b16) as the A operand.  Each lane
+//     then holds channels of its own head, so the rescale is lane-local.
 //     Block ids come through scalar loads, one tile at a time.
 //   attn_partition_valu  (any dtype incl. fp32): one token row per group of
 //     D*sizeof/16 lanes, dot products reduced across the group with shuffles,
@@ -200,6 +203,33 @@ template <> struct Mfma<F16> {
                                                   __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
   }
 };
+
+// 16x16x16 products for P.V (k = the 16 tokens of a tile): four elements of
+// A and of B per lane, as two dwords.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+template <typename T> struct Mfma16;
+template <> struct Mfma16<BF16> {
+  __device__ static __forceinline__ f32x4_t run(s16x4_t a, const uint2& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, __builtin_bit_cast(s16x4_t, b), c, 0, 0,
+                                                     0);
+  }
+};
+template <> struct Mfma16<F16> {
+  __device__ static __forceinline__ f32x4_t run(s16x4_t a, const uint2& b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+};
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives element i % 4 of the 8-byte chunks addressed by lanes
+// i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 of the same group, in that order.
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+__device__ __forceinline__ s16x4_t lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4_t*)(__attribute__((address_space(3))) char*)(p));
+}
 
 // Pairs of 16-bit values for the P.V product: probabilities of two tokens
 // packed to the element type (round to nearest even) and multiplied with the
@@ -731,11 +761,6 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
                        : (kSlotRegs <= 32 && G >= 4) ? 3 : 2;
   static_assert(D % 32 == 0 && TPR >= 1 && G <= kMaxGroup && G * D <= kMaxGD, "shape");
 
-  // Probabilities of the current tile per head: fp32 for the FMA form,
-  // pairs of 16-bit values (tokens 2j, 2j+1) for the dot2 form.
-  constexpr bool kDot2 = TPR >= 2;
-  __shared__ __align__(16) float p_lds[kWaves][G][kTile];
-  __shared__ __align__(16) float alpha_lds[kWaves][G];
   __shared__ float red_m[kWaves][G];
   __shared__ float red_l[kWaves][G];
   __shared__ __align__(16) float red_acc[kWaves][G][D];
@@ -743,7 +768,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
   // sits at position c ^ kswz(r), which keeps both the row-wise writes and
   // the operand-wise reads free of bank conflicts.
   __shared__ __align__(16) uint4 k_lds[kWaves][kTile * LPR];
-  uint32_t (*p2_lds)[G][kTile / 2] = reinterpret_cast<uint32_t (*)[G][kTile / 2]>(p_lds);
+  // V tile of each wave, token-major, rows padded by 32 bytes: the four rows
+  // one 16-lane group reads at a time (a 32-byte piece of each) then land in
+  // distinct banks, and so do the two groups of a half-wave.
+  constexpr int VP = D + 16;
+  __shared__ __align__(16) uint16_t v_lds[kWaves][kTile * VP];
   auto kswz = [](int r) {
     if constexpr (LPR >= 16) return r & 15;          // rows of >= 256 bytes
     else if constexpr (LPR == 8) return (r >> 1) & 7; // 128-byte rows: two per 256 bytes
@@ -829,21 +858,25 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
 
     float m_run = -INFINITY;  // running maximum of head `col` (log2 units)
     float l_run = 0.f;        // normaliser partial: tokens of C row group kgrp
-    float acc[G][8];
+    // O^T accumulator: block j holds channels 16j + 4*kgrp .. +3 of head col.
+    f32x4_t acc[D / 16];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int j = 0; j < D / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // This lane's piece of the transposed V reads: row 4*kgrp + col / 4,
+    // channels 4 * (col % 4) .. +3 of each 16-channel block.
+    const uint16_t* vt = &v_lds[w][(4 * kgrp + (col >> 2)) * VP + 4 * (col & 3)];
 
     auto consume = [&](auto slot, int tile) {
       constexpr int SL = decltype(slot)::value;
-      // K rows to LDS, then each lane takes its operand: row `col`, channels
-      // 32j + 8*kgrp .. +7 = chunk 4j + kgrp.  (The previous tile's reads of
-      // k_lds are ordered before these writes by the syncs that follow them.)
+      // K and V rows to LDS.  K: each lane then takes its operand, row `col`,
+      // channels 32j + 8*kgrp .. +7 = chunk 4j + kgrp.  (The previous tile's
+      // reads are ordered before these writes by the sync ending it.)
 #pragma unroll
       for (int i = 0; i < TPR; ++i) {
         const int r = TPR * vr + i;
         k_lds[w][r * LPR + (vc ^ kswz(r))] = expand8<T>(kb[SL][i]);
+        *reinterpret_cast<uint4*>(&v_lds[w][r * VP + vc * 8]) = expand8<T>(vb[SL][i]);
       }
       wave_lds_sync();
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
@@ -861,90 +894,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
 
-      // The previous tile's reads of alpha_lds / p_lds come before this
-      // tile's writes.
-      wave_lds_sync();
+      // Every lane holds its own head's maximum, so the rescale is lane-local.
       if (__any(mt > m_run + kRescaleThreshold)) {
         const float mn = fmaxf(m_run, mt);
         const float alpha = fast_exp2(m_run - mn);   // 0 on the first tile
         m_run = mn;
         l_run *= alpha;
-        if (kgrp == 0 && col < G) alpha_lds[w][col] = alpha;
-        wave_lds_sync();
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float a = alpha_lds[w][h];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] *= a;
-        }
+        for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
       }
 
       float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pv[i] = fast_exp2(sv[i] - m_run);   // masked: exp2(-inf) = 0
-      if constexpr (kDot2) {
-        // P rounded to the element type for the dot2 product; the normaliser
-        // sums the same rounded values, so the weights still sum to one.
-        const uint32_t q01 = Pair<T>::pack(pv[0], pv[1]);
-        const uint32_t q23 = Pair<T>::pack(pv[2], pv[3]);
-        l_run += (Pair<T>::lo(q01) + Pair<T>::hi(q01)) + (Pair<T>::lo(q23) + Pair<T>::hi(q23));
-        if (col < G) *reinterpret_cast<uint2*>(&p2_lds[w][col][2 * kgrp]) = make_uint2(q01, q23);
-      } else {
-        l_run += (pv[0] + pv[1]) + (pv[2] + pv[3]);
-        if (col < G)
-          *reinterpret_cast<float4*>(&p_lds[w][col][4 * kgrp]) = make_float4(pv[0], pv[1], pv[2], pv[3]);
-      }
+      // P rounded to the element type for the product; the normaliser sums
+      // the same rounded values, so the weights still sum to one.  The lane's
+      // four probabilities (tokens 4*kgrp + i, head col) are exactly its B
+      // operand of O^T = V^T . P^T.
+      const uint32_t q01 = Pair<T>::pack(pv[0], pv[1]);
+      const uint32_t q23 = Pair<T>::pack(pv[2], pv[3]);
+      l_run += (Pair<T>::lo(q01) + Pair<T>::hi(q01)) + (Pair<T>::lo(q23) + Pair<T>::hi(q23));
+      const uint2 pop = make_uint2(q01, q23);
+      // A operand of block j: V[4*kgrp + i][16j + col], i = 0..3, one
+      // transposed read.
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) acc[j] = Mfma16<T>::run(lds_read_tr16(vt + 16 * j), pop, acc[j]);
       wave_lds_sync();
-
-      // P.V on the vector ALU: lane (vr, vc) owns channels 8vc..8vc+7 of the
-      // tile's tokens TPR*vr + i.
-      if constexpr (kDot2) {
-        constexpr int NP = TPR / 2;   // token pairs per lane
-        uint32_t vp[NP][8];           // channel e of tokens (2k, 2k+1)
-#pragma unroll
-        for (int k = 0; k < NP; ++k) {
-          if constexpr (kF8) {
-            // Decode both tokens' codes and pack the pairs directly.
-            float fa[8], fb[8];
-            e4m3_decode4(vb[SL][2 * k].x, fa);
-            e4m3_decode4(vb[SL][2 * k].y, fa + 4);
-            e4m3_decode4(vb[SL][2 * k + 1].x, fb);
-            e4m3_decode4(vb[SL][2 * k + 1].y, fb + 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vp[k][e] = Pair<T>::pack(fa[e], fb[e]);
-          } else {
-            const uint4 a = vb[SL][2 * k], b = vb[SL][2 * k + 1];
-            vp[k][0] = pair_lo(a.x, b.x); vp[k][1] = pair_hi(a.x, b.x);
-            vp[k][2] = pair_lo(a.y, b.y); vp[k][3] = pair_hi(a.y, b.y);
-            vp[k][4] = pair_lo(a.z, b.z); vp[k][5] = pair_hi(a.z, b.z);
-            vp[k][6] = pair_lo(a.w, b.w); vp[k][7] = pair_hi(a.w, b.w);
-          }
-        }
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          uint32_t pp[NP];
-#pragma unroll
-          for (int k = 0; k < NP; ++k) pp[k] = p2_lds[w][h][NP * vr + k];
-#pragma unroll
-          for (int k = 0; k < NP; ++k)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = Pair<T>::dot2(pp[k], vp[k][e], acc[h][e]);
-        }
-      } else {
-        float vf[TPR][8];
-#pragma unroll
-        for (int i = 0; i < TPR; ++i) Cvt<T>::unpack(expand8<T>(vb[SL][i]), vf[i]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float ph[TPR];
-#pragma unroll
-          for (int i = 0; i < TPR; ++i) ph[i] = p_lds[w][h][TPR * vr + i];
-#pragma unroll
-          for (int i = 0; i < TPR; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(ph[i], vf[i][e], acc[h][e]);
-        }
-      }
     };
 
     // The ring: slots 0 .. kSlots-2 are filled first; then each step issues
@@ -969,27 +944,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
       }
     }
 
-    // Wave totals: l over the four C row groups, o over the V row groups.
+    // Wave totals: l over the four C row groups; o is complete per lane.
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
+    if (col < G) {
 #pragma unroll
-    for (int off = LPR; off < 64; off <<= 1)
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], off);
-    if (vr == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        *reinterpret_cast<float4*>(&red_acc[w][h][vc * 8]) =
-            make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-        *reinterpret_cast<float4*>(&red_acc[w][h][vc * 8 + 4]) =
-            make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      for (int j = 0; j < D / 16; ++j)
+        *reinterpret_cast<float4*>(&red_acc[w][col][16 * j + 4 * kgrp]) =
+            make_float4(acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+      if (kgrp == 0) {
+        red_m[w][col] = m_run;
+        red_l[w][col] = l_run;
       }
-    }
-    if (kgrp == 0 && col < G) {
-      red_m[w][col] = m_run;
-      red_l[w][col] = l_run;
     }
     finish_segment<T, D, G, kF8>(p, sg, w, bad, red_m, red_l, red_acc);
   });
