@@ -26,9 +26,11 @@ Sources, cited in the modules by tag and section:
 Modules:
   paging        block-table resolution, explicit gather, slot accounting
   attention     decode attention by explicit gather + two-pass softmax,
-                the block-wise online-softmax recurrence and the
-                log-sum-exp merge of partition states
-  cache_ops     cache append and block copy on pool copies
+                the block-wise online-softmax recurrence, the
+                log-sum-exp merge of partition states, and causal
+                chunked prefill over the paged history
+  cache_ops     cache append (one or several tokens per sequence) and
+                block copy on pool copies
   fp8           E4M3FN codes for FP8 cache blocks: encode, decode, append
   block_manager free list, reference counts, fork and copy-on-write
   allocator_toy contiguous-reservation vs paged accounting of a toy workload

@@ -159,3 +159,64 @@ def split_k_decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarr
                                                     scale, first, last))
             out[s, h] = merge_states(states)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Chunked prefill over the paged cache
+# ---------------------------------------------------------------------------
+
+def prefill_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                      tables: np.ndarray, lens, cu_seqlens, block_size: int,
+                      scale: float | None = None) -> np.ndarray:
+    """Causal attention of a chunk of query tokens per sequence over its
+    paged history.
+
+    [pofe] "How it works": at admission the prompt's blocks are allocated
+    and prefill writes into them, and attention over a block table is the
+    ordinary attention sum (one row of weights per query i) regrouped by
+    block; [pofe] "When memory runs out" and [lesson] "Preemption": a
+    recomputed sequence is prefilled again from its tokens in one pass.
+    The pages do not spell out the mask.  Reading: each query token attends
+    to itself and every earlier position, the decode rule applied to every
+    token of the chunk.  Sequence s holds L_s = lens[s] positions (the
+    chunk's own keys and values already appended), and its chunk is its last
+    n_s = cu_seqlens[s+1] - cu_seqlens[s] positions, so query j of the chunk
+    sits at position p = L_s - n_s + j and attends positions 0 .. p:
+
+        o[j, h] = sum_{t <= p} softmax_t(scale * q[j, h] . K[t, kvh(h)]) V[t, kvh(h)]
+
+    q:          [T, H_q, D], T = cu_seqlens[-1] (the chunks, packed)
+    pools:      [N, B, H_kv, D]; tables [S, max_blocks]
+    lens:       [S] context lengths including the chunk (n_s <= L_s)
+    cu_seqlens: [S + 1] chunk offsets into q, non-decreasing from 0
+    returns     float64 [T, H_q, D]
+    """
+    q = np.asarray(q, dtype=np.float64)
+    total, num_q_heads, head_dim = q.shape
+    num_kv_heads = k_pool.shape[2]
+    if num_q_heads % num_kv_heads != 0:
+        raise ValueError("num_q_heads must be a multiple of num_kv_heads")
+    group = num_q_heads // num_kv_heads
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    cu = [int(x) for x in cu_seqlens]
+    if cu[0] != 0 or cu[-1] != total or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must rise from 0 to the number of query tokens")
+    out = np.zeros((total, num_q_heads, head_dim), dtype=np.float64)
+    for s in range(len(cu) - 1):
+        n = cu[s + 1] - cu[s]
+        length = int(lens[s])
+        if n == 0:
+            continue
+        if n > length:
+            raise ValueError(f"sequence {s}: chunk of {n} tokens exceeds its length {length}")
+        k_seq = gather_contiguous(k_pool, tables[s], length, block_size).astype(np.float64)
+        v_seq = gather_contiguous(v_pool, tables[s], length, block_size).astype(np.float64)
+        for j in range(n):
+            pos = length - n + j
+            for h in range(num_q_heads):
+                kvh = h // group
+                z = scale * (k_seq[: pos + 1, kvh, :] @ q[cu[s] + j, h])   # [pos + 1]
+                p = _softmax_weights(z)
+                out[cu[s] + j, h] = p @ v_seq[: pos + 1, kvh, :]
+    return out

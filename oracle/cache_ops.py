@@ -59,3 +59,35 @@ def copy_blocks(k_pool: np.ndarray, v_pool: np.ndarray, src, dst):
         k_out[b] = k_pool[a]
         v_out[b] = v_pool[a]
     return k_out, v_out
+
+
+def append_tokens(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
+                  v_new: np.ndarray, tables: np.ndarray, lens_pre, cu_seqlens,
+                  block_size: int):
+    """Write a run of new tokens per sequence into its slots; return new pools.
+
+    The multi-token form of :func:`append_token`: sequence s appends the
+    n_s = cu_seqlens[s+1] - cu_seqlens[s] rows k_new[cu_seqlens[s] + j],
+    j < n_s, at positions lens_pre[s] + j, each resolved through the table
+    ([pofe] "How it works": the prompt's blocks are allocated at admission
+    and prefill writes into them; slot p mod b of entry floor(p / b)).  A
+    negative lens_pre marks a padding row that writes nothing.
+
+    k_new, v_new: [T, H_kv, D] packed; pools [N, B, H_kv, D]; lens_pre [S];
+    cu_seqlens [S + 1].
+    """
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    num_blocks = k_pool.shape[0]
+    cu = [int(x) for x in cu_seqlens]
+    for s, start in enumerate(lens_pre):
+        start = int(start)
+        if start < 0:
+            continue
+        for j in range(cu[s + 1] - cu[s]):
+            physical, offset = resolve(tables[s], block_size, start + j)
+            if not (0 <= physical < num_blocks):
+                raise IndexError(f"sequence {s}: block id {physical} outside the pool")
+            k_out[physical, offset] = k_new[cu[s] + j]
+            v_out[physical, offset] = v_new[cu[s] + j]
+    return k_out, v_out
