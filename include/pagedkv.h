@@ -336,6 +336,59 @@ int paged_decode_step_fp8(int kernel, void* out, const void* q, void* k_pool, vo
                           int dtype, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Chunked prefill                                                           */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [pofe] "How it works": at admission the prompt's blocks are allocated and
+ * prefill writes into them; [pofe] "When memory runs out" and [lesson]
+ * "Preemption": a recomputed sequence is prefilled again, prompt and
+ * generated tokens, in one pass.  A prefill batch is packed: sequence s
+ * contributes the n_s = cu_seqlens[s+1] - cu_seqlens[s] tokens
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1 of the packed arrays.
+ *   cu_seqlens : device int32 [num_seqs + 1], cu_seqlens[0] = 0, non-decreasing;
+ *                tokens of the packed arrays outside [cu_seqlens[0],
+ *                cu_seqlens[num_seqs]) belong to no sequence.
+ */
+
+/* paged_kv_append_tokens - write each sequence's run of new tokens into its
+ * cache slots: packed token cu_seqlens[s] + j (k_new, v_new : device
+ * [num_tokens, num_kv_heads, head_dim], dtype) goes to position
+ * context_lens_pre[s] + j, i.e. slot (that position) % B of block
+ * table[(that position) / B].  A negative context_lens_pre[s] marks a padding
+ * row that writes nothing; positions past the table row or naming an id
+ * outside the pool are skipped.  Bit copy; nothing else is written.  Two
+ * tokens must not name the same slot. */
+int paged_kv_append_tokens(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                           const int32_t* cu_seqlens, int num_tokens,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens_pre, int num_seqs, int num_blocks,
+                           int block_size, int num_kv_heads, int head_dim, int dtype,
+                           void* stream);
+
+/* paged_prefill_attention - causal attention of each sequence's chunk over
+ * its paged history.  context_lens[s] = L_s counts every position in the
+ * pool including the chunk's own (append them first); the chunk is the last
+ * n_s positions, so packed query token cu_seqlens[s] + j sits at position
+ * p = L_s - n_s + j and attends positions 0 .. p (the pages leave the mask
+ * implicit; this is the decode rule applied to every chunk token):
+ *     out[j, h] = sum_{t <= p} softmax_t(scale * q[j, h] . K[t, h / g]) V[t, h / g]
+ *   q, out : device [num_tokens, num_q_heads, head_dim], dtype F16 or BF16
+ *            (F32 and FP8 pools give PKV_ERR_UNSUPPORTED), head_dim % 32 == 0.
+ *   max_chunk_tokens : host upper bound on n_s used to size the launch; any
+ *            value >= 1 computes every row (a smaller one only runs with
+ *            less parallelism).
+ * A sequence with n_s > L_s or L_s > max_blocks_per_seq * block_size gets NaN
+ * rows; one whose table names an id outside the pool gets NaN rows for the
+ * rows of every workgroup that read it.  Needs no workspace. */
+int paged_prefill_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const int32_t* cu_seqlens, const int32_t* block_tables,
+                            int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                            int max_chunk_tokens, int num_blocks, int block_size,
+                            int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                            int dtype, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Host block manager (CPU only; no device calls)                            */
 /* ------------------------------------------------------------------------- */
 /*

@@ -75,6 +75,10 @@ _sig("paged_kv_append_fp8", _i32,
 _ATTN_ARGS_FP8 = _ATTN_ARGS[:14] + [_f32, _f32] + _ATTN_ARGS[14:]
 _sig("paged_decode_attention_fp8", _i32, [_i32] + _ATTN_ARGS_FP8)
 _sig("paged_decode_step_fp8", _i32, [_i32, _p, _p, _p, _p, _p, _p] + _ATTN_ARGS_FP8[4:])
+_sig("paged_kv_append_tokens", _i32,
+     [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p])
+_sig("paged_prefill_attention", _i32,
+     [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p])
 _sig("pkv_validate_tables", _i32, [_p, _i32, _p, _i32, _i32, _i32, _intp])
 _sig("pkv_bm_create", _i32, [_i32, _i32, ctypes.POINTER(_p)])
 _sig("pkv_bm_destroy", None, [_p])
@@ -197,6 +201,49 @@ def paged_kv_gather(k_out, v_out, k_pool, v_pool, block_tables, context_lens, *,
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), s, n, b, h, d, k_out.shape[1], dt,
         _stream(stream)), "paged_kv_gather")
+
+
+def paged_kv_append_tokens(k_pool, v_pool, k_new, v_new, cu_seqlens, block_tables,
+                           context_lens_pre, *, stream=None):
+    """Write packed token cu_seqlens[s] + j of k_new / v_new [T, kv_heads, head_dim]
+    to position context_lens_pre[s] + j of sequence s."""
+    n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    t = k_new.shape[0]
+    if k_new.shape != (t, h, d) or v_new.shape != (t, h, d):
+        raise ValueError("k_new / v_new must be [num_tokens, kv_heads, head_dim]")
+    s = block_tables.shape[0]
+    if block_tables.dim() != 2 or context_lens_pre.shape != (s,) or cu_seqlens.shape != (s + 1,):
+        raise ValueError("block_tables [num_seqs, max_blocks], context_lens_pre [num_seqs], "
+                         "cu_seqlens [num_seqs + 1]")
+    _check(_lib.paged_kv_append_tokens(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new", k_pool.dtype),
+        _dev(v_new, "v_new", k_pool.dtype), _dev(cu_seqlens, "cu_seqlens", torch.int32), t,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens_pre, "context_lens_pre", torch.int32), s, n, b, h, d, dt,
+        _stream(stream)), "paged_kv_append_tokens")
+
+
+def paged_prefill_attention(out, q, k_pool, v_pool, cu_seqlens, block_tables, context_lens,
+                            *, max_chunk_tokens=None, scale=None, stream=None):
+    """Causal attention of each sequence's chunk (its last n_s positions) over its
+    paged history; q / out [T, q_heads, head_dim] packed by cu_seqlens."""
+    n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    t, hq, dq = q.shape
+    if dq != d or out.shape != q.shape or out.dtype != q.dtype or q.dtype != k_pool.dtype:
+        raise ValueError("q / out must be [num_tokens, q_heads, head_dim] in the pool dtype")
+    s = block_tables.shape[0]
+    if block_tables.dim() != 2 or context_lens.shape != (s,) or cu_seqlens.shape != (s + 1,):
+        raise ValueError("block_tables [num_seqs, max_blocks], context_lens [num_seqs], "
+                         "cu_seqlens [num_seqs + 1]")
+    if max_chunk_tokens is None:
+        max_chunk_tokens = t
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(_lib.paged_prefill_attention(
+        _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), s, int(max_chunk_tokens), n, b, hq, h, d,
+        scale, dt, _stream(stream)), "paged_prefill_attention")
 
 
 def paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,

@@ -85,6 +85,43 @@ __global__ __launch_bounds__(kThreads) void append_fp8_kernel(
   }
 }
 
+// Several new tokens per sequence (prefill chunks): thread i copies 16-byte
+// chunk i % row_chunks of packed token i / row_chunks.  The token's sequence
+// is the s with cu[s] <= token < cu[s + 1] (binary search; cu is
+// non-decreasing), its position lens_pre[s] + token - cu[s] ([pofe] "How it
+// works": prefill writes the prompt into its blocks).
+__global__ __launch_bounds__(kThreads) void append_tokens_kernel(
+    char* __restrict__ k_pool, char* __restrict__ v_pool, const char* __restrict__ k_new,
+    const char* __restrict__ v_new, const int32_t* __restrict__ cu, int num_tokens,
+    const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ lens_pre,
+    int num_seqs, int num_blocks, int log2_b, int num_kv_heads, int head_dim, int elem_bytes) {
+  const size_t row_bytes = (size_t)num_kv_heads * head_dim * elem_bytes;
+  const int row_chunks = (int)(row_bytes / 16);
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (long long)num_tokens * row_chunks) return;
+  const int tok = (int)(i / row_chunks);
+  const int c = (int)(i - (long long)tok * row_chunks);
+  if (tok < cu[0] || tok >= cu[num_seqs]) return;           // not in any chunk
+  int lo = 0, hi = num_seqs - 1;                            // last s with cu[s] <= tok
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= tok) lo = mid;
+    else hi = mid - 1;
+  }
+  const int s = lo;
+  const int start = lens_pre[s];
+  if (start < 0) return;                                    // padding row
+  const int pos = start + (tok - cu[s]);
+  const int lb = logical_block(pos, log2_b);
+  if (pos < 0 || lb >= max_blocks) return;                  // past the table row: skip
+  const int blk = tables[(size_t)s * max_blocks + lb];
+  if (!valid_block(blk, num_blocks)) return;                // id outside the pool: skip
+  const size_t dst = row_offset(blk, pos, log2_b, num_kv_heads, 0, head_dim) * elem_bytes;
+  const size_t src = (size_t)tok * row_bytes;
+  store16(k_pool + dst + 16 * (size_t)c, load16(k_new + src + 16 * (size_t)c));
+  store16(v_pool + dst + 16 * (size_t)c, load16(v_new + src + 16 * (size_t)c));
+}
+
 // blockIdx.x = pair, blockIdx.y = slice of the block's chunks.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     char* __restrict__ k_pool, char* __restrict__ v_pool, const int32_t* __restrict__ src,
@@ -149,6 +186,30 @@ extern "C" int paged_kv_append(void* k_pool, void* v_pool, const void* k_new, co
   hipLaunchKernelGGL(append_kernel, dim3(num_seqs), dim3(kThreads), 0, (hipStream_t)stream,
                      (char*)k_pool, (char*)v_pool, (const char*)k_new, (const char*)v_new,
                      block_tables, max_blocks_per_seq, context_lens_pre, num_blocks,
+                     log2_exact(block_size), num_kv_heads, head_dim, dtype_bytes(dtype));
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" int paged_kv_append_tokens(void* k_pool, void* v_pool, const void* k_new,
+                                      const void* v_new, const int32_t* cu_seqlens,
+                                      int num_tokens, const int32_t* block_tables,
+                                      int max_blocks_per_seq, const int32_t* context_lens_pre,
+                                      int num_seqs, int num_blocks, int block_size,
+                                      int num_kv_heads, int head_dim, int dtype, void* stream) {
+  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq < 1) return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !cu_seqlens || !block_tables ||
+      !context_lens_pre)
+    return PKV_ERR_INVALID_ARG;
+  const long long row_chunks = (long long)num_kv_heads * head_dim * dtype_bytes(dtype) / 16;
+  const long long blocks = (num_tokens * row_chunks + kThreads - 1) / kThreads;
+  if (blocks > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(append_tokens_kernel, dim3((unsigned)blocks), dim3(kThreads), 0,
+                     (hipStream_t)stream, (char*)k_pool, (char*)v_pool, (const char*)k_new,
+                     (const char*)v_new, cu_seqlens, num_tokens, block_tables,
+                     max_blocks_per_seq, context_lens_pre, num_seqs, num_blocks,
                      log2_exact(block_size), num_kv_heads, head_dim, dtype_bytes(dtype));
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

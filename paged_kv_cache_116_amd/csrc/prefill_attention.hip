@@ -1,0 +1,307 @@
+// prefill_attention.hip - causal chunked prefill over the paged KV cache (gfx950).
+//
+// Sources cited by tag and section:
+//   [pofe]   "PagedAttention: paging the KV cache"
+//   [lesson] "PagedAttention" lesson in "How Text Is Generated"
+//
+// What is computed ([pofe] "How it works": at admission prefill writes the
+// prompt into freshly allocated blocks, and attention over a block table is
+// the ordinary attention sum, one row of weights per query, regrouped by
+// block; [pofe] "When memory runs out" and [lesson] "Preemption": a
+// recomputed sequence is prefilled again in one pass): sequence s holds L_s
+// positions in the pool, its chunk of n_s query tokens is its last n_s
+// positions, and query j (position p = L_s - n_s + j) attends positions
+// 0 .. p, the decode rule applied to every token of the chunk:
+//     out[j, h] = sum_{t <= p} softmax_t(scale * q[j, h] . K[t, h / g]) V[t, h / g]
+//
+// Work decomposition: one workgroup per (64-row block, KV head, sequence),
+// where a row is a (chunk token, query head of the KV head's group) pair,
+// token-major, so the g heads of a token sit in consecutive rows.  Each of
+// the 4 waves owns 16 rows.  The workgroup streams 16-token K/V tiles from
+// position 0 to the causal limit of its last row through two LDS buffers
+// (loads of tile k+1 in flight while tile k is used); every wave reads the
+// shared tiles.  Per wave and tile, as in the decode kernel:
+//   S^T[16 keys x 16 rows] = K . Q^T   (D/32 v_mfma_f32_16x16x32)
+//   causal mask per row, running max with lazy rescale, exp2
+//   O^T[D x 16 rows] += V^T . P^T      (D/16 v_mfma_f32_16x16x16; P stays in
+//                                       registers, V^T comes from
+//                                       transposing LDS reads)
+// Workgroups loop over further row blocks with stride gridDim.x, so any grid
+// width covers every chunk.
+#include <math.h>
+
+#include "pkv_common.h"
+#include "pkv_host.h"
+#include "pkv_mfma.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kTile = 16;
+constexpr int kRows = 16 * kWaves;        // rows per workgroup
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct PrefillParams {
+  void* out;
+  const void* q;
+  const char* k_pool;
+  const char* v_pool;
+  const int32_t* tables;
+  const int32_t* lens;
+  const int32_t* cu;
+  int max_blocks;
+  int num_blocks;
+  int log2_b;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;          // g = Hq / Hkv
+  float scale_log2;   // scale * log2(e)
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParams p) {
+  using S = typename T::storage;
+  constexpr int LPR = D / 8;                  // 16-byte chunks per K/V row
+  constexpr int KCH = D / 32;                 // MFMA k-chunks of 32 channels
+  constexpr int VP = D + 16;                  // V tile row pitch (elements)
+  constexpr int NCH = kTile * LPR;            // chunks per tile and pool
+  constexpr int CPT = (NCH + kThreads - 1) / kThreads;
+  static_assert(D % 32 == 0 && D <= 256, "head size");
+
+  // K tiles: chunk c of row r at c ^ kswz(r), conflict-free for the row-wise
+  // writes and the operand reads.  V tiles: rows padded by 32 bytes, so the
+  // transposed reads of a 16-lane group hit distinct banks.
+  __shared__ __align__(16) uint4 k_lds[2][kTile * LPR];
+  __shared__ __align__(16) uint16_t v_lds[2][kTile * VP];
+  __shared__ int bad_lds;
+  auto kswz = [](int r) {
+    if constexpr (LPR >= 16) return r & 15;
+    else if constexpr (LPR == 8) return (r >> 1) & 7;
+    else return (r >> 2) & 3;
+  };
+
+  const int s = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;    // score tile: key row / query row column
+  const int kgrp = lane >> 4;
+  const int g = p.group;
+  const int cu0 = p.cu[s];
+  const int n = p.cu[s + 1] - cu0;
+  const int L = p.lens[s];
+  const int rows = n * g;
+  const int max_len = p.max_blocks << p.log2_b;
+  // A chunk longer than its history, or a history past the table, has no
+  // defined result: its rows are NaN.
+  const bool invalid = n > L || L > max_len;
+  const int32_t* trow = p.tables + (size_t)s * p.max_blocks;
+
+  for (int rb = blockIdx.x; rb * kRows < rows; rb += gridDim.x) {
+    // This lane's row (column `col` of the wave's 16).
+    const int r = rb * kRows + w * 16 + col;
+    const bool row_ok = r < rows;
+    const int i = row_ok ? r / g : 0;
+    const int hh = row_ok ? r - i * g : 0;
+    const int h = kvh * g + hh;
+    const int pos = L - n + i;              // the row's position; keys 0 .. pos
+    S* orow = (S*)p.out + ((size_t)(cu0 + i) * p.num_q_heads + h) * D;
+
+    if (invalid) {   // uniform across the workgroup
+      if (row_ok) {
+        for (int d = kgrp; d < D; d += 4) Cvt<T>::store(orow + d, __builtin_nanf(""));
+      }
+      continue;
+    }
+
+    // Causal limits: the workgroup reads keys up to its last row's position,
+    // each wave computes up to its own last row's.
+    const int last_row = min(rb * kRows + kRows, rows) - 1;
+    const int tiles = (L - n + last_row / g) / kTile + 1;
+    const int w_first = rb * kRows + w * 16;
+    const int w_last = min(w_first + 16, rows) - 1;
+    const int w_tiles = w_first < rows ? (L - n + w_last / g) / kTile + 1 : 0;
+
+    // B operand of the score product: row `col`, channels 32j + 8*kgrp .. +7.
+    uint4 qop[KCH];
+    {
+      const S* qrow = (const S*)p.q + ((size_t)(cu0 + i) * p.num_q_heads + h) * D + kgrp * 8;
+#pragma unroll
+      for (int j = 0; j < KCH; ++j)
+        qop[j] = row_ok ? load16(qrow + 32 * j) : make_uint4(0, 0, 0, 0);
+    }
+
+    // Tile loads: thread tid takes chunks tid + 256u of the tile, the same
+    // chunk of K and of V; rows past L - 1 read row L - 1 (masked anyway).
+    int bad = 0;
+    uint4 kreg[CPT], vreg[CPT];
+    auto load_tile = [&](int kt) {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = tid + kThreads * u;
+        if (NCH % kThreads == 0 || c < NCH) {
+          const int row = c / LPR;
+          const int ch = c - row * LPR;
+          const int t = min(kt * kTile + row, L - 1);
+          int blk = trow[t >> p.log2_b];
+          if (!valid_block(blk, p.num_blocks)) {
+            bad = 1;
+            blk = 0;
+          }
+          const size_t off =
+              row_offset(blk, t, p.log2_b, p.num_kv_heads, kvh, D) * T::bytes + ch * 16;
+          kreg[u] = load16(p.k_pool + off);
+          vreg[u] = load16(p.v_pool + off);
+        }
+      }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = tid + kThreads * u;
+        if (NCH % kThreads == 0 || c < NCH) {
+          const int row = c / LPR;
+          const int ch = c - row * LPR;
+          k_lds[buf][row * LPR + (ch ^ kswz(row))] = kreg[u];
+          *reinterpret_cast<uint4*>(&v_lds[buf][row * VP + ch * 8]) = vreg[u];
+        }
+      }
+    };
+
+    float m_run = -INFINITY;   // running maximum of row `col` (log2 units)
+    float l_run = 0.f;         // normaliser partial: keys of C row group kgrp
+    f32x4_t acc[D / 16];       // O^T: block j holds channels 16j + 4*kgrp .. +3
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    if (tid == 0) bad_lds = 0;
+    load_tile(0);
+    for (int kt = 0; kt < tiles; ++kt) {
+      const int buf = kt & 1;
+      store_tile(buf);
+      // Tile kt visible to every wave; also, every wave is done with buffer
+      // buf ^ 1 (read in iteration kt - 1) before it is written next.
+      lds_barrier();
+      if (kt + 1 < tiles) load_tile(kt + 1);
+      if (kt < w_tiles) {
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KCH; ++j)
+          sc = Mfma<T>::run(k_lds[buf][col * LPR + ((4 * j + kgrp) ^ kswz(col))], qop[j], sc);
+        // Lane (col, kgrp) holds keys 16kt + 4*kgrp + e of row col.
+        const int t0 = kt * kTile + 4 * kgrp;
+        float sv[4];
+        float mt = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sv[e] = (row_ok && t0 + e <= pos) ? sc[e] * p.scale_log2 : -INFINITY;
+          mt = fmaxf(mt, sv[e]);
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        // Every row's first tile holds key 0, so m_run is finite from then on
+        // (rows past the chunk stay at -inf and are never written).
+        if (__any(mt > m_run + kRescaleThreshold)) {
+          const float mn = fmaxf(m_run, mt);
+          const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_run - mn);
+          m_run = mn;
+          l_run *= alpha;
+#pragma unroll
+          for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
+        }
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = m_run == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run);
+        // P rounded to the element type; l sums the same rounded values.
+        const uint32_t q01 = Pair<T>::pack(pv[0], pv[1]);
+        const uint32_t q23 = Pair<T>::pack(pv[2], pv[3]);
+        l_run += (Pair<T>::lo(q01) + Pair<T>::hi(q01)) + (Pair<T>::lo(q23) + Pair<T>::hi(q23));
+        const uint2 pop = make_uint2(q01, q23);
+        // A operand of block j: V[4*kgrp + e][16j + col], one transposed read.
+        const uint16_t* vt = &v_lds[buf][(4 * kgrp + (col >> 2)) * VP + 4 * (col & 3)];
+#pragma unroll
+        for (int j = 0; j < D / 16; ++j)
+          acc[j] = Mfma16<T>::run(lds_read_tr16(vt + 16 * j), pop, acc[j]);
+      }
+    }
+    if (bad) bad_lds = 1;
+    lds_barrier();
+    const bool any_bad = bad_lds != 0;
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    if (row_ok) {
+      const float inv = 1.f / l_run;
+      const float nan = __builtin_nanf("");
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) {
+        S* o = orow + 16 * j + 4 * kgrp;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Cvt<T>::store(o + e, any_bad ? nan : acc[j][e] * inv);
+      }
+    }
+    // LDS buffers and bad_lds are reused by the next row block.
+    lds_barrier();
+  }
+}
+
+template <typename T>
+hipError_t launch_prefill(const PrefillParams& p, int head_dim, dim3 grid, hipStream_t st) {
+  switch (head_dim) {
+    case 32: hipLaunchKernelGGL((attn_prefill_mfma<T, 32>), grid, dim3(kThreads), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((attn_prefill_mfma<T, 64>), grid, dim3(kThreads), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((attn_prefill_mfma<T, 128>), grid, dim3(kThreads), 0, st, p); break;
+    default: hipLaunchKernelGGL((attn_prefill_mfma<T, 256>), grid, dim3(kThreads), 0, st, p); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int paged_prefill_attention(void* out, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* cu_seqlens,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, int num_seqs,
+                                       int max_chunk_tokens, int num_blocks, int block_size,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       float scale, int dtype, void* stream) {
+  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (head_dim % 32 != 0) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_seqs > 65535 || max_chunk_tokens < 0 || max_blocks_per_seq < 1 ||
+      num_q_heads < 1 || num_kv_heads > 65535 || num_q_heads % num_kv_heads != 0 ||
+      !(scale > 0.f) || scale == INFINITY)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || max_chunk_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !cu_seqlens || !block_tables || !context_lens)
+    return PKV_ERR_INVALID_ARG;
+  PrefillParams p;
+  p.out = out;
+  p.q = q;
+  p.k_pool = (const char*)k_pool;
+  p.v_pool = (const char*)v_pool;
+  p.tables = block_tables;
+  p.lens = context_lens;
+  p.cu = cu_seqlens;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_blocks = num_blocks;
+  p.log2_b = log2_exact(block_size);
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.scale_log2 = scale * kLog2e;
+  // The grid's width only sets the parallelism: workgroups loop over any
+  // further row blocks of their (KV head, sequence).
+  const long long row_blocks = ((long long)max_chunk_tokens * p.group + kRows - 1) / kRows;
+  const dim3 grid((unsigned)std::min<long long>(row_blocks, 65535), num_kv_heads, num_seqs);
+  const hipError_t e = dtype == PKV_F16 ? launch_prefill<F16>(p, head_dim, grid, (hipStream_t)stream)
+                                        : launch_prefill<BF16>(p, head_dim, grid, (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}

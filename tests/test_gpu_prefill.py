@@ -1,0 +1,216 @@
+"""GPU parity of the multi-token append and the chunked-prefill attention.
+
+The append must match oracle.cache_ops.append_tokens bit for bit.  Prefill
+attention must match oracle.attention.prefill_attention (float64) within the
+16-bit tolerance |gpu - ref| <= 2e-2 + 1e-2 |ref|; the oracle's inputs are
+host copies of the seeded workload, never GPU results.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attention as o_attn
+from oracle import cache_ops as o_cache
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_kv_cache_116_amd as pkv
+else:  # collected on CPU only to be deselected by -m "not gpu"
+    pkv = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.init()
+
+
+def f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def i32(a):
+    return torch.as_tensor(np.asarray(a, dtype=np.int32), device="cuda")
+
+
+def check_close(gpu, ref, label):
+    g = gpu.detach().float().cpu().double().numpy()
+    err = np.abs(g - ref)
+    print(f"  {label} max_abs={err.max():.3e}", flush=True)
+    assert np.isfinite(g).all(), label
+    bad = err > 2e-2 + 1e-2 * np.abs(ref)
+    assert not bad.any(), f"{label}: {int(bad.sum())} elements out of tolerance"
+
+
+def run_append(w):
+    kp, vp = w.k_pool.cuda(), w.v_pool.cuda()
+    pkv.paged_kv_append_tokens(kp, vp, w.k_new.cuda(), w.v_new.cuda(), i32(w.cu), i32(w.tables),
+                               i32(w.lens_pre))
+    return kp, vp
+
+
+def bits(t):
+    """The raw element bits of a tensor as a numpy integer array (the oracle's
+    append is a byte move, so it runs on these directly and NaN payloads
+    survive untouched)."""
+    it = {1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()]
+    return t.detach().cpu().view(it).numpy()
+
+
+def oracle_pools(w):
+    return o_cache.append_tokens(f64(w.k_pool), f64(w.v_pool), f64(w.k_new), f64(w.v_new),
+                                 w.tables, w.lens_pre, w.cu, w.block_size)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("B", [4, 8, 16, 32])
+def test_append_tokens_is_bit_exact(dtype, B):
+    w = workloads.make_prefill_workload(31 + B, lens=[5, 40, 17, 64, 9], chunks=[5, 7, 0, 33, 1],
+                                        block_size=B, num_q_heads=4, num_kv_heads=2,
+                                        head_dim=32, dtype=dtype, spare_blocks=3)
+    kp, vp = run_append(w)
+    torch.cuda.synchronize()
+    ek, ev = o_cache.append_tokens(bits(w.k_pool), bits(w.v_pool), bits(w.k_new),
+                                   bits(w.v_new), w.tables, w.lens_pre, w.cu, w.block_size)
+    assert np.array_equal(bits(kp), ek)
+    assert np.array_equal(bits(vp), ev)
+
+
+def test_append_tokens_padding_rows_and_packed_gaps():
+    # Sequence 1 is a padding row (negative length): its tokens write nothing.
+    w = workloads.make_prefill_workload(7, lens=[12, 20, 6], chunks=[4, 6, 6], block_size=4,
+                                        num_q_heads=2, num_kv_heads=1, head_dim=16,
+                                        dtype="f16")
+    lens_pre = w.lens_pre.copy()
+    lens_pre[1] = -1
+    kp, vp = w.k_pool.cuda(), w.v_pool.cuda()
+    pkv.paged_kv_append_tokens(kp, vp, w.k_new.cuda(), w.v_new.cuda(), i32(w.cu),
+                               i32(w.tables), i32(lens_pre))
+    torch.cuda.synchronize()
+    ek, ev = o_cache.append_tokens(bits(w.k_pool), bits(w.v_pool), bits(w.k_new),
+                                   bits(w.v_new), w.tables, lens_pre, w.cu, 4)
+    assert np.array_equal(bits(kp), ek)
+    assert np.array_equal(bits(vp), ev)
+
+
+PREFILL_CASES = [
+    # Hq, Hkv, D, B, dtype, lens, chunks
+    (8, 1, 128, 16, "bf16", [1, 17, 300, 40, 1000], [1, 5, 64, 33, 1]),
+    (8, 2, 64, 8, "f16", [100, 37, 250], [100, 37, 17]),
+    (32, 8, 128, 16, "bf16", [129, 64, 700], [129, 16, 80]),
+    (4, 4, 32, 32, "bf16", [90, 3, 257], [45, 3, 256]),
+    (16, 2, 256, 16, "f16", [200, 33], [70, 33]),
+    (6, 3, 128, 4, "bf16", [50, 123], [50, 1]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_prefill_matches_oracle(case):
+    Hq, Hkv, D, B, dtype, lens, chunks = PREFILL_CASES[case]
+    w = workloads.make_prefill_workload(100 + case, lens=lens, chunks=chunks, block_size=B,
+                                        num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                        dtype=dtype)
+    kp, vp = run_append(w)
+    out = torch.empty_like(w.q, device="cuda")
+    pkv.paged_prefill_attention(out, w.q.cuda(), kp, vp, i32(w.cu), i32(w.tables), i32(w.lens),
+                                max_chunk_tokens=int(max(chunks)))
+    torch.cuda.synchronize()
+    ek, ev = oracle_pools(w)
+    ref = o_attn.prefill_attention(f64(w.q), ek, ev, w.tables, w.lens, w.cu, B, w.scale)
+    check_close(out, ref, f"prefill case {case}")
+
+
+def test_prefill_grid_narrower_than_the_chunks():
+    # max_chunk_tokens = 1: each workgroup loops over every row block.
+    w = workloads.make_prefill_workload(5, lens=[300, 150], chunks=[300, 90], block_size=16,
+                                        num_q_heads=8, num_kv_heads=2, head_dim=128)
+    kp, vp = run_append(w)
+    a = torch.empty_like(w.q, device="cuda")
+    b = torch.empty_like(w.q, device="cuda")
+    args = (w.q.cuda(), kp, vp, i32(w.cu), i32(w.tables), i32(w.lens))
+    pkv.paged_prefill_attention(a, *args, max_chunk_tokens=1)
+    pkv.paged_prefill_attention(b, *args, max_chunk_tokens=300)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_one_token_chunks_agree_with_decode():
+    w = workloads.make_prefill_workload(9, lens=[1, 33, 500, 64], chunks=[1, 1, 1, 1],
+                                        block_size=16, num_q_heads=16, num_kv_heads=2,
+                                        head_dim=128)
+    kp, vp = run_append(w)
+    out = torch.empty_like(w.q, device="cuda")
+    pkv.paged_prefill_attention(out, w.q.cuda(), kp, vp, i32(w.cu), i32(w.tables), i32(w.lens))
+    dec = torch.empty_like(out)
+    ws = torch.empty(pkv.paged_decode_workspace_bytes(4, 16, 128, int(w.lens.max())),
+                     dtype=torch.uint8, device="cuda")
+    pkv.paged_decode_attention(dec, w.q.cuda(), kp, vp, i32(w.tables), i32(w.lens), workspace=ws)
+    torch.cuda.synchronize()
+    ek, ev = oracle_pools(w)
+    ref = o_attn.decode_attention(f64(w.q), ek, ev, w.tables, w.lens, 16)
+    check_close(out, ref, "one-token chunks")
+    check_close(dec, ref, "decode on the same pools")
+
+
+def test_invalid_sequences_get_nan_rows_only():
+    w = workloads.make_prefill_workload(3, lens=[40, 30, 20], chunks=[10, 30, 5], block_size=16,
+                                        num_q_heads=4, num_kv_heads=1, head_dim=64)
+    kp, vp = run_append(w)
+    lens = w.lens.copy()
+    lens[1] = 29          # the chunk (30 tokens) is longer than the history
+    out = torch.zeros_like(w.q, device="cuda")
+    pkv.paged_prefill_attention(out, w.q.cuda(), kp, vp, i32(w.cu), i32(w.tables), i32(lens))
+    torch.cuda.synchronize()
+    o = out.float().cpu()
+    assert torch.isnan(o[w.cu[1]:w.cu[2]]).all()
+    assert torch.isfinite(o[: w.cu[1]]).all() and torch.isfinite(o[w.cu[2]:]).all()
+
+
+def test_bad_block_id_gives_nan_not_a_fault():
+    w = workloads.make_prefill_workload(4, lens=[40, 40], chunks=[8, 8], block_size=16,
+                                        num_q_heads=4, num_kv_heads=1, head_dim=64)
+    kp, vp = run_append(w)
+    tables = w.tables.copy()
+    tables[0, 1] = w.num_blocks + 5          # outside the pool
+    out = torch.zeros_like(w.q, device="cuda")
+    pkv.paged_prefill_attention(out, w.q.cuda(), kp, vp, i32(w.cu), i32(tables), i32(w.lens))
+    torch.cuda.synchronize()
+    o = out.float().cpu()
+    assert torch.isnan(o[:8]).all()
+    assert torch.isfinite(o[8:]).all()
+
+
+def test_full_size_prefill_sampled_tokens():
+    # The default batch: 16 whole prompts (~15.6k tokens), 32 / 8 heads of 128.
+    w = workloads.make_prefill_workload(device="cuda")
+    # Host copies of the inputs first: the GPU append below writes the pools
+    # in place.
+    kpool_h, vpool_h = f64(w.k_pool), f64(w.v_pool)
+    knew_h, vnew_h = f64(w.k_new), f64(w.v_new)
+    kp, vp = run_append(w)
+    out = torch.empty_like(w.q)
+    pkv.paged_prefill_attention(out, w.q, kp, vp, i32(w.cu), i32(w.tables), i32(w.lens),
+                                max_chunk_tokens=int(w.chunks.max()))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    # A query token's output depends on its query and positions 0..p only:
+    # the oracle runs each sampled token as a one-token chunk over the
+    # p + 1 positions of its sequence (host copies of the seeded inputs).
+    rng = np.random.default_rng(1)
+    for s in rng.choice(len(w.lens), 3, replace=False):
+        s = int(s)
+        one = dict(tables=w.tables[s:s + 1], lens_pre=w.lens_pre[s:s + 1],
+                   cu=np.array([0, w.chunks[s]]))
+        ek, ev = o_cache.append_tokens(kpool_h, vpool_h, knew_h[w.cu[s]:w.cu[s + 1]],
+                                       vnew_h[w.cu[s]:w.cu[s + 1]], one["tables"],
+                                       one["lens_pre"], one["cu"], w.block_size)
+        for j in sorted(set([0, int(w.chunks[s]) - 1] + rng.integers(0, w.chunks[s], 4).tolist())):
+            p = int(w.lens[s] - w.chunks[s] + j)
+            q1 = f64(w.q[w.cu[s] + j: w.cu[s] + j + 1])
+            ref = o_attn.prefill_attention(q1, ek, ev, one["tables"], [p + 1], [0, 1],
+                                           w.block_size, w.scale)
+            check_close(out[w.cu[s] + j: w.cu[s] + j + 1], ref, f"seq {s} token {j}")

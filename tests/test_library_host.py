@@ -116,6 +116,49 @@ def test_fp8_entry_points_validate_arguments():
         pkv.PKV_ERR_INVALID_ARG
 
 
+def prefill(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, tables=FAKE, mb=4, lens=FAKE, s=2, mc=8,
+             n=16, b=16, hq=8, hkv=2, d=128, scale=0.1, dt=2, stream=None)
+    a.update(kw)
+    return lib.paged_prefill_attention(a["out"], a["q"], a["k"], a["v"], a["cu"], a["tables"],
+                                       a["mb"], a["lens"], a["s"], a["mc"], a["n"], a["b"],
+                                       a["hq"], a["hkv"], a["d"], a["scale"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=7, hkv=2), pkv.PKV_ERR_INVALID_ARG),
+    (dict(d=16), pkv.PKV_ERR_UNSUPPORTED),         # the matrix-core kernel needs D % 32 == 0
+    (dict(d=96), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(dt=0), pkv.PKV_ERR_UNSUPPORTED),         # F32
+    (dict(dt=3), pkv.PKV_ERR_UNSUPPORTED),         # FP8 pools
+    (dict(b=12), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(s=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(mc=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(cu=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(q=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(scale=0.0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
+    (dict(s=0, q=None), pkv.PKV_OK),               # nothing to do
+    (dict(mc=0, q=None), pkv.PKV_OK),
+])
+def test_prefill_rejects_bad_arguments(kw, code):
+    assert prefill(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 4, FAKE, 2, 16, 16, 2, 128, 2, None),
+     pkv.PKV_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, -1, FAKE, 4, FAKE, 2, 16, 16, 2, 128, 2, None),
+     pkv.PKV_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 16, 12, 2, 128, 2, None),
+     pkv.PKV_ERR_UNSUPPORTED),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, 4, FAKE, 2, 16, 16, 2, 128, 2, None), pkv.PKV_OK),
+    ((None, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, FAKE, 0, 16, 16, 2, 128, 2, None), pkv.PKV_OK),
+])
+def test_append_tokens_validates_arguments(args, code):
+    assert lib.paged_kv_append_tokens(*args) == code
+
+
 def test_zero_sequences_is_a_noop():
     assert attn(s=0) == pkv.PKV_OK
     assert lib.paged_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, 16, 16, 2, 128, 2, None) == 0

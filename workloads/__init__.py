@@ -285,3 +285,108 @@ def extract_sequences(w: Workload, seqs, dtype=np.float64):
     return dict(k_pool=pool(w.k_pool[idx]), v_pool=pool(w.v_pool[idx]), tables=tables,
                 lens=w.lens[seqs].copy(), lens_pre=w.lens_pre[seqs].copy(),
                 q=host(w.q[sel]), k_new=host(w.k_new[sel]), v_new=host(w.v_new[sel]))
+
+
+# ---------------------------------------------------------------------------
+# Prefill chunks
+# ---------------------------------------------------------------------------
+
+PREFILL_NAME = "prefill_gqa32x8_bf16"
+
+
+@dataclass
+class PrefillWorkload:
+    """A packed prefill batch over a paged cache.
+
+    Sequence s has ``lens[s]`` positions once its chunk is appended; the
+    chunk is its last ``chunks[s]`` positions.  The pool holds positions
+    0 .. lens[s] - chunks[s] - 1; the chunk's keys and values are in
+    ``k_new`` / ``v_new`` (packed by ``cu``), its queries in ``q``.  Every
+    other slot is NaN when poisoned.
+    """
+    name: str
+    dtype: str
+    block_size: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    num_blocks: int
+    lens: np.ndarray        # int32 [S]
+    chunks: np.ndarray      # int32 [S]
+    cu: np.ndarray          # int32 [S + 1]
+    tables: np.ndarray      # int32 [S, max_blocks], -1 padded
+    q: torch.Tensor         # [T, H_q, D]
+    k_new: torch.Tensor     # [T, H_kv, D]
+    v_new: torch.Tensor
+    k_pool: torch.Tensor    # [N, B, H_kv, D]
+    v_pool: torch.Tensor
+    seed: int = 0
+
+    @property
+    def lens_pre(self) -> np.ndarray:
+        return (self.lens - self.chunks).astype(np.int32)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+def make_prefill_workload(seed: int = 2000, *, batch: int = 16, lens=None, chunks=None,
+                          block_size: int = 16, num_q_heads: int = 32, num_kv_heads: int = 8,
+                          head_dim: int = 128, dtype: str = "bf16", device="cpu",
+                          poison: bool = True, spare_blocks: int = 1) -> PrefillWorkload:
+    """Draw a prefill batch.  Default: whole prompts (chunk = history) with the
+    prompt-length law of the [pofe] "Simulation: batch size doubles,
+    throughput does not" section (log-normal, median 584 and 95th percentile
+    2,155 tokens, at most 4,096), on the 32 query / 8 KV heads of 128 of the
+    [arch] "Production PyTorch Implementation" driver.  ``lens`` / ``chunks``
+    override the draw (chunks default to the whole history)."""
+    rng = np.random.default_rng(seed)
+    if lens is None:
+        sigma = math.log(2155 / 584) / 1.6448536269514722
+        lens = np.rint(np.exp(rng.normal(math.log(584), sigma, size=batch)))
+        lens = np.clip(lens, 16, 4096)
+    lens = np.asarray(lens, dtype=np.int64)
+    chunks = lens.copy() if chunks is None else np.asarray(chunks, dtype=np.int64)
+    if chunks.shape != lens.shape or (chunks < 0).any() or (chunks > lens).any():
+        raise ValueError("chunks must lie in [0, lens]")
+    B = block_size
+    nbs = [-(-int(L) // B) for L in lens]
+    num_blocks = sum(nbs) + spare_blocks
+    perm = rng.permutation(num_blocks)
+    tables = np.full((len(lens), max(max(nbs), 1)), -1, dtype=np.int32)
+    pos = 0
+    for s, n in enumerate(nbs):
+        tables[s, :n] = perm[pos:pos + n]
+        pos += n
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    T = int(cu[-1])
+
+    tdtype = DTYPES[dtype]
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(tdtype)
+
+    q = randn(T, num_q_heads, head_dim)
+    k_new = randn(T, num_kv_heads, head_dim)
+    v_new = randn(T, num_kv_heads, head_dim)
+    k_pool = randn(num_blocks, B, num_kv_heads, head_dim)
+    v_pool = randn(num_blocks, B, num_kv_heads, head_dim)
+    if poison:
+        empty = np.ones((num_blocks, B), dtype=bool)     # slots holding no token yet
+        for s, n in enumerate(nbs):
+            held = int(lens[s] - chunks[s])
+            for t in range(held):
+                empty[tables[s, t // B], t % B] = False
+        mask = torch.as_tensor(empty, device=dev)
+        k_pool[mask] = float("nan")
+        v_pool[mask] = float("nan")
+    return PrefillWorkload(name=PREFILL_NAME, dtype=dtype, block_size=B,
+                           num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                           head_dim=head_dim, num_blocks=num_blocks,
+                           lens=lens.astype(np.int32), chunks=chunks.astype(np.int32), cu=cu,
+                           tables=tables, q=q, k_new=k_new, v_new=v_new, k_pool=k_pool,
+                           v_pool=v_pool, seed=seed)
