@@ -14,6 +14,10 @@ Default workload: the 70B-shaped GQA decode batch (64 query / 8 KV heads of
 128, bf16, B = 16, 256 sequences with log-uniform lengths in [512, 8192],
 pool of 1.1x the needed blocks with shuffled ids), drawn on the GPU.
 
+`--workload prefill` times the chunked-prefill path instead: the
+multi-token append of 16 whole prompts and causal prefill attention over
+them (tokens/s, with the attention kernel priced against the MFMA peak).
+
 Prints one JSON line.  `value` is KV GB/s over the whole step: valid key and
 value bytes of every sequence, divided by the step time.  The `roofline`
 object prices the partition kernel (the dominant one) against the 8 TB/s HBM
@@ -51,6 +55,10 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+                    help="decode: the paged decode step on --config (default); prefill: "
+                         "multi-token append + causal chunked-prefill attention on a batch of "
+                         "16 whole prompts (32 q / 8 kv heads of 128, bf16, B 16)")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-tokens", type=int, default=0,
@@ -112,6 +120,8 @@ def main(argv=None) -> int:
         return 2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "prefill":
+        return run_prefill(args, torch, pkv, workloads, dev)
 
     calib = None
     if args.calibrate:
@@ -370,6 +380,163 @@ def main(argv=None) -> int:
                                 else f"attn_partition_{kname}"),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "copy_gbps": round(copy_gbps, 1) if copy_gbps else None,
+        "parity": parity,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0 if (parity is None or parity["ok"]) else 1
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 matrix peak
+
+
+def run_prefill(args, torch, pkv, workloads, dev) -> int:
+    """A step: paged_kv_append_tokens of every prompt's keys and values, then
+    paged_prefill_attention over them (whole prompts, causal).  `value` is
+    prompt tokens per second over the step; the roofline prices the
+    attention kernel's algorithmic matrix flops, 4 * D per (query head,
+    visible key) pair, against the dense bf16 MFMA peak."""
+    t0 = time.time()
+    w = workloads.make_prefill_workload(device=dev)
+    torch.cuda.synchronize()
+    S, T = len(w.lens), int(w.cu[-1])
+    Hq, Hkv, D, B = w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    print(f"# workload {w.name}: {S} prompts, {T} tokens, blocks={w.num_blocks}, "
+          f"drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    # Host copies for the oracle, before any library call writes the pools.
+    rng = np.random.default_rng(7)
+    check = sorted(rng.choice(S, size=2, replace=False).tolist())
+    host = {k: getattr(w, k).detach().to("cpu").to(torch.float64).numpy()
+            for k in ("k_pool", "v_pool", "k_new", "v_new", "q")} if not args.no_check else None
+
+    pre_len = (w.lens - w.chunks).astype(np.int64)
+    visible = sum(int(((pre_len[s] + np.arange(w.chunks[s]) + 1)).sum()) for s in range(S))
+    flops = 4.0 * D * Hq * visible
+    tables = torch.as_tensor(w.tables, device=dev)
+    lens = torch.as_tensor(w.lens, device=dev)
+    lens_pre = torch.as_tensor(w.lens_pre, device=dev)
+    cu = torch.as_tensor(w.cu, device=dev)
+    out = torch.empty_like(w.q)
+    max_chunk = int(w.chunks.max())
+    stream = torch.cuda.current_stream()
+
+    def append():
+        pkv.paged_kv_append_tokens(w.k_pool, w.v_pool, w.k_new, w.v_new, cu, tables, lens_pre,
+                                   stream=stream)
+
+    def attention():
+        pkv.paged_prefill_attention(out, w.q, w.k_pool, w.v_pool, cu, tables, lens,
+                                    max_chunk_tokens=max_chunk, scale=w.scale, stream=stream)
+
+    def step():
+        append()
+        attention()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    start, end = ev(), ev()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    marks = [[ev() for _ in range(3)] for _ in range(args.steps)]
+    for m in marks:
+        m[0].record(stream)
+        append()
+        m[1].record(stream)
+        attention()
+        m[2].record(stream)
+    torch.cuda.synchronize()
+    t_app = statistics.mean(m[0].elapsed_time(m[1]) for m in marks)
+    t_attn = [m[1].elapsed_time(m[2]) for m in marks]
+    attn_ms = statistics.mean(t_attn)
+    print(f"# timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, attention {attn_ms * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
+    parity = None
+    cpu = None
+    if host is not None or args.cpu_seconds > 0:
+        from oracle import attention as o_attn
+        from oracle import cache_ops as o_cache
+
+        def oracle_token(s, j):
+            """Output of chunk token j of prompt s, as a one-token chunk over
+            its p + 1 visible positions."""
+            sl = slice(int(w.cu[s]), int(w.cu[s + 1]))
+            kp, vp = o_cache.append_tokens(host["k_pool"], host["v_pool"], host["k_new"][sl],
+                                           host["v_new"][sl], w.tables[s:s + 1],
+                                           w.lens_pre[s:s + 1], [0, int(w.chunks[s])], B)
+            p = int(pre_len[s] + j)
+            q1 = host["q"][int(w.cu[s]) + j: int(w.cu[s]) + j + 1]
+            return o_attn.prefill_attention(q1, kp, vp, w.tables[s:s + 1], [p + 1], [0, 1], B,
+                                            w.scale)
+
+        if host is not None:
+            errs, ok = [], True
+            for s in check:
+                for j in sorted(set([0, int(w.chunks[s]) - 1] +
+                                    rng.integers(0, int(w.chunks[s]), 3).tolist())):
+                    ref = oracle_token(s, j)
+                    got = out[int(w.cu[s]) + j: int(w.cu[s]) + j + 1].double().cpu().numpy()
+                    err = np.abs(got - ref)
+                    errs.append(float(err.max()))
+                    ok &= bool(np.isfinite(got).all() and (err <= 2e-2 + 1e-2 * np.abs(ref)).all())
+            parity = {"sampled_prompts": check, "max_abs_err": max(errs), "ok": ok}
+        if args.cpu_seconds > 0 and host is not None:
+            # The oracle on the shortest prompt, whole (append + attention),
+            # repeated for the time budget; single threaded.
+            os.environ.setdefault("OMP_NUM_THREADS", "1")
+            s = int(np.argmin(w.chunks))
+            sl = slice(int(w.cu[s]), int(w.cu[s + 1]))
+            spent, passes = 0.0, 0
+            while spent < args.cpu_seconds:
+                t = time.perf_counter()
+                kp, vp = o_cache.append_tokens(host["k_pool"], host["v_pool"], host["k_new"][sl],
+                                               host["v_new"][sl], w.tables[s:s + 1],
+                                               w.lens_pre[s:s + 1], [0, int(w.chunks[s])], B)
+                o_attn.prefill_attention(host["q"][sl], kp, vp, w.tables[s:s + 1],
+                                         w.lens[s:s + 1], [0, int(w.chunks[s])], B, w.scale)
+                spent += time.perf_counter() - t
+                passes += 1
+            cpu = {"value": round(passes * int(w.chunks[s]) / spent, 2), "unit": "tokens/s",
+                   "cores": 1, "kind": "oracle",
+                   "sample": f"prompt {s} ({int(w.chunks[s])} tokens) of the batch, whole, "
+                             f"{passes} pass(es) in {spent:.1f}s, append + float64 causal "
+                             "attention"}
+            print(f"# cpu oracle: {cpu['value']} tokens/s over {spent:.1f}s", file=sys.stderr,
+                  flush=True)
+
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    result = {
+        "metric": "paged prefill tokens/s (attention TFLOP/s vs MFMA peak)",
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": "prefill: 16 whole prompts, log-normal lengths (median 584, p95 "
+                               "2155, at most 4096), 32 q / 8 kv heads, D 128, B 16, bf16",
+                   "name": w.name, "prompts": S, "tokens": T, "block_size": B,
+                   "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D},
+        "us": {"step": round(ms_step * 1e3, 2), "append": round(t_app * 1e3, 2),
+               "attention": round(attn_ms * 1e3, 2),
+               "attention_p10": round(float(np.percentile(t_attn, 10)) * 1e3, 2),
+               "attention_p90": round(float(np.percentile(t_attn, 90)) * 1e3, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_prefill_mfma", "algorithmic_flops_per_launch": flops},
         "parity": parity,
         "cpu_baseline": cpu,
     }
