@@ -19,6 +19,10 @@ Semantics follow [pofe] "Minimal implementation" (``BlockPool`` and
   [arch] 4. steps 1-4; [pofe] ``Sequence.append``).  The slot written is
   len mod B of the last entry; len then grows by one.
 
+Preemption by swapping ([pofe] "When memory runs out") moves a whole
+sequence out (every block released, its contents to be copied to host
+memory) and back in (fresh blocks, all or none).
+
 Running out of blocks raises :class:`NoFreeBlock` ([pofe] raises MemoryError
 asking for a preemption; [arch] Step 1 raises MemoryError as well) and leaves
 every table and count as it was.  The data movement itself (block copy,
@@ -70,6 +74,7 @@ class OracleSequence:
         self.pool = pool
         self.table: list[int] = []
         self.len = 0
+        self.swapped = False
 
     def reserve_prompt(self, n_tokens: int) -> None:
         """Admission: allocate ceil(n / B) blocks for an n-token prompt
@@ -89,6 +94,8 @@ class OracleSequence:
         [note] "Shared prefixes can share physical storage")."""
         if self.table or self.len:
             raise ValueError("adopt_prefix is for an empty sequence")
+        if source.swapped:
+            raise ValueError("a swapped-out sequence has no blocks to share")
         if n_blocks * self.pool.block_size > source.len:
             raise ValueError("only full blocks of the source can be adopted")
         self.table = [self.pool.share(i) for i in source.table[:n_blocks]]
@@ -98,6 +105,8 @@ class OracleSequence:
         """Admit ``n_tokens`` more prompt tokens after the current length,
         allocating the blocks they need; the current last block must not be a
         shared partial block (prefill never writes into shared blocks)."""
+        if self.swapped:
+            raise ValueError("swap the sequence in first")
         b = self.pool.block_size
         if self.len % b != 0 and self.pool.ref[self.table[-1]] > 1:
             raise ValueError("cannot extend into a shared partial block")
@@ -108,6 +117,8 @@ class OracleSequence:
         self.len += n_tokens
 
     def fork(self) -> "OracleSequence":
+        if self.swapped:
+            raise ValueError("swap the sequence in first")
         child = OracleSequence(self.pool)
         child.table = [self.pool.share(i) for i in self.table]
         child.len = self.len
@@ -116,6 +127,8 @@ class OracleSequence:
     def append_slot(self):
         """Decide where the next token goes; returns (block, slot, cow) with
         cow = (old, new) when a copy-on-write is needed, else None."""
+        if self.swapped:
+            raise ValueError("swap the sequence in first")
         b = self.pool.block_size
         cow = None
         if self.len % b == 0:
@@ -130,8 +143,38 @@ class OracleSequence:
         self.len += 1
         return block, slot, cow
 
+    def swap_out(self) -> list[int]:
+        """Preempt by swapping ([pofe] "When memory runs out": whole
+        sequences, all or none of their blocks, are copied to CPU memory).
+        Returns the table (the blocks to copy out, slot i = logical block i)
+        and releases every block; the length is kept.  Reading: shared blocks
+        are copied as well and their references dropped, so a swapped-in
+        sequence owns private copies."""
+        if self.swapped:
+            raise ValueError("sequence already swapped out")
+        out = list(self.table)
+        for i in self.table:
+            self.pool.release(i)
+        self.table = []
+        self.swapped = True
+        return out
+
+    def swap_in(self) -> list[int]:
+        """Bring a swapped sequence back: allocate ceil(len / B) blocks, all
+        or none ([pofe]: whole sequences), and return them in table order
+        (host slot i goes to block i)."""
+        if not self.swapped:
+            raise ValueError("sequence is not swapped out")
+        need = -(-self.len // self.pool.block_size)
+        if need > self.pool.num_free():
+            raise NoFreeBlock("not enough free blocks to swap the sequence in")
+        self.table = [self.pool.alloc() for _ in range(need)]
+        self.swapped = False
+        return list(self.table)
+
     def free_all(self) -> None:
         for i in self.table:
             self.pool.release(i)
         self.table = []
         self.len = 0
+        self.swapped = False

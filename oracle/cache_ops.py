@@ -91,3 +91,36 @@ def append_tokens(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
             k_out[physical, offset] = k_new[cu[s] + j]
             v_out[physical, offset] = v_new[cu[s] + j]
     return k_out, v_out
+
+
+def swap_out(k_pool: np.ndarray, v_pool: np.ndarray, ids):
+    """Copy whole blocks ids[i] to host buffers slot i; return (host_k, host_v).
+
+    [pofe] "When memory runs out": a preempted sequence's blocks are copied
+    to CPU memory and back later; [lesson] "Preemption": copy blocks to
+    pinned host memory and back.  The host buffers are [n, B, H_kv, D]; slot
+    i holds block ids[i] bit for bit.
+    """
+    ids = [int(x) for x in ids]
+    num_blocks = k_pool.shape[0]
+    if any(not (0 <= i < num_blocks) for i in ids):
+        raise IndexError("block id outside the pool")
+    return k_pool[ids].copy(), v_pool[ids].copy()
+
+
+def swap_in(k_pool: np.ndarray, v_pool: np.ndarray, ids, host_k: np.ndarray,
+            host_v: np.ndarray):
+    """Copy host slot i back into block ids[i]; return new pools.  The ids
+    must be distinct (each names the block a swapped-in sequence now owns)."""
+    ids = [int(x) for x in ids]
+    num_blocks = k_pool.shape[0]
+    if len(set(ids)) != len(ids):
+        raise ValueError("swap-in destinations must be distinct")
+    if any(not (0 <= i < num_blocks) for i in ids):
+        raise IndexError("block id outside the pool")
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    for slot, i in enumerate(ids):
+        k_out[i] = host_k[slot]
+        v_out[i] = host_v[slot]
+    return k_out, v_out
