@@ -336,6 +336,33 @@ int paged_decode_step_fp8(int kernel, void* out, const void* q, void* k_pool, vo
                           int dtype, void* stream);
 
 /* ------------------------------------------------------------------------- */
+/* Swap: preemption to host memory                                           */
+/* ------------------------------------------------------------------------- */
+
+/*
+ * [pofe] "When memory runs out": a preempted sequence's blocks (all or none)
+ * are copied to CPU memory and back later; [lesson] "Preemption": swap copies
+ * blocks to pinned host memory and back, costing link bandwidth and no
+ * compute.  One launch moves any list of scattered blocks:
+ *   block_ids      : device int32 [num], block i of the list;
+ *   host_k, host_v : pinned, device-mapped host memory (hipHostMalloc, or a
+ *                    torch tensor made with pin_memory=True), each
+ *                    [num, block_size, num_kv_heads, head_dim] of the pool
+ *                    dtype (any pool dtype, FP8 included): slot i holds block
+ *                    block_ids[i], bit for bit.
+ * An id outside [0, num_blocks) is skipped (its slot or block is left
+ * untouched).  Swap-in destinations must be distinct.  The host buffers must
+ * stay allocated until the stream has finished the copy.  The block manager
+ * (pkv_bm_seq_swap_out / _in) decides which blocks move.
+ */
+int paged_kv_swap_out(const void* k_pool, const void* v_pool, const int32_t* block_ids, int num,
+                      void* host_k, void* host_v, int num_blocks, int block_size,
+                      int num_kv_heads, int head_dim, int dtype, void* stream);
+int paged_kv_swap_in(void* k_pool, void* v_pool, const int32_t* block_ids, int num,
+                     const void* host_k, const void* host_v, int num_blocks, int block_size,
+                     int num_kv_heads, int head_dim, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------- */
 /* Chunked prefill                                                           */
 /* ------------------------------------------------------------------------- */
 
@@ -440,6 +467,21 @@ int pkv_bm_append_batch(pkv_block_manager* bm, const int* seqs, int n, int32_t* 
                         int32_t* slot_out, int32_t* cow_src_out, int32_t* cow_dst_out,
                         int* num_cow_out);
 int pkv_bm_seq_free(pkv_block_manager* bm, int seq);        /* release all blocks; id retired */
+/* Preemption by swapping ([pofe] "When memory runs out": whole sequences).
+ * swap_out writes seq's table (the blocks to copy out with paged_kv_swap_out;
+ * host slot i = logical block i) to blocks_out[0..*n_out), releases every
+ * block, shared ones included, and keeps the length; the sequence is then
+ * swapped: append, extend, fork, adopt-prefix and export refuse it
+ * (PKV_ERR_INVALID_ARG).  Enqueue the copy before any work that may write
+ * the released blocks.  swap_in allocates ceil(len / B) fresh blocks, all or
+ * none (PKV_ERR_NO_FREE_BLOCK changes nothing), and writes them in table
+ * order for paged_kv_swap_in; sharing is not restored.  cap is the room in
+ * blocks_out (too small: PKV_ERR_INVALID_ARG, nothing changes). */
+int pkv_bm_seq_swap_out(pkv_block_manager* bm, int seq, int32_t* blocks_out, int cap,
+                        int* n_out);
+int pkv_bm_seq_swap_in(pkv_block_manager* bm, int seq, int32_t* blocks_out, int cap,
+                       int* n_out);
+int pkv_bm_seq_is_swapped(const pkv_block_manager* bm, int seq);   /* 1, 0, or error */
 int pkv_bm_seq_len(const pkv_block_manager* bm, int seq);   /* >= 0, or error */
 int pkv_bm_seq_num_blocks(const pkv_block_manager* bm, int seq);
 /* Copy up to cap table entries of seq into out; returns the count copied. */

@@ -79,6 +79,11 @@ _sig("paged_kv_append_tokens", _i32,
      [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("paged_prefill_attention", _i32,
      [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p])
+_sig("paged_kv_swap_out", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
+_sig("paged_kv_swap_in", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
+_sig("pkv_bm_seq_swap_out", _i32, [_p, _i32, _p, _i32, _intp])
+_sig("pkv_bm_seq_swap_in", _i32, [_p, _i32, _p, _i32, _intp])
+_sig("pkv_bm_seq_is_swapped", _i32, [_p, _i32])
 _sig("pkv_validate_tables", _i32, [_p, _i32, _p, _i32, _i32, _i32, _intp])
 _sig("pkv_bm_create", _i32, [_i32, _i32, ctypes.POINTER(_p)])
 _sig("pkv_bm_destroy", None, [_p])
@@ -201,6 +206,38 @@ def paged_kv_gather(k_out, v_out, k_pool, v_pool, block_tables, context_lens, *,
         _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
         _dev(context_lens, "context_lens", torch.int32), s, n, b, h, d, k_out.shape[1], dt,
         _stream(stream)), "paged_kv_gather")
+
+
+def _host_blocks(t: torch.Tensor, name: str, shape, dtype) -> int:
+    if not isinstance(t, torch.Tensor) or t.is_cuda or not t.is_pinned():
+        raise ValueError(f"{name} must be a pinned host tensor (pin_memory=True)")
+    if not t.is_contiguous() or tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)}")
+    return t.data_ptr()
+
+
+def paged_kv_swap_out(k_pool, v_pool, block_ids, host_k, host_v, *, stream=None):
+    """Copy blocks block_ids[i] of both pools to pinned host slots i."""
+    n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    m = block_ids.shape[0]
+    shape = (m, b, h, d)
+    _check(_lib.paged_kv_swap_out(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(block_ids, "block_ids", torch.int32),
+        m, _host_blocks(host_k, "host_k", shape, k_pool.dtype),
+        _host_blocks(host_v, "host_v", shape, k_pool.dtype), n, b, h, d, dt, _stream(stream)),
+        "paged_kv_swap_out")
+
+
+def paged_kv_swap_in(k_pool, v_pool, block_ids, host_k, host_v, *, stream=None):
+    """Copy pinned host slots i back into blocks block_ids[i] (distinct)."""
+    n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    m = block_ids.shape[0]
+    shape = (m, b, h, d)
+    _check(_lib.paged_kv_swap_in(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(block_ids, "block_ids", torch.int32),
+        m, _host_blocks(host_k, "host_k", shape, k_pool.dtype),
+        _host_blocks(host_v, "host_v", shape, k_pool.dtype), n, b, h, d, dt, _stream(stream)),
+        "paged_kv_swap_in")
 
 
 def paged_kv_append_tokens(k_pool, v_pool, k_new, v_new, cu_seqlens, block_tables,
@@ -436,6 +473,28 @@ class BlockManager:
 
     def seq_free(self, seq: int) -> None:
         _check(_lib.pkv_bm_seq_free(self._h, seq), "pkv_bm_seq_free")
+
+    def seq_swap_out(self, seq: int) -> list:
+        """Preempt seq by swapping: returns its table (blocks to copy out, host
+        slot i = logical block i) and releases every block."""
+        cap = max(1, self.seq_num_blocks(seq))
+        buf = (ctypes.c_int32 * cap)()
+        n = ctypes.c_int()
+        _check(_lib.pkv_bm_seq_swap_out(self._h, seq, buf, cap, ctypes.byref(n)),
+               "pkv_bm_seq_swap_out")
+        return list(buf[: n.value])
+
+    def seq_swap_in(self, seq: int) -> list:
+        """Fresh blocks for a swapped sequence (all or none), in table order."""
+        cap = max(1, -(-self.seq_len(seq) // self.block_size))
+        buf = (ctypes.c_int32 * cap)()
+        n = ctypes.c_int()
+        _check(_lib.pkv_bm_seq_swap_in(self._h, seq, buf, cap, ctypes.byref(n)),
+               "pkv_bm_seq_swap_in")
+        return list(buf[: n.value])
+
+    def seq_is_swapped(self, seq: int) -> bool:
+        return bool(_check(_lib.pkv_bm_seq_is_swapped(self._h, seq), "pkv_bm_seq_is_swapped"))
 
     def seq_len(self, seq: int) -> int:
         return _check(_lib.pkv_bm_seq_len(self._h, seq), "pkv_bm_seq_len")

@@ -60,6 +60,7 @@ struct pkv_block_manager {
     std::vector<int32_t> table;
     int len = 0;
     bool live = false;
+    bool swapped = false;   // preempted by swapping: no blocks, length kept
   };
   int num_blocks = 0;
   int block_size = 0;
@@ -69,6 +70,8 @@ struct pkv_block_manager {
 
   bool block_ok(int b) const { return b >= 0 && b < num_blocks; }
   bool seq_ok(int s) const { return s >= 0 && s < (int)seqs.size() && seqs[s].live; }
+  // A live sequence that holds its blocks (not swapped out).
+  bool seq_resident(int s) const { return seq_ok(s) && !seqs[s].swapped; }
 
   int alloc() {   // caller has checked that the free list is not empty
     const int i = free_list.back();
@@ -170,7 +173,7 @@ extern "C" int pkv_bm_seq_new(pkv_block_manager* bm, int* seq_out) {
 }
 
 extern "C" int pkv_bm_seq_extend(pkv_block_manager* bm, int seq, int n_tokens) {
-  if (!bm || !bm->seq_ok(seq) || n_tokens < 0) return PKV_ERR_INVALID_ARG;
+  if (!bm || !bm->seq_resident(seq) || n_tokens < 0) return PKV_ERR_INVALID_ARG;
   auto& q = bm->seqs[seq];
   const int b = bm->block_size;
   if (q.len % b != 0 && bm->ref[q.table.back()] > 1) return PKV_ERR_INVALID_ARG;
@@ -184,7 +187,7 @@ extern "C" int pkv_bm_seq_extend(pkv_block_manager* bm, int seq, int n_tokens) {
 }
 
 extern "C" int pkv_bm_seq_adopt_prefix(pkv_block_manager* bm, int seq, int src, int n_blocks) {
-  if (!bm || !bm->seq_ok(seq) || !bm->seq_ok(src) || n_blocks < 0 || seq == src)
+  if (!bm || !bm->seq_resident(seq) || !bm->seq_resident(src) || n_blocks < 0 || seq == src)
     return PKV_ERR_INVALID_ARG;
   auto& q = bm->seqs[seq];
   const auto& from = bm->seqs[src];
@@ -199,7 +202,7 @@ extern "C" int pkv_bm_seq_adopt_prefix(pkv_block_manager* bm, int seq, int src, 
 }
 
 extern "C" int pkv_bm_seq_fork(pkv_block_manager* bm, int parent, int* child_out) {
-  if (!bm || !bm->seq_ok(parent) || !child_out) return PKV_ERR_INVALID_ARG;
+  if (!bm || !bm->seq_resident(parent) || !child_out) return PKV_ERR_INVALID_ARG;
   int child = -1;
   int st = pkv_bm_seq_new(bm, &child);
   if (st != PKV_OK) return st;
@@ -214,7 +217,7 @@ extern "C" int pkv_bm_seq_fork(pkv_block_manager* bm, int parent, int* child_out
 
 extern "C" int pkv_bm_seq_append_slot(pkv_block_manager* bm, int seq, int* block_out,
                                       int* slot_out, int* cow_src_out) {
-  if (!bm || !bm->seq_ok(seq) || !block_out || !slot_out || !cow_src_out)
+  if (!bm || !bm->seq_resident(seq) || !block_out || !slot_out || !cow_src_out)
     return PKV_ERR_INVALID_ARG;
   auto& q = bm->seqs[seq];
   if (q.len == 0x7fffffff) return PKV_ERR_INVALID_ARG;
@@ -241,7 +244,8 @@ extern "C" int pkv_bm_append_batch(pkv_block_manager* bm, const int* seqs, int n
   }
   for (int i = 0; i < n; ++i) {
     const int s = seqs[i];
-    if (!bm->seq_ok(s) || seen[s] || bm->seqs[s].len == 0x7fffffff) return PKV_ERR_INVALID_ARG;
+    if (!bm->seq_resident(s) || seen[s] || bm->seqs[s].len == 0x7fffffff)
+      return PKV_ERR_INVALID_ARG;
     seen[s] = 1;
     need += bm->append_need(bm->seqs[s]);
   }
@@ -270,7 +274,54 @@ extern "C" int pkv_bm_seq_free(pkv_block_manager* bm, int seq) {
   q.table.shrink_to_fit();
   q.len = 0;
   q.live = false;
+  q.swapped = false;
   return PKV_OK;
+}
+
+// Preemption by swapping ([pofe] "When memory runs out": whole sequences, all
+// or none of their blocks, are copied to CPU memory and back).  swap_out hands
+// back the table (the blocks to copy out; host slot i = logical block i) and
+// releases every block, shared ones included; swap_in allocates fresh blocks
+// for the kept length, all or none.
+extern "C" int pkv_bm_seq_swap_out(pkv_block_manager* bm, int seq, int32_t* blocks_out, int cap,
+                                   int* n_out) {
+  if (!bm || !bm->seq_resident(seq) || !n_out || cap < 0) return PKV_ERR_INVALID_ARG;
+  auto& q = bm->seqs[seq];
+  const int n = (int)q.table.size();
+  if (n > cap || (n > 0 && !blocks_out)) return PKV_ERR_INVALID_ARG;
+  for (int j = 0; j < n; ++j) blocks_out[j] = q.table[j];
+  for (int32_t b : q.table) bm->release(b);
+  q.table.clear();
+  q.swapped = true;
+  *n_out = n;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_seq_swap_in(pkv_block_manager* bm, int seq, int32_t* blocks_out, int cap,
+                                  int* n_out) {
+  if (!bm || !bm->seq_ok(seq) || !bm->seqs[seq].swapped || !n_out || cap < 0)
+    return PKV_ERR_INVALID_ARG;
+  auto& q = bm->seqs[seq];
+  const int need = (int)(((long long)q.len + bm->block_size - 1) / bm->block_size);
+  if (need > cap || (need > 0 && !blocks_out)) return PKV_ERR_INVALID_ARG;
+  if (need > (int)bm->free_list.size()) return PKV_ERR_NO_FREE_BLOCK;
+  try {
+    q.table.reserve(need);
+  } catch (...) {
+    return PKV_ERR_INVALID_ARG;
+  }
+  for (int j = 0; j < need; ++j) {
+    q.table.push_back(bm->alloc());
+    blocks_out[j] = q.table.back();
+  }
+  q.swapped = false;
+  *n_out = need;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_seq_is_swapped(const pkv_block_manager* bm, int seq) {
+  if (!bm || !bm->seq_ok(seq)) return PKV_ERR_INVALID_ARG;
+  return bm->seqs[seq].swapped ? 1 : 0;
 }
 
 extern "C" int pkv_bm_seq_len(const pkv_block_manager* bm, int seq) {
@@ -297,7 +348,7 @@ extern "C" int pkv_bm_export_tables(const pkv_block_manager* bm, const int* seqs
   if (n == 0) return PKV_OK;
   if (!seqs || !out || !lens_out) return PKV_ERR_INVALID_ARG;
   for (int i = 0; i < n; ++i) {
-    if (!bm->seq_ok(seqs[i]) || (int)bm->seqs[seqs[i]].table.size() > ld)
+    if (!bm->seq_resident(seqs[i]) || (int)bm->seqs[seqs[i]].table.size() > ld)
       return PKV_ERR_INVALID_ARG;
   }
   for (int i = 0; i < n; ++i) {

@@ -138,6 +138,33 @@ __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
   }
 }
 
+// Swap ([pofe] "When memory runs out": a preempted sequence's blocks are
+// copied to CPU memory and back; [lesson] "Preemption": pinned host memory).
+// blockIdx.x = list entry i, blockIdx.y = slice of the block's chunks.  The
+// host buffers are pinned, device-mapped memory: the kernel reads or writes
+// them directly over the host link, one 16-byte chunk per thread, so one
+// launch moves any set of scattered blocks.
+template <bool kToHost>
+__global__ __launch_bounds__(kThreads) void swap_kernel(
+    char* __restrict__ k_pool, char* __restrict__ v_pool, char* __restrict__ host_k,
+    char* __restrict__ host_v, const int32_t* __restrict__ ids, int num_blocks,
+    size_t block_bytes) {
+  const int b = ids[blockIdx.x];
+  if (!valid_block(b, num_blocks)) return;
+  const size_t chunks = block_bytes / 16;
+  const size_t pb = (size_t)b * block_bytes, hb = (size_t)blockIdx.x * block_bytes;
+  for (size_t c = (size_t)blockIdx.y * kThreads + threadIdx.x; c < chunks;
+       c += (size_t)gridDim.y * kThreads) {
+    if constexpr (kToHost) {
+      store16(host_k + hb + 16 * c, load16(k_pool + pb + 16 * c));
+      store16(host_v + hb + 16 * c, load16(v_pool + pb + 16 * c));
+    } else {
+      store16(k_pool + pb + 16 * c, load16(host_k + hb + 16 * c));
+      store16(v_pool + pb + 16 * c, load16(host_v + hb + 16 * c));
+    }
+  }
+}
+
 constexpr int kGatherTokens = 16;
 
 // blockIdx.y = sequence, blockIdx.x = group of kGatherTokens tokens.
@@ -260,6 +287,44 @@ extern "C" int paged_kv_copy_blocks(void* k_pool, void* v_pool, const int32_t* s
                      (hipStream_t)stream, (char*)k_pool, (char*)v_pool, src, dst, num_blocks,
                      block_bytes);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+static int swap_blocks(bool to_host, void* k_pool, void* v_pool, void* host_k, void* host_v,
+                       const int32_t* block_ids, int num, int num_blocks, int block_size,
+                       int num_kv_heads, int head_dim, int dtype, void* stream) {
+  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  if (num < 0 || num > 0x7fffffff / 2) return PKV_ERR_INVALID_ARG;
+  if (num == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !host_k || !host_v || !block_ids) return PKV_ERR_INVALID_ARG;
+  const size_t block_bytes = (size_t)block_size * num_kv_heads * head_dim * dtype_bytes(dtype);
+  const size_t chunks = block_bytes / 16;
+  const int slices = (int)std::min<size_t>(16, (chunks + kThreads - 1) / kThreads);
+  if (to_host)
+    hipLaunchKernelGGL(swap_kernel<true>, dim3(num, slices), dim3(kThreads), 0,
+                       (hipStream_t)stream, (char*)k_pool, (char*)v_pool, (char*)host_k,
+                       (char*)host_v, block_ids, num_blocks, block_bytes);
+  else
+    hipLaunchKernelGGL(swap_kernel<false>, dim3(num, slices), dim3(kThreads), 0,
+                       (hipStream_t)stream, (char*)k_pool, (char*)v_pool, (char*)host_k,
+                       (char*)host_v, block_ids, num_blocks, block_bytes);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" int paged_kv_swap_out(const void* k_pool, const void* v_pool,
+                                 const int32_t* block_ids, int num, void* host_k, void* host_v,
+                                 int num_blocks, int block_size, int num_kv_heads, int head_dim,
+                                 int dtype, void* stream) {
+  return swap_blocks(true, (void*)k_pool, (void*)v_pool, host_k, host_v, block_ids, num,
+                     num_blocks, block_size, num_kv_heads, head_dim, dtype, stream);
+}
+
+extern "C" int paged_kv_swap_in(void* k_pool, void* v_pool, const int32_t* block_ids, int num,
+                                const void* host_k, const void* host_v, int num_blocks,
+                                int block_size, int num_kv_heads, int head_dim, int dtype,
+                                void* stream) {
+  return swap_blocks(false, k_pool, v_pool, (void*)host_k, (void*)host_v, block_ids, num,
+                     num_blocks, block_size, num_kv_heads, head_dim, dtype, stream);
 }
 
 extern "C" int paged_kv_gather(void* k_out, void* v_out, const void* k_pool, const void* v_pool,

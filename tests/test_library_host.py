@@ -359,3 +359,77 @@ def test_cpp_manager_matches_oracle_on_random_operations(seed):
         row = tables[i].tolist()
         assert row[: len(o.table)] == o.table and all(x == -1 for x in row[len(o.table):])
         assert lens[i] == o.len
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cpp_swap_matches_oracle_on_random_operations(seed):
+    rng = np.random.default_rng(500 + seed)
+    N = int(rng.integers(8, 40))
+    B = int(rng.choice([1, 2, 4, 8]))
+    opool = OracleBlockPool(N, B)
+    bm = pkv.BlockManager(N, B)
+    live = []   # (oracle seq, cpp id)
+
+    def same_state():
+        assert bm.num_free() == opool.num_free()
+        assert [bm.refcount(i) for i in range(N)] == opool.ref
+        for o, c in live:
+            assert bm.seq_table(c) == o.table and bm.seq_len(c) == o.len
+            assert bm.seq_is_swapped(c) == o.swapped
+
+    for _ in range(300):
+        op = int(rng.integers(0, 6))
+        if op == 0 or not live:
+            n = int(rng.integers(1, 3 * B + 2))
+            o, c = OracleSequence(opool), bm.seq_new()
+            try:
+                o.reserve_prompt(n)
+                bm.seq_extend(c, n)
+                live.append((o, c))
+            except NoFreeBlock:
+                with pytest.raises(pkv.NoFreeBlockError):
+                    bm.seq_extend(c, n)
+                bm.seq_free(c)
+        else:
+            o, c = live[int(rng.integers(len(live)))]
+            if op == 1 and not o.swapped:
+                live.append((o.fork(), bm.seq_fork(c)))
+            elif op == 2:
+                if o.swapped:
+                    with pytest.raises(pkv.PagedKVError):
+                        bm.seq_append_slot(c)
+                else:
+                    try:
+                        blk, slot, cow = o.append_slot()
+                        assert bm.seq_append_slot(c) == (blk, slot, -1 if cow is None else cow[0])
+                    except NoFreeBlock:
+                        with pytest.raises(pkv.NoFreeBlockError):
+                            bm.seq_append_slot(c)
+            elif op == 3:
+                if o.swapped:
+                    try:
+                        exp = o.swap_in()
+                        assert bm.seq_swap_in(c) == exp
+                    except NoFreeBlock:
+                        with pytest.raises(pkv.NoFreeBlockError):
+                            bm.seq_swap_in(c)
+                else:
+                    assert bm.seq_swap_out(c) == o.swap_out()
+            elif op == 4:
+                o.free_all()
+                bm.seq_free(c)
+                live.remove((o, c))
+            elif op == 5 and o.swapped:
+                with pytest.raises(pkv.PagedKVError):
+                    bm.seq_fork(c)
+                with pytest.raises(pkv.PagedKVError):
+                    bm.seq_swap_out(c)
+        same_state()
+
+
+def test_swap_entry_points_validate_arguments():
+    a = (FAKE, FAKE, FAKE, 4, FAKE, FAKE, 16, 16, 2, 128, 2, None)
+    assert lib.paged_kv_swap_out(*a[:3], -1, *a[4:]) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.paged_kv_swap_out(*a[:4], None, *a[5:]) == pkv.PKV_ERR_INVALID_ARG
+    assert lib.paged_kv_swap_in(*a[:6], 16, 12, *a[8:]) == pkv.PKV_ERR_UNSUPPORTED
+    assert lib.paged_kv_swap_in(*a[:3], 0, *a[4:]) == pkv.PKV_OK
