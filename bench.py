@@ -55,10 +55,12 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", choices=["decode", "prefill"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "swap"], default="decode",
                     help="decode: the paged decode step on --config (default); prefill: "
                          "multi-token append + causal chunked-prefill attention on a batch of "
-                         "16 whole prompts (32 q / 8 kv heads of 128, bf16, B 16)")
+                         "16 whole prompts (32 q / 8 kv heads of 128, bf16, B 16); swap: "
+                         "preempt a quarter of --config's sequences to pinned host memory "
+                         "and back")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None)
     ap.add_argument("--partition-tokens", type=int, default=0,
@@ -122,6 +124,8 @@ def main(argv=None) -> int:
     torch.cuda.set_device(dev)
     if args.workload == "prefill":
         return run_prefill(args, torch, pkv, workloads, dev)
+    if args.workload == "swap":
+        return run_swap(args, torch, pkv, workloads, dev)
 
     calib = None
     if args.calibrate:
@@ -542,6 +546,88 @@ def run_prefill(args, torch, pkv, workloads, dev) -> int:
     }
     print(json.dumps(result), flush=True)
     return 0 if (parity is None or parity["ok"]) else 1
+
+
+HOST_LINK_PEAK_GBPS = 64.0   # PCIe Gen5 x16, one direction
+
+
+def run_swap(args, torch, pkv, workloads, dev) -> int:
+    """A step: swap every fourth sequence of the decode batch out to pinned
+    host memory (paged_kv_swap_out of their blocks, K and V) and back in at
+    the same ids (paged_kv_swap_in).  `value` is bytes moved per second over
+    the step, both directions; each direction is priced against the host
+    link's one-way peak.  The copies are checked bit for bit."""
+    w = workloads.make_workload(args.config, device=dev)
+    B = w.block_size
+    seqs = list(range(0, w.num_seqs, 4))
+    ids = np.concatenate([w.tables[s, : -(-int(w.lens[s]) // B)] for s in seqs]).astype(np.int32)
+    n = len(ids)
+    shape = (n,) + tuple(w.k_pool.shape[1:])
+    hk = torch.empty(shape, dtype=w.k_pool.dtype, pin_memory=True)
+    hv = torch.empty(shape, dtype=w.k_pool.dtype, pin_memory=True)
+    t_ids = torch.as_tensor(ids, device=dev)
+    moved = 2 * hk.numel() * hk.element_size()          # K and V, one direction
+    print(f"# swap: {len(seqs)} of {w.num_seqs} sequences, {n} blocks, "
+          f"{moved / 1e9:.3f} GB per direction", file=sys.stderr, flush=True)
+    ref_k = w.k_pool[t_ids.long()].clone()
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    for _ in range(min(args.warmup, 3)):
+        pkv.paged_kv_swap_out(w.k_pool, w.v_pool, t_ids, hk, hv, stream=stream)
+        pkv.paged_kv_swap_in(w.k_pool, w.v_pool, t_ids, hk, hv, stream=stream)
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 10))
+    t_out, t_in = [], []
+    start, end = ev(), ev()
+    start.record(stream)
+    for _ in range(steps):
+        a, b, c = ev(), ev(), ev()
+        a.record(stream)
+        pkv.paged_kv_swap_out(w.k_pool, w.v_pool, t_ids, hk, hv, stream=stream)
+        b.record(stream)
+        pkv.paged_kv_swap_in(w.k_pool, w.v_pool, t_ids, hk, hv, stream=stream)
+        c.record(stream)
+        t_out.append((a, b))
+        t_in.append((b, c))
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    ms_out = statistics.mean(x.elapsed_time(y) for x, y in t_out)
+    ms_in = statistics.mean(x.elapsed_time(y) for x, y in t_in)
+    ok = bool(torch.equal(hk.view(torch.int16), ref_k.cpu().view(torch.int16)) and
+              torch.equal(w.k_pool[t_ids.long()].view(torch.int16), ref_k.view(torch.int16)))
+    gbps_out = moved / (ms_out * 1e-3) / 1e9
+    gbps_in = moved / (ms_in * 1e-3) / 1e9
+    print(f"# out {ms_out * 1e3:.0f} us ({gbps_out:.1f} GB/s), in {ms_in * 1e3:.0f} us "
+          f"({gbps_in:.1f} GB/s)", file=sys.stderr, flush=True)
+    result = {
+        "metric": "paged KV swap GB/s (out + in, pinned host memory)",
+        "value": round(2 * moved / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": min(args.warmup, 3),
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"swap every fourth sequence of: {WORKLOAD_DESC[args.config]}",
+                   "name": w.name, "sequences": len(seqs), "blocks": n,
+                   "bytes_per_direction": moved},
+        "us": {"step": round(ms_step * 1e3, 1), "swap_out": round(ms_out * 1e3, 1),
+               "swap_in": round(ms_in * 1e3, 1)},
+        "roofline": {"bound": "host-link", "achieved": round(min(gbps_out, gbps_in), 2),
+                     "achieved_out": round(gbps_out, 2), "achieved_in": round(gbps_in, 2),
+                     "peak": HOST_LINK_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(min(gbps_out, gbps_in) / HOST_LINK_PEAK_GBPS, 4),
+                     "traffic": None, "kernel": "swap_kernel"},
+        "parity": {"bit_exact": ok, "ok": ok},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0 if ok else 1
 
 
 if __name__ == "__main__":
