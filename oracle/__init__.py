@@ -32,7 +32,10 @@ Modules:
   cache_ops     cache append (one or several tokens per sequence) and
                 block copy on pool copies
   fp8           E4M3FN codes for FP8 cache blocks: encode, decode, append
-  block_manager free list, reference counts, fork and copy-on-write
+  block_manager free list, reference counts, fork, copy-on-write and
+                preemption by swapping
+  prefix_cache  automatic prefix caching: block-aligned prefixes of token
+                ids looked up and shared, evictable cached blocks
   allocator_toy contiguous-reservation vs paged accounting of a toy workload
 
 Every function in this package is pinned by a ``-m "not gpu"`` test against
