@@ -482,6 +482,26 @@ int pkv_bm_seq_swap_out(pkv_block_manager* bm, int seq, int32_t* blocks_out, int
 int pkv_bm_seq_swap_in(pkv_block_manager* bm, int seq, int32_t* blocks_out, int cap,
                        int* n_out);
 int pkv_bm_seq_is_swapped(const pkv_block_manager* bm, int seq);   /* 1, 0, or error */
+
+/* Automatic prefix caching ([lesson] "Sharing, and the reference counting it
+ * needs": block-aligned prefixes of token ids are looked up in a global table
+ * and shared on a hit, only when every token id is equal; [claims] "Paged
+ * Attention": a hit needs an unbroken matching prefix).
+ * pkv_bm_seq_admit_prompt admits an empty sequence with its prompt token ids
+ * (host int32 [n_tokens]): the longest cached prefix of full blocks is shared
+ * (count + 1), the remaining ceil(n / B) - hits blocks are allocated (all or
+ * none: PKV_ERR_NO_FREE_BLOCK changes nothing), and the new full blocks are
+ * entered under their prefixes.  *cached_tokens_out = hits * B: the caller
+ * writes positions cached .. n-1 (paged_kv_append_tokens) before any
+ * attention reads them, and may run prefill for those positions only
+ * (paged_prefill_attention with context n and chunk n - cached).
+ * Cache keys chain a 64-bit mix over the prefix; an entry also keeps its own
+ * token ids and its parent key, both checked on a hit.  A cached block whose
+ * count falls to 0 stays hittable; it is evicted, oldest first, when an
+ * allocation finds no plain free block.  pkv_bm_num_free counts both kinds. */
+int pkv_bm_seq_admit_prompt(pkv_block_manager* bm, int seq, const int32_t* tokens, int n_tokens,
+                            int* cached_tokens_out);
+int pkv_bm_num_cached(const pkv_block_manager* bm);   /* cached blocks, or error */
 int pkv_bm_seq_len(const pkv_block_manager* bm, int seq);   /* >= 0, or error */
 int pkv_bm_seq_num_blocks(const pkv_block_manager* bm, int seq);
 /* Copy up to cap table entries of seq into out; returns the count copied. */

@@ -84,6 +84,8 @@ _sig("paged_kv_swap_in", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32
 _sig("pkv_bm_seq_swap_out", _i32, [_p, _i32, _p, _i32, _intp])
 _sig("pkv_bm_seq_swap_in", _i32, [_p, _i32, _p, _i32, _intp])
 _sig("pkv_bm_seq_is_swapped", _i32, [_p, _i32])
+_sig("pkv_bm_seq_admit_prompt", _i32, [_p, _i32, _p, _i32, _intp])
+_sig("pkv_bm_num_cached", _i32, [_p])
 _sig("pkv_validate_tables", _i32, [_p, _i32, _p, _i32, _i32, _i32, _intp])
 _sig("pkv_bm_create", _i32, [_i32, _i32, ctypes.POINTER(_p)])
 _sig("pkv_bm_destroy", None, [_p])
@@ -492,6 +494,18 @@ class BlockManager:
         _check(_lib.pkv_bm_seq_swap_in(self._h, seq, buf, cap, ctypes.byref(n)),
                "pkv_bm_seq_swap_in")
         return list(buf[: n.value])
+
+    def seq_admit_prompt(self, seq: int, tokens) -> int:
+        """Admit an empty sequence with its prompt token ids, sharing the
+        longest cached prefix of full blocks; returns the cached token count."""
+        toks = (ctypes.c_int32 * max(1, len(tokens)))(*[int(t) for t in tokens])
+        cached = ctypes.c_int()
+        _check(_lib.pkv_bm_seq_admit_prompt(self._h, seq, toks, len(tokens),
+                                            ctypes.byref(cached)), "pkv_bm_seq_admit_prompt")
+        return cached.value
+
+    def num_cached(self) -> int:
+        return _check(_lib.pkv_bm_num_cached(self._h), "pkv_bm_num_cached")
 
     def seq_is_swapped(self, seq: int) -> bool:
         return bool(_check(_lib.pkv_bm_seq_is_swapped(self._h, seq), "pkv_bm_seq_is_swapped"))

@@ -1,15 +1,22 @@
 // host_runtime.cpp - host side of libpagedkv: status names, version, table
 // validation and the block manager (free list, reference counts, per-sequence
-// tables with fork and copy-on-write).  CPU only; no device calls.
+// tables with fork, copy-on-write, swapping and automatic prefix caching).
+// CPU only; no device calls.
 //
 // Sources cited by tag and section:
-//   [pofe] "PagedAttention: paging the KV cache"
-//   [note] "PagedAttention: Manage the Cache Without Moving the Sequence"
-//   [arch] "PagedAttention: Virtual-Memory KV Cache Management, Continuous
-//          Batching, and PyTorch Architecture"
+//   [pofe]   "PagedAttention: paging the KV cache"
+//   [lesson] "PagedAttention" lesson in "How Text Is Generated"
+//   [note]   "PagedAttention: Manage the Cache Without Moving the Sequence"
+//   [claims] "Paged Attention" claims page
+//   [arch]   "PagedAttention: Virtual-Memory KV Cache Management, Continuous
+//            Batching, and PyTorch Architecture"
 #include <stdint.h>
 
+#include <algorithm>
+#include <iterator>
+#include <list>
 #include <new>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/pagedkv.h"
@@ -68,19 +75,69 @@ struct pkv_block_manager {
   std::vector<int32_t> ref;
   std::vector<Seq> seqs;
 
+  // Automatic prefix caching ([lesson] "Sharing, and the reference counting
+  // it needs": block-aligned prefixes of token ids in a global table; [claims]
+  // "Paged Attention": a hit needs an unbroken matching prefix).  A full
+  // prompt block is keyed by a 64-bit chain over the prefix: key_j =
+  // mix(key_{j-1}, tokens of block j).  An entry keeps its parent key and its
+  // own token ids, and a lookup checks both, so a false hit needs two whole
+  // prefixes whose 64-bit chains collide.  A cached block whose count falls
+  // to 0 keeps its entry and waits in `lru` (oldest first) until a hit
+  // revives it or an allocation with an empty free list evicts it.
+  struct CacheEntry {
+    int32_t block;
+    uint64_t parent;
+    std::vector<int32_t> tokens;
+  };
+  std::unordered_map<uint64_t, CacheEntry> cache;
+  std::vector<uint64_t> key_of;   // per block: its key, when cached[b]
+  std::vector<char> cached;
+  std::list<int32_t> lru;
+  std::vector<std::list<int32_t>::iterator> lru_pos;
+
+  // SplitMix64 finaliser (Steele, Lea and Flood, 2014) as the mixing step.
+  static uint64_t mix(uint64_t x) {
+    x += 0x9e3779b97f4a7c15ULL;
+    x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ULL;
+    x = (x ^ (x >> 27)) * 0x94d049bb133111ebULL;
+    return x ^ (x >> 31);
+  }
+  static uint64_t chain(uint64_t parent, const int32_t* t, int n) {
+    uint64_t k = mix(parent ^ 0x70726566697843ULL);
+    for (int i = 0; i < n; ++i) k = mix(k ^ (uint64_t)(uint32_t)t[i]);
+    return k;
+  }
+  // Blocks an allocation may take: free ones and evictable cached ones.
+  long long allocatable() const { return (long long)free_list.size() + (long long)lru.size(); }
+
   bool block_ok(int b) const { return b >= 0 && b < num_blocks; }
   bool seq_ok(int s) const { return s >= 0 && s < (int)seqs.size() && seqs[s].live; }
   // A live sequence that holds its blocks (not swapped out).
   bool seq_resident(int s) const { return seq_ok(s) && !seqs[s].swapped; }
 
-  int alloc() {   // caller has checked that the free list is not empty
-    const int i = free_list.back();
-    free_list.pop_back();
+  int alloc() {   // caller has checked that allocatable() > 0
+    int i;
+    if (!free_list.empty()) {
+      i = free_list.back();
+      free_list.pop_back();
+    } else {          // evict the oldest cached block with count 0
+      i = lru.front();
+      lru.pop_front();
+      cache.erase(key_of[i]);
+      cached[i] = 0;
+    }
     ref[i] = 1;
     return i;
   }
   void release(int i) {
-    if (--ref[i] == 0) free_list.push_back(i);
+    if (--ref[i] == 0) {
+      if (cached[i]) {
+        lru.push_back(i);
+        lru_pos[i] = std::prev(lru.end());
+      } else {
+        free_list.push_back(i);
+      }
+    }
   }
 
   // Blocks the next append of sequence s needs from the free list (0 or 1):
@@ -121,6 +178,9 @@ extern "C" int pkv_bm_create(int num_blocks, int block_size, pkv_block_manager**
     bm->free_list.resize(num_blocks);
     for (int i = 0; i < num_blocks; ++i) bm->free_list[i] = i;
     bm->ref.assign(num_blocks, 0);
+    bm->key_of.assign(num_blocks, 0);
+    bm->cached.assign(num_blocks, 0);
+    bm->lru_pos.resize(num_blocks);
   } catch (...) {
     delete bm;
     return PKV_ERR_INVALID_ARG;
@@ -133,7 +193,7 @@ extern "C" void pkv_bm_destroy(pkv_block_manager* bm) { delete bm; }
 
 extern "C" int pkv_bm_num_free(const pkv_block_manager* bm) {
   if (!bm) return PKV_ERR_INVALID_ARG;
-  return (int)bm->free_list.size();
+  return (int)bm->allocatable();
 }
 
 extern "C" int pkv_bm_refcount(const pkv_block_manager* bm, int block) {
@@ -143,7 +203,7 @@ extern "C" int pkv_bm_refcount(const pkv_block_manager* bm, int block) {
 
 extern "C" int pkv_bm_alloc(pkv_block_manager* bm, int* block_out) {
   if (!bm || !block_out) return PKV_ERR_INVALID_ARG;
-  if (bm->free_list.empty()) return PKV_ERR_NO_FREE_BLOCK;
+  if (bm->allocatable() == 0) return PKV_ERR_NO_FREE_BLOCK;
   *block_out = bm->alloc();
   return PKV_OK;
 }
@@ -180,7 +240,7 @@ extern "C" int pkv_bm_seq_extend(pkv_block_manager* bm, int seq, int n_tokens) {
   const long long total = (long long)q.len + n_tokens;
   if (total > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   const long long need = (total + b - 1) / b - (long long)q.table.size();
-  if (need > (long long)bm->free_list.size()) return PKV_ERR_NO_FREE_BLOCK;
+  if (need > bm->allocatable()) return PKV_ERR_NO_FREE_BLOCK;
   for (long long i = 0; i < need; ++i) q.table.push_back(bm->alloc());
   q.len = (int)total;
   return PKV_OK;
@@ -221,7 +281,7 @@ extern "C" int pkv_bm_seq_append_slot(pkv_block_manager* bm, int seq, int* block
     return PKV_ERR_INVALID_ARG;
   auto& q = bm->seqs[seq];
   if (q.len == 0x7fffffff) return PKV_ERR_INVALID_ARG;
-  if (bm->append_need(q) > (int)bm->free_list.size()) return PKV_ERR_NO_FREE_BLOCK;
+  if (bm->append_need(q) > bm->allocatable()) return PKV_ERR_NO_FREE_BLOCK;
   bm->append(q, block_out, slot_out, cow_src_out);
   return PKV_OK;
 }
@@ -249,7 +309,7 @@ extern "C" int pkv_bm_append_batch(pkv_block_manager* bm, const int* seqs, int n
     seen[s] = 1;
     need += bm->append_need(bm->seqs[s]);
   }
-  if (need > (long long)bm->free_list.size()) return PKV_ERR_NO_FREE_BLOCK;
+  if (need > bm->allocatable()) return PKV_ERR_NO_FREE_BLOCK;
   int ncow = 0;
   for (int i = 0; i < n; ++i) {
     int blk, slot, cow;
@@ -304,7 +364,7 @@ extern "C" int pkv_bm_seq_swap_in(pkv_block_manager* bm, int seq, int32_t* block
   auto& q = bm->seqs[seq];
   const int need = (int)(((long long)q.len + bm->block_size - 1) / bm->block_size);
   if (need > cap || (need > 0 && !blocks_out)) return PKV_ERR_INVALID_ARG;
-  if (need > (int)bm->free_list.size()) return PKV_ERR_NO_FREE_BLOCK;
+  if (need > bm->allocatable()) return PKV_ERR_NO_FREE_BLOCK;
   try {
     q.table.reserve(need);
   } catch (...) {
@@ -360,4 +420,81 @@ extern "C" int pkv_bm_export_tables(const pkv_block_manager* bm, const int* seqs
     lens_out[i] = q.len;
   }
   return PKV_OK;
+}
+
+// Admission with prefix caching: share the cached blocks of the longest
+// cached block-aligned prefix of `tokens`, allocate the rest (all or none),
+// and enter the new full blocks under their prefixes (the caller writes
+// their positions before any attention reads them).  A prefix already
+// cached under another block, out of the walk's reach because its parent
+// was evicted, keeps that block.
+extern "C" int pkv_bm_seq_admit_prompt(pkv_block_manager* bm, int seq, const int32_t* tokens,
+                                       int n_tokens, int* cached_tokens_out) {
+  if (!bm || !bm->seq_resident(seq) || n_tokens < 0 || !cached_tokens_out ||
+      (n_tokens > 0 && !tokens))
+    return PKV_ERR_INVALID_ARG;
+  auto& q = bm->seqs[seq];
+  if (!q.table.empty() || q.len != 0) return PKV_ERR_INVALID_ARG;
+  const int b = bm->block_size;
+  const int full = n_tokens / b;
+  std::vector<int32_t> hits;
+  std::vector<uint64_t> keys;
+  try {
+    keys.reserve(full);
+    uint64_t parent = 0;
+    for (int j = 0; j < full; ++j) {
+      const int32_t* t = tokens + (size_t)j * b;
+      const uint64_t k = pkv_block_manager::chain(parent, t, b);
+      keys.push_back(k);
+      if (hits.size() == (size_t)j) {
+        auto it = bm->cache.find(k);
+        if (it != bm->cache.end() && it->second.parent == parent &&
+            std::equal(it->second.tokens.begin(), it->second.tokens.end(), t))
+          hits.push_back(it->second.block);
+      }
+      parent = k;
+    }
+  } catch (...) {
+    return PKV_ERR_INVALID_ARG;
+  }
+  const long long need = ((long long)n_tokens + b - 1) / b - (long long)hits.size();
+  long long revived = 0;
+  for (int32_t h : hits) revived += bm->ref[h] == 0 ? 1 : 0;
+  if (need > bm->allocatable() - revived) return PKV_ERR_NO_FREE_BLOCK;
+  try {
+    q.table.reserve(hits.size() + need);
+    bm->cache.reserve(bm->cache.size() + (size_t)(full - (int)hits.size()));
+  } catch (...) {
+    return PKV_ERR_INVALID_ARG;
+  }
+  for (int32_t h : hits) {
+    if (bm->ref[h] == 0) {
+      bm->lru.erase(bm->lru_pos[h]);
+      bm->ref[h] = 1;
+    } else {
+      bm->ref[h] += 1;
+    }
+    q.table.push_back(h);
+  }
+  for (long long i = 0; i < need; ++i) q.table.push_back(bm->alloc());
+  for (int j = (int)hits.size(); j < full; ++j) {
+    const uint64_t k = keys[j];
+    if (bm->cache.count(k)) continue;
+    const int32_t blk = q.table[j];
+    pkv_block_manager::CacheEntry e;
+    e.block = blk;
+    e.parent = j == 0 ? 0 : keys[j - 1];
+    e.tokens.assign(tokens + (size_t)j * b, tokens + (size_t)(j + 1) * b);
+    bm->cache.emplace(k, std::move(e));
+    bm->key_of[blk] = k;
+    bm->cached[blk] = 1;
+  }
+  q.len = n_tokens;
+  *cached_tokens_out = (int)hits.size() * b;
+  return PKV_OK;
+}
+
+extern "C" int pkv_bm_num_cached(const pkv_block_manager* bm) {
+  if (!bm) return PKV_ERR_INVALID_ARG;
+  return (int)bm->cache.size();
 }

@@ -433,3 +433,62 @@ def test_swap_entry_points_validate_arguments():
     assert lib.paged_kv_swap_out(*a[:4], None, *a[5:]) == pkv.PKV_ERR_INVALID_ARG
     assert lib.paged_kv_swap_in(*a[:6], 16, 12, *a[8:]) == pkv.PKV_ERR_UNSUPPORTED
     assert lib.paged_kv_swap_in(*a[:3], 0, *a[4:]) == pkv.PKV_OK
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cpp_prefix_cache_matches_oracle_on_random_traffic(seed):
+    from oracle.prefix_cache import OraclePrefixPool, admit_prompt
+    rng = np.random.default_rng(900 + seed)
+    N = int(rng.integers(10, 48))
+    B = int(rng.choice([1, 2, 4, 8]))
+    opool = OraclePrefixPool(N, B)
+    bm = pkv.BlockManager(N, B)
+    prefixes = [list(rng.integers(0, 30, 3 * B)) for _ in range(3)]
+    live = []
+
+    def same_state():
+        assert bm.num_free() == opool.num_free()
+        assert bm.num_cached() == opool.num_cached()
+        assert [bm.refcount(i) for i in range(N)] == opool.ref
+        for o, c in live:
+            assert bm.seq_table(c) == o.table and bm.seq_len(c) == o.len
+
+    for _ in range(250):
+        op = int(rng.integers(0, 5))
+        if op <= 1 or not live:
+            p = prefixes[int(rng.integers(3))][: int(rng.integers(0, 3 * B + 1))]
+            toks = p + list(rng.integers(0, 30, int(rng.integers(0, 2 * B + 2))))
+            o, c = OracleSequence(opool), bm.seq_new()
+            try:
+                exp = admit_prompt(o, toks)
+                assert bm.seq_admit_prompt(c, toks) == exp
+                live.append((o, c))
+            except NoFreeBlock:
+                with pytest.raises(pkv.NoFreeBlockError):
+                    bm.seq_admit_prompt(c, toks)
+                bm.seq_free(c)
+        elif op == 2:
+            o, c = live[int(rng.integers(len(live)))]
+            try:
+                blk, slot, cow = o.append_slot()
+                assert bm.seq_append_slot(c) == (blk, slot, -1 if cow is None else cow[0])
+            except NoFreeBlock:
+                with pytest.raises(pkv.NoFreeBlockError):
+                    bm.seq_append_slot(c)
+        elif op == 3:
+            o, c = live[int(rng.integers(len(live)))]
+            live.append((o.fork(), bm.seq_fork(c)))
+        else:
+            o, c = live.pop(int(rng.integers(len(live))))
+            o.free_all()
+            bm.seq_free(c)
+        same_state()
+
+
+def test_admit_prompt_validates_arguments():
+    bm = pkv.BlockManager(8, 4)
+    s = bm.seq_new()
+    bm.seq_extend(s, 3)
+    with pytest.raises(pkv.PagedKVError):
+        bm.seq_admit_prompt(s, [1, 2, 3, 4])    # not an empty sequence
+    assert lib.pkv_bm_seq_admit_prompt(None, 0, None, 0, None) == pkv.PKV_ERR_INVALID_ARG
