@@ -220,3 +220,29 @@ def prefill_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                 p = _softmax_weights(z)
                 out[cu[s] + j, h] = p @ v_seq[: pos + 1, kvh, :]
     return out
+
+
+def decode_log_normaliser(q: np.ndarray, k_pool: np.ndarray, tables: np.ndarray, lens,
+                          block_size: int, scale: float | None = None) -> np.ndarray:
+    """Natural log of each head's softmax normaliser in decode attention:
+    lse[s, h] = ln sum_{t<L_s} exp(scale * q[s, h] . K[t, kvh(h)]), computed as
+    max z + ln sum exp(z - max z) (the stabilising shift of the two-pass
+    softmax above).  -inf for an empty sequence.  Two normalised partial
+    results over disjoint key sets combine with these weights, which is how
+    the merge of [arch] 3. reads when each part is already normalised."""
+    q = np.asarray(q, dtype=np.float64)
+    num_seqs, num_q_heads, head_dim = q.shape
+    group = num_q_heads // k_pool.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    out = np.full((num_seqs, num_q_heads), -math.inf)
+    for s in range(num_seqs):
+        length = int(lens[s])
+        if length == 0:
+            continue
+        k_seq = gather_contiguous(k_pool, tables[s], length, block_size).astype(np.float64)
+        for h in range(num_q_heads):
+            z = scale * (k_seq[:, h // group, :] @ q[s, h])
+            zmax = z.max()
+            out[s, h] = zmax + math.log(np.exp(z - zmax).sum())
+    return out

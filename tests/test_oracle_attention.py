@@ -274,3 +274,36 @@ def test_recurrence_keeps_the_running_maximum():
     np.testing.assert_allclose(o / l, ref[0, 0], rtol=1e-12, atol=1e-13)
     split = attention.split_k_decode_attention(q, kp, vp, tables, [L], B, B)
     np.testing.assert_allclose(split, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_log_normaliser_matches_scipy_and_recombines():
+    # scipy's logsumexp is an independent routine; and the normalised halves
+    # of a split history, weighted by e^lse, give the whole result.
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(41)
+    B, D, Hq, Hkv = 4, 8, 4, 2
+    lens = [1, 7, 13]
+    k_h = [rng.standard_normal((L, Hkv, D)) * 3 for L in lens]
+    v_h = [rng.standard_normal((L, Hkv, D)) for L in lens]
+    q = rng.standard_normal((3, Hq, D))
+    kp, tables = build_paged(k_h, B, 12, np.random.default_rng(2))
+    vp, _ = build_paged(v_h, B, 12, np.random.default_rng(2))
+    lse = attention.decode_log_normaliser(q, kp, tables, lens, B)
+    scale = 1 / math.sqrt(D)
+    for s, L in enumerate(lens):
+        for h in range(Hq):
+            z = scale * k_h[s][:, h // 2, :] @ q[s, h]
+            assert abs(lse[s, h] - logsumexp(z)) < 1e-12
+    # Split sequence 2 (13 tokens) at 8 = two blocks: prefix and suffix.
+    s, cut = 2, 8
+    pre = attention.decode_attention(q[s:s + 1], kp, vp, tables[s:s + 1], [cut], B)
+    lp = attention.decode_log_normaliser(q[s:s + 1], kp, tables[s:s + 1], [cut], B)
+    suf_tab = np.concatenate([tables[s:s + 1, cut // B:], np.full((1, cut // B), -1)], axis=1)
+    suf = attention.decode_attention(q[s:s + 1], kp, vp, suf_tab, [13 - cut], B)
+    ls = attention.decode_log_normaliser(q[s:s + 1], kp, suf_tab, [13 - cut], B)
+    m = np.maximum(lp, ls)[..., None]
+    wa, wb = np.exp(lp[..., None] - m), np.exp(ls[..., None] - m)
+    comb = (wa * pre + wb * suf) / (wa + wb)
+    full = attention.decode_attention(q[s:s + 1], kp, vp, tables[s:s + 1], [13], B)
+    np.testing.assert_allclose(comb, full, rtol=1e-12, atol=1e-13)
+    assert np.isneginf(attention.decode_log_normaliser(q[:1], kp, tables[:1], [0], B)).all()
