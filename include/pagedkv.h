@@ -277,6 +277,56 @@ int paged_decode_step(int kernel, void* out, const void* q, void* k_pool, void* 
                       int head_dim, float scale, int partition_tokens, void* workspace,
                       size_t workspace_bytes, int dtype, void* stream);
 
+/* paged_decode_attention_lse - paged_decode_attention_with that also writes
+ * the natural log of each head's softmax normaliser:
+ *   lse : device float [num_seqs, num_q_heads],
+ *         lse[s, h] = ln sum_{t < L_s} exp(scale * q[s, h] . K[t, kvh(h)]);
+ * -inf for L_s <= 0, NaN where the output row is NaN.  Accurate to about
+ * 2e-3 absolute on 16-bit pools (the normaliser sums probabilities rounded
+ * to the element type, as the output's weights do).  Two normalised
+ * results over disjoint key sets combine exactly with these weights (the
+ * block-combining operator of [arch] "3. Non-Contiguous Online Softmax
+ * Attention Kernel" applied to normalised parts). */
+int paged_decode_attention_lse(int kernel, float* lse, void* out, const void* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int num_seqs, int num_blocks,
+                               int block_size, int num_q_heads, int num_kv_heads, int head_dim,
+                               float scale, int partition_tokens, void* workspace,
+                               size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * paged_decode_attention_cascade - decode attention that reads each shared
+ * prefix once per group of sequences ([lesson] "Sharing, and the reference
+ * counting it needs": sequences with a common prompt prefix share its
+ * blocks; [pofe] "Sharing and copy-on-write").  Group z has the members
+ * group_members[group_offsets[z] .. group_offsets[z+1]) (device int32), which
+ * share their first group_prefix_blocks[z] table entries (the caller's
+ * contract; a sequence belongs to at most one group; max_group_size bounds
+ * the member counts and only sizes the launch).  Result: the same attention
+ * as paged_decode_attention_with, computed as
+ *   - the group's queries against the prefix blocks, read once (matrix
+ *     cores, states in float);
+ *   - paged_decode_attention_lse over each sequence's remaining blocks;
+ *   - per member, O = (e^(a-M) O_prefix + e^(b-M) O_rest) / (e^(a-M) + e^(b-M)),
+ *     a, b the log normalisers, M = max(a, b).
+ * Sequences outside every group get plain decode attention.  A member
+ * shorter than its group's prefix, or a prefix longer than the table row,
+ * gets NaN rows.  F16 / BF16 pools, head_dim % 32 == 0.  Workspace:
+ * paged_decode_cascade_workspace_bytes (256-byte aligned). */
+size_t paged_decode_cascade_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
+                                            int max_blocks_per_seq, int block_size);
+int paged_decode_attention_cascade(int kernel, void* out, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_tables,
+                                   int max_blocks_per_seq, const int32_t* context_lens,
+                                   int num_seqs, const int32_t* group_offsets,
+                                   const int32_t* group_members,
+                                   const int32_t* group_prefix_blocks, int num_groups,
+                                   int max_group_size, int num_blocks, int block_size,
+                                   int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                                   void* workspace, size_t workspace_bytes, int dtype,
+                                   void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* FP8 cache blocks                                                           */
 /* ------------------------------------------------------------------------- */

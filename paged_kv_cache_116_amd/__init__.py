@@ -79,6 +79,11 @@ _sig("paged_kv_append_tokens", _i32,
      [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("paged_prefill_attention", _i32,
      [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p])
+_sig("paged_decode_attention_lse", _i32, [_i32, _p] + _ATTN_ARGS)
+_sig("paged_decode_cascade_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32])
+_sig("paged_decode_attention_cascade", _i32,
+     [_i32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+      _i32, _f32, _p, _sz, _i32, _p])
 _sig("paged_kv_swap_out", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("paged_kv_swap_in", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("pkv_bm_seq_swap_out", _i32, [_p, _i32, _p, _i32, _intp])
@@ -357,6 +362,60 @@ def paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_lens, *
         _check(_lib.paged_decode_attention(*args), "paged_decode_attention")
     else:
         _check(_lib.paged_decode_attention_with(int(kernel), *args), "paged_decode_attention_with")
+
+
+def paged_decode_attention_lse(out, lse, q, k_pool, v_pool, block_tables, context_lens, *,
+                               scale=None, partition_tokens=0, workspace=None, stream=None,
+                               kernel=PKV_ATTN_AUTO):
+    """Decode attention plus lse [num_seqs, H_q] (float32): the natural log of each
+    head's softmax normaliser."""
+    args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                      partition_tokens, workspace, stream)
+    if lse.shape != q.shape[:2]:
+        raise ValueError("lse must be [num_seqs, num_q_heads]")
+    _check(_lib.paged_decode_attention_lse(int(kernel), _dev(lse, "lse", torch.float32), *args),
+           "paged_decode_attention_lse")
+
+
+def paged_decode_cascade_workspace_bytes(num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                                         block_size) -> int:
+    return int(_lib.paged_decode_cascade_workspace_bytes(num_seqs, num_q_heads, head_dim,
+                                                         max_blocks_per_seq, block_size))
+
+
+def paged_decode_attention_cascade(out, q, k_pool, v_pool, block_tables, context_lens,
+                                   group_offsets, group_members, group_prefix_blocks, *,
+                                   max_group_size=None, scale=None, workspace=None, stream=None,
+                                   kernel=PKV_ATTN_AUTO):
+    """Decode attention reading each group's shared prefix blocks once (see the C
+    header).  group_offsets [G + 1], group_members [M], group_prefix_blocks [G]:
+    int32 GPU tensors."""
+    n, b, h, d, dt = _pool_dims(k_pool, v_pool)
+    s, hq, dq = q.shape
+    if dq != d or out.shape != q.shape or q.dtype != k_pool.dtype or out.dtype != q.dtype:
+        raise ValueError("q / out must be [num_seqs, num_q_heads, head_dim] in the pool dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
+        raise ValueError("block_tables [num_seqs, max_blocks] and context_lens [num_seqs]")
+    g = group_prefix_blocks.shape[0]
+    if group_offsets.shape != (g + 1,) or group_members.dim() != 1:
+        raise ValueError("group_offsets [G + 1], group_members [M], group_prefix_blocks [G]")
+    mb = block_tables.shape[1]
+    if max_group_size is None:
+        max_group_size = group_members.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        need = paged_decode_cascade_workspace_bytes(s, hq, d, mb, b)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.paged_decode_attention_cascade(
+        int(kernel), _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32), mb,
+        _dev(context_lens, "context_lens", torch.int32), s,
+        _dev(group_offsets, "group_offsets", torch.int32),
+        _dev(group_members, "group_members", torch.int32),
+        _dev(group_prefix_blocks, "group_prefix_blocks", torch.int32), g, int(max_group_size),
+        n, b, hq, h, d, float(scale), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        dt, _stream(stream)), "paged_decode_attention_cascade")
 
 
 def paged_decode_attention_with(kernel, out, q, k_pool, v_pool, block_tables, context_lens, **kw):

@@ -154,6 +154,7 @@ struct AttnParams {
   int kv_fp8;        // pools hold E4M3FN codes
   float k_scale;     // FP8 pools: value = code * scale (the decode-step append divides)
   float v_scale;     // multiplies the weighted V sum (1 unless FP8)
+  float* lse;        // optional [S, Hq]: natural log of each head's softmax normaliser
 };
 
 // A sequence is live when 0 < L <= max_blocks * B; it then has ceil(L/16) tiles.
@@ -265,6 +266,11 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
       const float fill = p.lens[sd] <= 0 ? 0.f : __builtin_nanf("");
       S* row = (S*)p.out + (size_t)sd * row_elems;
       for (size_t i = tid; i < row_elems; i += kPlanThreads) Cvt<T>::store(row + i, fill);
+      if (p.lse) {   // nothing to attend: log 0; an over-long length: NaN
+        const float lfill = p.lens[sd] <= 0 ? -INFINITY : __builtin_nanf("");
+        for (int h = tid; h < p.num_q_heads; h += kPlanThreads)
+          p.lse[(size_t)sd * p.num_q_heads + h] = lfill;
+      }
     }
     lds_barrier();
     if (tid == kPlanThreads - 1) carry_lds = excl + nt;
@@ -406,6 +412,12 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
   }
 }
 
+// Natural log of a softmax normaliser kept as (m, l) in log2 units:
+// ln(l * 2^m) = (m + log2 l) * ln 2.
+__device__ __forceinline__ float lse_of(float m, float l) {
+  return (m + log2f(l)) * 0.69314718055994531f;
+}
+
 // ---------------------------------------------------------------------------
 // Claim walk shared by both partition kernels.
 // ---------------------------------------------------------------------------
@@ -522,6 +534,8 @@ __device__ __forceinline__ void emit_item(const AttnParams& p, const Segment& sg
     Cvt<T>::store(o + 1, bad ? nan : num.y * inv);
     Cvt<T>::store(o + 2, bad ? nan : num.z * inv);
     Cvt<T>::store(o + 3, bad ? nan : num.w * inv);
+    if (p.lse && d == 0)
+      p.lse[(size_t)sg.s * p.num_q_heads + kv.h0 + h] = bad ? nan : lse_of(big_m, den);
   } else {
     const size_t slot = ((size_t)sg.pair * p.kw + kw) * G + h;
     *reinterpret_cast<float4*>(p.ws_acc + slot * D + d) =
@@ -1143,6 +1157,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
       const float inv = 1.f / dsum;
       store4<T>(p, s, kv.h0 + h, f - h * D,
                 make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv));
+      if (p.lse && f == h * D) p.lse[(size_t)s * p.num_q_heads + kv.h0 + h] = lse_of(big, dsum);
     }
     lds_barrier();   // the LDS buffers are reused by the next task
   }
@@ -1169,11 +1184,15 @@ __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
     for (int j = 0; j < kF4; ++j) {
       const int f = 4 * lane + 256 * j;
       const int h = min(f / D, G - 1);
-      const float inv = 1.f / __shfl(den, h);
+      const float dh = __shfl(den, h);
+      const float mh = __shfl(st.run_m, h);
+      const float inv = 1.f / dh;
       if (f < kv.nh * D)
         store4<T>(p, s, kv.h0 + h, f - h * D,
                   make_float4(st.acc[j].x * inv, st.acc[j].y * inv, st.acc[j].z * inv,
                               st.acc[j].w * inv));
+      if (p.lse && f < kv.nh * D && f == h * D)
+        p.lse[(size_t)s * p.num_q_heads + kv.h0 + h] = lse_of(mh, dh);
     }
   }
 }
@@ -1439,6 +1458,119 @@ hipError_t launch_merge(const AttnParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Cascade decode over shared prefixes ([lesson] "Sharing, and the reference
+// counting it needs": sequences with a common prompt prefix share its
+// blocks).  Each group's shared prefix is read once for all its members
+// (attn_prefill_mfma in prefix mode), each sequence's private suffix by the
+// decode path above, and the two normalised results are combined with their
+// log normalisers:
+//     O = (e^(a - M) O_prefix + e^(b - M) O_suffix) / (e^(a - M) + e^(b - M)),
+// a, b the two natural log normalisers and M = max(a, b).
+// ---------------------------------------------------------------------------
+
+// Suffix tables start as copies of the tables (sequences outside every group
+// keep their whole history).
+__global__ __launch_bounds__(kThreads) void cascade_tables(const int32_t* __restrict__ tables,
+                                                           const int32_t* __restrict__ lens,
+                                                           int mb, int32_t* __restrict__ suf_tables,
+                                                           int32_t* __restrict__ suf_lens) {
+  const size_t row = (size_t)blockIdx.x * mb;
+  for (int j = threadIdx.x; j < mb; j += kThreads) suf_tables[row + j] = tables[row + j];
+  if (threadIdx.x == 0) suf_lens[blockIdx.x] = lens[blockIdx.x];
+}
+
+// Group z's members: the suffix table row starts past the prefix_blocks[z]
+// shared blocks and the length drops by their tokens.  A member shorter than
+// the prefix, or a prefix past the table, gets an over-long length, which
+// the decode path turns into NaN rows.
+__global__ __launch_bounds__(kThreads) void cascade_members(
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ lens, int mb, int log2_b,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ members,
+    const int32_t* __restrict__ prefix_blocks, int32_t* __restrict__ suf_tables,
+    int32_t* __restrict__ suf_lens) {
+  const int z = blockIdx.x;
+  const int pb = prefix_blocks[z];
+  const bool ok = pb >= 0 && pb <= mb;
+  for (int m = offsets[z]; m < offsets[z + 1]; ++m) {
+    const int s = members[m];
+    const size_t row = (size_t)s * mb;
+    for (int j = threadIdx.x; j < mb; j += kThreads)
+      suf_tables[row + j] = (ok && j + pb < mb) ? tables[row + j + pb] : -1;
+    if (threadIdx.x == 0) {
+      const long long pt = ok ? (long long)pb << log2_b : 0;
+      const int L = lens[s];
+      suf_lens[s] = (!ok || L < pt) ? (mb << log2_b) + 1 : L - (int)pt;
+    }
+  }
+}
+
+// out[s] = combination of the prefix state (o_pre, lse_pre) and the suffix
+// output already in out[s] (lse_suf), for every member s; 8 channels per
+// thread.  An empty side (log normaliser -inf) weighs 0; NaN propagates.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void cascade_combine(
+    void* __restrict__ out, const float* __restrict__ o_pre, const float* __restrict__ lse_pre,
+    const float* __restrict__ lse_suf, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ members, int num_q_heads, int head_dim) {
+  using S = typename T::storage;
+  const int z = blockIdx.x;
+  const int row = num_q_heads * head_dim;
+  for (int m = offsets[z]; m < offsets[z + 1]; ++m) {
+    const int s = members[m];
+    S* o = (S*)out + (size_t)s * row;
+    const float* pre = o_pre + (size_t)s * row;
+    for (int c = threadIdx.x; c < row / 8; c += kThreads) {
+      const int h = (8 * c) / head_dim;
+      const float a = lse_pre[(size_t)s * num_q_heads + h];
+      const float b = lse_suf[(size_t)s * num_q_heads + h];
+      float wa = 0.f, wb = 0.f;
+      const bool nan_in = a != a || b != b;
+      const float mx = fmaxf(a, b);
+      if (mx != -INFINITY) {
+        wa = a == -INFINITY ? 0.f : expf(a - mx);
+        wb = b == -INFINITY ? 0.f : expf(b - mx);
+      }
+      const float inv = (wa + wb) > 0.f ? 1.f / (wa + wb) : 0.f;
+      float suf[8];
+      Cvt<T>::unpack(load16(o + 8 * c), suf);
+      const float4 p0 = *reinterpret_cast<const float4*>(pre + 8 * c);
+      const float4 p1 = *reinterpret_cast<const float4*>(pre + 8 * c + 4);
+      const float pv[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        // A side with weight 0 adds nothing (not 0 * its value, which could be NaN).
+        float v = 0.f;
+        if (wa > 0.f) v += wa * pv[e];
+        if (wb > 0.f) v += wb * suf[e];
+        Cvt<T>::store(o + 8 * c + e, nan_in ? __builtin_nanf("") : v * inv);
+      }
+    }
+  }
+}
+
+// Workspace of the cascade: suffix tables and lengths, prefix states, the
+// two log-normaliser arrays, then the decode workspace.
+struct CascadeWs {
+  size_t tables, lens, o_pre, lse_pre, lse_suf, decode, total;
+};
+CascadeWs cascade_layout(int num_seqs, int num_q_heads, int head_dim, int max_blocks,
+                         int block_size) {
+  CascadeWs w;
+  const size_t S = (size_t)num_seqs;
+  w.tables = 0;
+  w.lens = w.tables + align256(S * max_blocks * 4);
+  w.o_pre = w.lens + align256(S * 4);
+  w.lse_pre = w.o_pre + align256(S * num_q_heads * head_dim * 4);
+  w.lse_suf = w.lse_pre + align256(S * num_q_heads * 4);
+  w.decode = w.lse_suf + align256(S * num_q_heads * 4);
+  w.total = w.decode + align256(paged_decode_workspace_bytes(
+                           num_seqs, num_q_heads, head_dim,
+                           (int)std::min<long long>((long long)max_blocks * block_size, 1 << 30),
+                           0));
+  return w;
+}
+
 int decode_attention_impl(int phase, int kernel, void* out, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* block_tables, int max_blocks_per_seq,
                           const int32_t* context_lens, int num_seqs, int num_blocks,
@@ -1446,7 +1578,8 @@ int decode_attention_impl(int phase, int kernel, void* out, const void* q, const
                           float scale, int partition_tokens, void* workspace,
                           size_t workspace_bytes, int dtype, void* stream,
                           const void* k_new = nullptr, const void* v_new = nullptr,
-                          bool kv_fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
+                          bool kv_fp8 = false, float k_scale = 1.f, float v_scale = 1.f,
+                          float* lse = nullptr) {
   Launch L;
   const int st = prepare(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                          context_lens, num_seqs, num_blocks, block_size, num_q_heads,
@@ -1454,6 +1587,7 @@ int decode_attention_impl(int phase, int kernel, void* out, const void* q, const
                          workspace_bytes, dtype, &L, kv_fp8, k_scale, v_scale);
   if (st != PKV_OK || num_seqs == 0) return st;
   L.p.k_new = (const char*)k_new;
+  L.p.lse = lse;
   L.p.v_new = (const char*)v_new;
   hipStream_t hs = (hipStream_t)stream;
   if (phase & kPhasePlan) {
@@ -1577,4 +1711,92 @@ extern "C" int paged_decode_step_fp8(int kernel, void* out, const void* q, void*
                                     block_size, num_q_heads, num_kv_heads, head_dim, scale,
                                     partition_tokens, workspace, workspace_bytes, dtype, stream,
                                     k_new, v_new, true, k_scale, v_scale);
+}
+
+extern "C" int paged_decode_attention_lse(int kernel, float* lse, PKV_ATTN_ARGS) {
+  if (num_seqs > 0 && !lse) return PKV_ERR_INVALID_ARG;
+  return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, PKV_ATTN_PASS, nullptr, nullptr,
+                                    false, 1.f, 1.f, lse);
+}
+
+extern "C" size_t paged_decode_cascade_workspace_bytes(int num_seqs, int num_q_heads,
+                                                       int head_dim, int max_blocks_per_seq,
+                                                       int block_size) {
+  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_blocks_per_seq < 1 ||
+      block_size < 1)
+    return 0;
+  return pkv::cascade_layout(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size)
+      .total;
+}
+
+extern "C" int paged_decode_attention_cascade(
+    int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+    int num_seqs, const int32_t* group_offsets, const int32_t* group_members,
+    const int32_t* group_prefix_blocks, int num_groups, int max_group_size, int num_blocks,
+    int block_size, int num_q_heads, int num_kv_heads, int head_dim, float scale,
+    void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  using namespace pkv;
+  if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
+  if (head_dim % 32 != 0 || !supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (num_groups < 0 || num_groups > 65535 || max_group_size < 0 || num_seqs < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_groups > 0 && (!group_offsets || !group_members || !group_prefix_blocks))
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PKV_OK;
+  if (max_blocks_per_seq < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || num_kv_heads > 65535)
+    return PKV_ERR_INVALID_ARG;
+  const CascadeWs w =
+      cascade_layout(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size);
+  if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0)
+    return PKV_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  int32_t* suf_tables = (int32_t*)(ws + w.tables);
+  int32_t* suf_lens = (int32_t*)(ws + w.lens);
+  float* o_pre = (float*)(ws + w.o_pre);
+  float* lse_pre = (float*)(ws + w.lse_pre);
+  float* lse_suf = (float*)(ws + w.lse_suf);
+  // Validate the decode call on the suffix tables before launching anything.
+  {
+    Launch L;
+    const int st = prepare(kernel, out, q, k_pool, v_pool, suf_tables, max_blocks_per_seq,
+                           suf_lens, num_seqs, num_blocks, block_size, num_q_heads, num_kv_heads,
+                           head_dim, scale, 0, ws + w.decode, workspace_bytes - w.decode, dtype,
+                           &L, false, 1.f, 1.f);
+    if (st != PKV_OK) return st;
+  }
+  hipStream_t hs = (hipStream_t)stream;
+  const int log2_b = log2_exact(block_size);
+  hipLaunchKernelGGL(cascade_tables, dim3(num_seqs), dim3(kThreads), 0, hs, block_tables,
+                     context_lens, max_blocks_per_seq, suf_tables, suf_lens);
+  if (num_groups > 0) {
+    hipLaunchKernelGGL(cascade_members, dim3(num_groups), dim3(kThreads), 0, hs, block_tables,
+                       context_lens, max_blocks_per_seq, log2_b, group_offsets, group_members,
+                       group_prefix_blocks, suf_tables, suf_lens);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+    const int st = launch_prefix_states(q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                                        num_blocks, block_size, num_q_heads, num_kv_heads,
+                                        head_dim, scale, group_offsets, group_members,
+                                        group_prefix_blocks, num_groups, max_group_size, o_pre,
+                                        lse_pre, dtype, stream);
+    if (st != PKV_OK) return st;
+  }
+  int st = decode_attention_impl(kPhaseAll, kernel, out, q, k_pool, v_pool, suf_tables,
+                                 max_blocks_per_seq, suf_lens, num_seqs, num_blocks, block_size,
+                                 num_q_heads, num_kv_heads, head_dim, scale, 0, ws + w.decode,
+                                 workspace_bytes - w.decode, dtype, stream, nullptr, nullptr,
+                                 false, 1.f, 1.f, lse_suf);
+  if (st != PKV_OK) return st;
+  if (num_groups > 0) {
+    if (dtype == PKV_F16)
+      hipLaunchKernelGGL(cascade_combine<F16>, dim3(num_groups), dim3(kThreads), 0, hs, out,
+                         o_pre, lse_pre, lse_suf, group_offsets, group_members, num_q_heads,
+                         head_dim);
+    else
+      hipLaunchKernelGGL(cascade_combine<BF16>, dim3(num_groups), dim3(kThreads), 0, hs, out,
+                         o_pre, lse_pre, lse_suf, group_offsets, group_members, num_q_heads,
+                         head_dim);
+  }
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

@@ -59,9 +59,22 @@ struct PrefillParams {
   int num_kv_heads;
   int group;          // g = Hq / Hkv
   float scale_log2;   // scale * log2(e)
+  // Shared-prefix states (the kPrefix kernel): group z has members
+  // members[offsets[z] .. offsets[z+1]) sharing their first prefix_blocks[z]
+  // table entries; each member's rows get the normalised output over those
+  // positions (o_states, float [S, Hq, D]) and its log normaliser (lse).
+  const int32_t* offsets;
+  const int32_t* members;
+  const int32_t* prefix_blocks;
+  float* o_states;
+  float* lse;
 };
 
-template <typename T, int D>
+// kPrefix = false: causal chunked prefill, blockIdx.z = sequence.
+// kPrefix = true: attention of every member's query over its group's shared
+// prefix (no mask; all prefix positions precede the query), blockIdx.z =
+// group; writes float states instead of the output.
+template <typename T, int D, bool kPrefix>
 __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParams p) {
   using S = typename T::storage;
   constexpr int LPR = D / 8;                  // 16-byte chunks per K/V row
@@ -83,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
     else return (r >> 2) & 3;
   };
 
-  const int s = blockIdx.z;
+  const int z = blockIdx.z;
   const int kvh = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -91,15 +104,32 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
   const int col = lane & 15;    // score tile: key row / query row column
   const int kgrp = lane >> 4;
   const int g = p.group;
-  const int cu0 = p.cu[s];
-  const int n = p.cu[s + 1] - cu0;
-  const int L = p.lens[s];
-  const int rows = n * g;
   const int max_len = p.max_blocks << p.log2_b;
-  // A chunk longer than its history, or a history past the table, has no
-  // defined result: its rows are NaN.
-  const bool invalid = n > L || L > max_len;
-  const int32_t* trow = p.tables + (size_t)s * p.max_blocks;
+  // Prefill: the chunk of sequence z is tokens cu0 .. cu0 + n - 1 of q, at
+  // positions L - n .. L - 1.  Prefix: the n members of group z, every row
+  // attending positions 0 .. L - 1 of the shared prefix (L = its tokens).
+  int cu0, n, L;
+  bool invalid;
+  const int32_t* trow;
+  if constexpr (kPrefix) {
+    cu0 = p.offsets[z];
+    n = p.offsets[z + 1] - cu0;
+    L = p.prefix_blocks[z] << p.log2_b;
+    // A prefix past the table row has no defined result: NaN rows.
+    invalid = p.prefix_blocks[z] < 0 || p.prefix_blocks[z] > p.max_blocks;
+    trow = p.tables + (size_t)(n > 0 ? p.members[cu0] : 0) * p.max_blocks;
+  } else {
+    cu0 = p.cu[z];
+    n = p.cu[z + 1] - cu0;
+    L = p.lens[z];
+    // A chunk longer than its history, or a history past the table, has no
+    // defined result: its rows are NaN.
+    invalid = n > L || L > max_len;
+    trow = p.tables + (size_t)z * p.max_blocks;
+  }
+  const int rows = n * g;
+  // Position of row i's query: keys 0 .. pos(i) are visible.
+  auto pos_of = [&](int i) { return kPrefix ? L - 1 : L - n + i; };
 
   for (int rb = blockIdx.x; rb * kRows < rows; rb += gridDim.x) {
     // This lane's row (column `col` of the wave's 16).
@@ -108,28 +138,39 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
     const int i = row_ok ? r / g : 0;
     const int hh = row_ok ? r - i * g : 0;
     const int h = kvh * g + hh;
-    const int pos = L - n + i;              // the row's position; keys 0 .. pos
-    S* orow = (S*)p.out + ((size_t)(cu0 + i) * p.num_q_heads + h) * D;
+    const int pos = pos_of(i);              // the row's position; keys 0 .. pos
+    // The row of q (and of the output): packed token cu0 + i, or member i's
+    // sequence.
+    const size_t qi = kPrefix ? (size_t)(row_ok ? p.members[cu0 + i] : 0) : (size_t)(cu0 + i);
+    S* orow = (S*)p.out + (qi * p.num_q_heads + h) * D;
+    float* srow = kPrefix ? p.o_states + (qi * p.num_q_heads + h) * D : nullptr;
 
-    if (invalid) {   // uniform across the workgroup
+    if (invalid || (kPrefix && L == 0)) {   // uniform across the workgroup
       if (row_ok) {
-        for (int d = kgrp; d < D; d += 4) Cvt<T>::store(orow + d, __builtin_nanf(""));
+        if constexpr (kPrefix) {   // NaN, or an empty prefix: sum 0, log 0
+          const float v = invalid ? __builtin_nanf("") : 0.f;
+          for (int d = kgrp; d < D; d += 4) srow[d] = v;
+          if (kgrp == 0)
+            p.lse[qi * p.num_q_heads + h] = invalid ? __builtin_nanf("") : -INFINITY;
+        } else {
+          for (int d = kgrp; d < D; d += 4) Cvt<T>::store(orow + d, __builtin_nanf(""));
+        }
       }
       continue;
     }
 
-    // Causal limits: the workgroup reads keys up to its last row's position,
+    // Key limits: the workgroup reads keys up to its last row's position,
     // each wave computes up to its own last row's.
     const int last_row = min(rb * kRows + kRows, rows) - 1;
-    const int tiles = (L - n + last_row / g) / kTile + 1;
+    const int tiles = pos_of(last_row / g) / kTile + 1;
     const int w_first = rb * kRows + w * 16;
     const int w_last = min(w_first + 16, rows) - 1;
-    const int w_tiles = w_first < rows ? (L - n + w_last / g) / kTile + 1 : 0;
+    const int w_tiles = w_first < rows ? pos_of(w_last / g) / kTile + 1 : 0;
 
     // B operand of the score product: row `col`, channels 32j + 8*kgrp .. +7.
     uint4 qop[KCH];
     {
-      const S* qrow = (const S*)p.q + ((size_t)(cu0 + i) * p.num_q_heads + h) * D + kgrp * 8;
+      const S* qrow = (const S*)p.q + (qi * p.num_q_heads + h) * D + kgrp * 8;
 #pragma unroll
       for (int j = 0; j < KCH; ++j)
         qop[j] = row_ok ? load16(qrow + 32 * j) : make_uint4(0, 0, 0, 0);
@@ -236,11 +277,23 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
     if (row_ok) {
       const float inv = 1.f / l_run;
       const float nan = __builtin_nanf("");
+      if constexpr (kPrefix) {
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) {
-        S* o = orow + 16 * j + 4 * kgrp;
+        for (int j = 0; j < D / 16; ++j)
+          *reinterpret_cast<float4*>(srow + 16 * j + 4 * kgrp) =
+              any_bad ? make_float4(nan, nan, nan, nan)
+                      : make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv,
+                                    acc[j][3] * inv);
+        if (kgrp == 0)   // ln(l * 2^m), m and l in log2 units
+          p.lse[qi * p.num_q_heads + h] =
+              any_bad ? nan : (m_run + log2f(l_run)) * 0.69314718055994531f;
+      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Cvt<T>::store(o + e, any_bad ? nan : acc[j][e] * inv);
+        for (int j = 0; j < D / 16; ++j) {
+          S* o = orow + 16 * j + 4 * kgrp;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Cvt<T>::store(o + e, any_bad ? nan : acc[j][e] * inv);
+        }
       }
     }
     // LDS buffers and bad_lds are reused by the next row block.
@@ -248,13 +301,21 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
   }
 }
 
-template <typename T>
+template <typename T, bool kPrefix>
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, dim3 grid, hipStream_t st) {
   switch (head_dim) {
-    case 32: hipLaunchKernelGGL((attn_prefill_mfma<T, 32>), grid, dim3(kThreads), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((attn_prefill_mfma<T, 64>), grid, dim3(kThreads), 0, st, p); break;
-    case 128: hipLaunchKernelGGL((attn_prefill_mfma<T, 128>), grid, dim3(kThreads), 0, st, p); break;
-    default: hipLaunchKernelGGL((attn_prefill_mfma<T, 256>), grid, dim3(kThreads), 0, st, p); break;
+    case 32:
+      hipLaunchKernelGGL((attn_prefill_mfma<T, 32, kPrefix>), grid, dim3(kThreads), 0, st, p);
+      break;
+    case 64:
+      hipLaunchKernelGGL((attn_prefill_mfma<T, 64, kPrefix>), grid, dim3(kThreads), 0, st, p);
+      break;
+    case 128:
+      hipLaunchKernelGGL((attn_prefill_mfma<T, 128, kPrefix>), grid, dim3(kThreads), 0, st, p);
+      break;
+    default:
+      hipLaunchKernelGGL((attn_prefill_mfma<T, 256, kPrefix>), grid, dim3(kThreads), 0, st, p);
+      break;
   }
   return hipGetLastError();
 }
@@ -282,7 +343,7 @@ extern "C" int paged_prefill_attention(void* out, const void* q, const void* k_p
   if (num_seqs == 0 || max_chunk_tokens == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !cu_seqlens || !block_tables || !context_lens)
     return PKV_ERR_INVALID_ARG;
-  PrefillParams p;
+  PrefillParams p{};
   p.out = out;
   p.q = q;
   p.k_pool = (const char*)k_pool;
@@ -301,7 +362,47 @@ extern "C" int paged_prefill_attention(void* out, const void* q, const void* k_p
   // further row blocks of their (KV head, sequence).
   const long long row_blocks = ((long long)max_chunk_tokens * p.group + kRows - 1) / kRows;
   const dim3 grid((unsigned)std::min<long long>(row_blocks, 65535), num_kv_heads, num_seqs);
-  const hipError_t e = dtype == PKV_F16 ? launch_prefill<F16>(p, head_dim, grid, (hipStream_t)stream)
-                                        : launch_prefill<BF16>(p, head_dim, grid, (hipStream_t)stream);
+  const hipError_t e =
+      dtype == PKV_F16 ? launch_prefill<F16, false>(p, head_dim, grid, (hipStream_t)stream)
+                       : launch_prefill<BF16, false>(p, head_dim, grid, (hipStream_t)stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
+
+namespace pkv {
+
+// Shared-prefix states for the cascade decode: for every member of every
+// group, the normalised attention output over the group's shared prefix
+// blocks (float [S, Hq, D]) and its natural log normaliser ([S, Hq]).
+int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
+                         const int32_t* tables, int max_blocks, int num_blocks, int block_size,
+                         int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                         const int32_t* offsets, const int32_t* members,
+                         const int32_t* prefix_blocks, int num_groups, int max_group_size,
+                         float* o_states, float* lse, int dtype, void* stream) {
+  PrefillParams p{};
+  p.q = q;
+  p.k_pool = (const char*)k_pool;
+  p.v_pool = (const char*)v_pool;
+  p.tables = tables;
+  p.max_blocks = max_blocks;
+  p.num_blocks = num_blocks;
+  p.log2_b = log2_exact(block_size);
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = num_q_heads / num_kv_heads;
+  p.scale_log2 = scale * kLog2e;
+  p.offsets = offsets;
+  p.members = members;
+  p.prefix_blocks = prefix_blocks;
+  p.o_states = o_states;
+  p.lse = lse;
+  const long long row_blocks = ((long long)max_group_size * p.group + kRows - 1) / kRows;
+  const dim3 grid((unsigned)std::max<long long>(1, std::min<long long>(row_blocks, 65535)),
+                  num_kv_heads, num_groups);
+  const hipError_t e =
+      dtype == PKV_F16 ? launch_prefill<F16, true>(p, head_dim, grid, (hipStream_t)stream)
+                       : launch_prefill<BF16, true>(p, head_dim, grid, (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace pkv
