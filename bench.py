@@ -55,7 +55,8 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", choices=["decode", "prefill", "swap"], default="decode",
+    ap.add_argument("--workload", choices=["decode", "prefill", "swap", "cascade"],
+                    default="decode",
                     help="decode: the paged decode step on --config (default); prefill: "
                          "multi-token append + causal chunked-prefill attention on a batch of "
                          "16 whole prompts (32 q / 8 kv heads of 128, bf16, B 16); swap: "
@@ -126,6 +127,8 @@ def main(argv=None) -> int:
         return run_prefill(args, torch, pkv, workloads, dev)
     if args.workload == "swap":
         return run_swap(args, torch, pkv, workloads, dev)
+    if args.workload == "cascade":
+        return run_cascade(args, torch, pkv, workloads, dev)
 
     calib = None
     if args.calibrate:
@@ -628,6 +631,145 @@ def run_swap(args, torch, pkv, workloads, dev) -> int:
     }
     print(json.dumps(result), flush=True)
     return 0 if ok else 1
+
+
+def run_cascade(args, torch, pkv, workloads, dev) -> int:
+    """The shared-prefix config (config 4: 128 sequences over one 64-block,
+    1024-token prefix): a step is the append plus paged_decode_attention_cascade
+    with the whole batch as one group, next to the same step through plain
+    decode attention (cache-retaining loads).  `value` is logical KV bytes per
+    second (every sequence's whole history, as for decode); the roofline
+    prices the distinct bytes the cascade has to read (the prefix once, every
+    private suffix once, q, out) over the cascade call."""
+    if args.config != 4:
+        print("--workload cascade runs on the shared-prefix config (--config 4)", file=sys.stderr)
+        return 2
+    t0 = time.time()
+    w = workloads.make_workload(4, device=dev)
+    torch.cuda.synchronize()
+    S, Hq, Hkv, D, B = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    npre = len(w.shared_blocks)
+    print(f"# workload {w.name}: {S} seqs, prefix {npre} blocks, tokens={int(w.lens.sum())}, "
+          f"drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    rng = np.random.default_rng(7)
+    check_seqs = sorted(rng.choice(S, size=4, replace=False).tolist())
+    check_inputs = None if args.no_check else workloads.extract_sequences(w, check_seqs)
+
+    esize, qsize = w.k_pool.element_size(), w.q.element_size()
+    lens64 = w.lens.astype(np.int64)
+    row = Hkv * D * 2 * esize                       # K and V bytes of one token
+    kv_logical = int(lens64.sum()) * row
+    kv_distinct = (npre * B + int((lens64 - npre * B).sum())) * row
+    alg_distinct = kv_distinct + 2 * S * Hq * D * qsize
+
+    tables = torch.as_tensor(w.tables, device=dev)
+    lens = torch.as_tensor(w.lens, device=dev)
+    lens_pre = torch.as_tensor(w.lens_pre, device=dev)
+    offsets = torch.as_tensor(np.array([0, S], np.int32), device=dev)
+    members = torch.arange(S, dtype=torch.int32, device=dev)
+    prefix = torch.as_tensor(np.array([npre], np.int32), device=dev)
+    out_c = torch.empty_like(w.q)
+    out_d = torch.empty_like(w.q)
+    ws_c = torch.empty(max(1, pkv.paged_decode_cascade_workspace_bytes(
+        S, Hq, D, w.max_blocks, B)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(1, pkv.paged_decode_workspace_bytes(S, Hq, D, w.max_blocks * B, 0)),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def append():
+        pkv.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, tables, lens_pre,
+                            stream=stream)
+
+    def cascade():
+        pkv.paged_decode_attention_cascade(out_c, w.q, w.k_pool, w.v_pool, tables, lens,
+                                           offsets, members, prefix, max_group_size=S,
+                                           scale=w.scale, workspace=ws_c, stream=stream)
+
+    def decode():
+        pkv.paged_decode_attention_with(pkv.PKV_ATTN_AUTO | pkv.PKV_ATTN_CACHE_KV, out_d, w.q,
+                                        w.k_pool, w.v_pool, tables, lens, scale=w.scale,
+                                        workspace=ws_d, stream=stream)
+
+    # The append writes the same bytes every time, so repeated steps are
+    # idempotent.
+    for _ in range(args.warmup):
+        append()
+        cascade()
+        decode()
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fns):
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps):
+            for f in fns:
+                f()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms_step = timed([append, cascade])
+    ms_casc = timed([cascade])
+    ms_dec_step = timed([append, decode])
+    ms_dec = timed([decode])
+    print(f"# cascade step {ms_step * 1e3:.1f} us (attention {ms_casc * 1e3:.1f}); plain decode "
+          f"step {ms_dec_step * 1e3:.1f} us (attention {ms_dec * 1e3:.1f})", file=sys.stderr,
+          flush=True)
+
+    parity = None
+    if check_inputs is not None:
+        from oracle import attention as o_attn
+        from oracle import cache_ops as o_cache
+        c = check_inputs
+        kp, vp = o_cache.append_token(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
+                                      c["tables"], c["lens_pre"], B)
+        ref = o_attn.decode_attention(c["q"], kp, vp, c["tables"], c["lens"], B, w.scale)
+        idx = torch.as_tensor(check_seqs, device=dev)
+        err_c = np.abs(out_c[idx].double().cpu().numpy() - ref)
+        err_d = np.abs(out_d[idx].double().cpu().numpy() - ref)
+        ok = bool((err_c <= 2e-2 + 1e-2 * np.abs(ref)).all() and
+                  (err_d <= 2e-2 + 1e-2 * np.abs(ref)).all())
+        parity = {"sampled_seqs": check_seqs, "max_abs_err": float(err_c.max()),
+                  "max_abs_err_plain": float(err_d.max()), "ok": ok}
+        print(f"# parity on {check_seqs}: cascade {err_c.max():.3e}, plain {err_d.max():.3e}, "
+              f"ok={ok}", file=sys.stderr, flush=True)
+
+    achieved = alg_distinct / (ms_casc * 1e-3) / 1e9
+    result = {
+        "metric": "shared-prefix decode attention, logical KV GB/s + seq-layer steps/s",
+        "value": round(kv_logical / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "cascade decode over " + WORKLOAD_DESC[4], "name": w.name,
+                   "batch": S, "prefix_blocks": npre, "block_size": B, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "tokens": int(lens64.sum())},
+        "seq_layer_steps_per_s": round(S / (ms_step * 1e-3), 1),
+        "kv_bytes_logical": kv_logical,
+        "kv_bytes_distinct": kv_distinct,
+        "us": {"step": round(ms_step * 1e3, 2), "cascade": round(ms_casc * 1e3, 2),
+               "plain_decode_step": round(ms_dec_step * 1e3, 2),
+               "plain_decode_attention": round(ms_dec * 1e3, 2)},
+        "speedup_over_plain_decode": round(ms_dec_step / ms_step, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
+                     "kernel": "cascade call (prefix + suffix decode + combine launches)",
+                     "algorithmic_bytes_per_launch": alg_distinct},
+        "parity": parity,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
+    return 0 if (parity is None or parity["ok"]) else 1
 
 
 if __name__ == "__main__":

@@ -306,10 +306,11 @@ int paged_decode_attention_lse(int kernel, float* lse, void* out, const void* q,
  * the member counts and only sizes the launch).  Result: the same attention
  * as paged_decode_attention_with, computed as
  *   - the group's queries against the prefix blocks, read once (matrix
- *     cores, states in float);
+ *     cores, states in float), the prefix split into up to 8 key ranges
+ *     (one per 128 table tokens at most) so that the launch fills the GPU;
  *   - paged_decode_attention_lse over each sequence's remaining blocks;
- *   - per member, O = (e^(a-M) O_prefix + e^(b-M) O_rest) / (e^(a-M) + e^(b-M)),
- *     a, b the log normalisers, M = max(a, b).
+ *   - per member, O = sum_r e^(a_r - M) O_r / sum_r e^(a_r - M) over the
+ *     prefix ranges and the rest, a_r their log normalisers, M = max a_r.
  * Sequences outside every group get plain decode attention.  A member
  * shorter than its group's prefix, or a prefix longer than the table row,
  * gets NaN rows.  F16 / BF16 pools, head_dim % 32 == 0.  Workspace:

@@ -35,10 +35,11 @@ inline int check_pool_shape(int num_blocks, int block_size, int num_kv_heads, in
 
 // Defined in prefill_attention.hip; used by the cascade decode.
 int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
-                         const int32_t* tables, int max_blocks, int num_blocks, int block_size,
-                         int num_q_heads, int num_kv_heads, int head_dim, float scale,
-                         const int32_t* offsets, const int32_t* members,
-                         const int32_t* prefix_blocks, int num_groups, int max_group_size,
-                         float* o_states, float* lse, int dtype, void* stream);
+                         const int32_t* tables, const int32_t* lens, int max_blocks,
+                         int num_seqs, int num_blocks, int block_size, int num_q_heads,
+                         int num_kv_heads, int head_dim, float scale, const int32_t* offsets,
+                         const int32_t* members, const int32_t* prefix_blocks, int num_groups,
+                         int max_group_size, int splits, float* o_states, float* lse,
+                         int32_t* suf_tables, int32_t* suf_lens, int dtype, void* stream);
 
 }  // namespace pkv

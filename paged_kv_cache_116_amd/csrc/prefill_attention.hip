@@ -28,6 +28,13 @@
 //                                       transposing LDS reads)
 // Workgroups loop over further row blocks with stride gridDim.x, so any grid
 // width covers every chunk.
+//
+// Shared-prefix mode (for the cascade decode): the rows are (member, query
+// head) pairs of a group whose members share their first blocks; every row
+// sees the whole prefix, so nothing is masked.  The prefix's tiles are split
+// into `splits` contiguous key ranges, one per workgroup, each producing a
+// normalised state and its log normaliser; the cascade's combine step merges
+// them with the suffix result by the log-sum-exp rule.
 #include <math.h>
 
 #include "pkv_common.h"
@@ -61,19 +68,27 @@ struct PrefillParams {
   float scale_log2;   // scale * log2(e)
   // Shared-prefix states (the kPrefix kernel): group z has members
   // members[offsets[z] .. offsets[z+1]) sharing their first prefix_blocks[z]
-  // table entries; each member's rows get the normalised output over those
-  // positions (o_states, float [S, Hq, D]) and its log normaliser (lse).
+  // table entries; key range r of the prefix gives each member's rows the
+  // normalised output over those positions (o_states + r * S * Hq * D, float
+  // [S, Hq, D]) and its log normaliser (lse + r * S * Hq, [S, Hq]).  The
+  // workgroups of range 0 and KV head 0 also write each member's suffix
+  // table row (its entries past the prefix, then -1) and suffix length.
   const int32_t* offsets;
   const int32_t* members;
   const int32_t* prefix_blocks;
   float* o_states;
   float* lse;
+  int splits;          // key ranges per prefix (1 for prefill)
+  int num_seqs;
+  int32_t* suf_tables;
+  int32_t* suf_lens;
 };
 
 // kPrefix = false: causal chunked prefill, blockIdx.z = sequence.
 // kPrefix = true: attention of every member's query over its group's shared
 // prefix (no mask; all prefix positions precede the query), blockIdx.z =
-// group; writes float states instead of the output.
+// group, blockIdx.x = row block * splits + key range; writes float states
+// instead of the output.
 template <typename T, int D, bool kPrefix>
 __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParams p) {
   using S = typename T::storage;
@@ -97,6 +112,10 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
   };
 
   const int z = blockIdx.z;
+  // Prefix mode: key range `split` of the prefix's tiles.
+  const int split = kPrefix ? (int)(blockIdx.x % p.splits) : 0;
+  const int rb_first = kPrefix ? (int)(blockIdx.x / p.splits) : (int)blockIdx.x;
+  const int rb_stride = kPrefix ? (int)(gridDim.x / p.splits) : (int)gridDim.x;
   const int kvh = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -131,7 +150,29 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
   // Position of row i's query: keys 0 .. pos(i) are visible.
   auto pos_of = [&](int i) { return kPrefix ? L - 1 : L - n + i; };
 
-  for (int rb = blockIdx.x; rb * kRows < rows; rb += gridDim.x) {
+  for (int rb = rb_first; rb * kRows < rows; rb += rb_stride) {
+    if constexpr (kPrefix) {
+      // Suffix tables of the members whose first row lies in this row block.
+      if (split == 0 && kvh == 0) {
+        const int pb = p.prefix_blocks[z];
+        const int i0 = (rb * kRows + g - 1) / g;
+        const int i1 = min(n, (rb * kRows + kRows + g - 1) / g);
+        for (int i = i0; i < i1; ++i) {
+          const int s = p.members[cu0 + i];
+          const size_t row = (size_t)s * p.max_blocks;
+          for (int j = tid; j < p.max_blocks; j += kThreads)
+            p.suf_tables[row + j] = (!invalid && j + pb < p.max_blocks) ? p.tables[row + j + pb]
+                                                                        : -1;
+          if (tid == 0) {
+            // A member shorter than the prefix, or a prefix past the table,
+            // gets an over-long length, which the decode path turns into NaN
+            // rows.
+            const int Ls = p.lens[s];
+            p.suf_lens[s] = (invalid || Ls < L) ? max_len + 1 : Ls - L;
+          }
+        }
+      }
+    }
     // This lane's row (column `col` of the wave's 16).
     const int r = rb * kRows + w * 16 + col;
     const bool row_ok = r < rows;
@@ -143,15 +184,20 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
     // sequence.
     const size_t qi = kPrefix ? (size_t)(row_ok ? p.members[cu0 + i] : 0) : (size_t)(cu0 + i);
     S* orow = (S*)p.out + (qi * p.num_q_heads + h) * D;
-    float* srow = kPrefix ? p.o_states + (qi * p.num_q_heads + h) * D : nullptr;
+    const size_t state = (size_t)split * p.num_seqs * p.num_q_heads + qi * p.num_q_heads + h;
+    float* srow = kPrefix ? p.o_states + state * D : nullptr;
+    // Prefix mode: this workgroup's key range, tiles kt_lo .. kt_hi - 1.
+    const int all_tiles = (L + kTile - 1) / kTile;
+    const int span = kPrefix ? (all_tiles + p.splits - 1) / p.splits : all_tiles;
+    const int kt_lo = kPrefix ? min(split * span, all_tiles) : 0;
+    const int kt_hi = kPrefix ? min(kt_lo + span, all_tiles) : 0;
 
-    if (invalid || (kPrefix && L == 0)) {   // uniform across the workgroup
+    if (invalid || (kPrefix && kt_lo == kt_hi)) {   // uniform across the workgroup
       if (row_ok) {
-        if constexpr (kPrefix) {   // NaN, or an empty prefix: sum 0, log 0
+        if constexpr (kPrefix) {   // NaN, or an empty key range: sum 0, log 0
           const float v = invalid ? __builtin_nanf("") : 0.f;
           for (int d = kgrp; d < D; d += 4) srow[d] = v;
-          if (kgrp == 0)
-            p.lse[qi * p.num_q_heads + h] = invalid ? __builtin_nanf("") : -INFINITY;
+          if (kgrp == 0) p.lse[state] = invalid ? __builtin_nanf("") : -INFINITY;
         } else {
           for (int d = kgrp; d < D; d += 4) Cvt<T>::store(orow + d, __builtin_nanf(""));
         }
@@ -162,10 +208,10 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
     // Key limits: the workgroup reads keys up to its last row's position,
     // each wave computes up to its own last row's.
     const int last_row = min(rb * kRows + kRows, rows) - 1;
-    const int tiles = pos_of(last_row / g) / kTile + 1;
+    const int tiles = kPrefix ? kt_hi : pos_of(last_row / g) / kTile + 1;
     const int w_first = rb * kRows + w * 16;
     const int w_last = min(w_first + 16, rows) - 1;
-    const int w_tiles = w_first < rows ? pos_of(w_last / g) / kTile + 1 : 0;
+    const int w_tiles = w_first >= rows ? 0 : kPrefix ? kt_hi : pos_of(w_last / g) / kTile + 1;
 
     // B operand of the score product: row `col`, channels 32j + 8*kgrp .. +7.
     uint4 qop[KCH];
@@ -220,9 +266,9 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
     for (int j = 0; j < D / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     if (tid == 0) bad_lds = 0;
-    load_tile(0);
-    for (int kt = 0; kt < tiles; ++kt) {
-      const int buf = kt & 1;
+    load_tile(kt_lo);
+    for (int kt = kt_lo; kt < tiles; ++kt) {
+      const int buf = (kt - kt_lo) & 1;
       store_tile(buf);
       // Tile kt visible to every wave; also, every wave is done with buffer
       // buf ^ 1 (read in iteration kt - 1) before it is written next.
@@ -285,8 +331,7 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
                       : make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv,
                                     acc[j][3] * inv);
         if (kgrp == 0)   // ln(l * 2^m), m and l in log2 units
-          p.lse[qi * p.num_q_heads + h] =
-              any_bad ? nan : (m_run + log2f(l_run)) * 0.69314718055994531f;
+          p.lse[state] = any_bad ? nan : (m_run + log2f(l_run)) * 0.69314718055994531f;
       } else {
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
@@ -351,6 +396,7 @@ extern "C" int paged_prefill_attention(void* out, const void* q, const void* k_p
   p.tables = block_tables;
   p.lens = context_lens;
   p.cu = cu_seqlens;
+  p.splits = 1;
   p.max_blocks = max_blocks_per_seq;
   p.num_blocks = num_blocks;
   p.log2_b = log2_exact(block_size);
@@ -371,19 +417,23 @@ extern "C" int paged_prefill_attention(void* out, const void* q, const void* k_p
 namespace pkv {
 
 // Shared-prefix states for the cascade decode: for every member of every
-// group, the normalised attention output over the group's shared prefix
-// blocks (float [S, Hq, D]) and its natural log normaliser ([S, Hq]).
+// group and each of `splits` key ranges of the group's shared prefix, the
+// normalised attention output over that range (float [splits, S, Hq, D]) and
+// its natural log normaliser ([splits, S, Hq]); also the members' suffix
+// tables and lengths.
 int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
-                         const int32_t* tables, int max_blocks, int num_blocks, int block_size,
-                         int num_q_heads, int num_kv_heads, int head_dim, float scale,
-                         const int32_t* offsets, const int32_t* members,
-                         const int32_t* prefix_blocks, int num_groups, int max_group_size,
-                         float* o_states, float* lse, int dtype, void* stream) {
+                         const int32_t* tables, const int32_t* lens, int max_blocks,
+                         int num_seqs, int num_blocks, int block_size, int num_q_heads,
+                         int num_kv_heads, int head_dim, float scale, const int32_t* offsets,
+                         const int32_t* members, const int32_t* prefix_blocks, int num_groups,
+                         int max_group_size, int splits, float* o_states, float* lse,
+                         int32_t* suf_tables, int32_t* suf_lens, int dtype, void* stream) {
   PrefillParams p{};
   p.q = q;
   p.k_pool = (const char*)k_pool;
   p.v_pool = (const char*)v_pool;
   p.tables = tables;
+  p.lens = lens;
   p.max_blocks = max_blocks;
   p.num_blocks = num_blocks;
   p.log2_b = log2_exact(block_size);
@@ -391,14 +441,21 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.scale_log2 = scale * kLog2e;
+  p.splits = splits;
+  p.num_seqs = num_seqs;
+  p.suf_tables = suf_tables;
+  p.suf_lens = suf_lens;
   p.offsets = offsets;
   p.members = members;
   p.prefix_blocks = prefix_blocks;
   p.o_states = o_states;
   p.lse = lse;
+  if (splits < 1 || splits > 65535) return PKV_ERR_INVALID_ARG;
+  // blockIdx.x = row block * splits + key range; workgroups loop over any
+  // further row blocks.
   const long long row_blocks = ((long long)max_group_size * p.group + kRows - 1) / kRows;
-  const dim3 grid((unsigned)std::max<long long>(1, std::min<long long>(row_blocks, 65535)),
-                  num_kv_heads, num_groups);
+  const long long rbx = std::max<long long>(1, std::min<long long>(row_blocks, 65535 / splits));
+  const dim3 grid((unsigned)(rbx * splits), num_kv_heads, num_groups);
   const hipError_t e =
       dtype == PKV_F16 ? launch_prefill<F16, true>(p, head_dim, grid, (hipStream_t)stream)
                        : launch_prefill<BF16, true>(p, head_dim, grid, (hipStream_t)stream);

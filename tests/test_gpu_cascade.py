@@ -164,3 +164,48 @@ def test_cascade_full_size_config4_sampled():
                                   w.scale)
     check_close(out[torch.as_tensor([0, 17, 127], device="cuda")], ref, "cascade config 4")
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("hq,hkv,bs,batch,prefix_tokens", [
+    (12, 2, 16, 40, 400),     # g = 6: members straddle 64-row blocks; 4 row blocks
+    (32, 8, 8, 70, 200),      # block size 8, 25 prefix blocks, 5 row blocks
+    (32, 8, 32, 30, 512),     # block size 32
+    (16, 16, 4, 9, 36),       # block size 4: the prefix ends inside a 16-token tile
+])
+def test_cascade_key_ranges_and_row_blocks(hq, hkv, bs, batch, prefix_tokens):
+    """Prefix states split into several key ranges (some empty when the prefix
+    has fewer tiles than ranges), groups spanning several row blocks, and
+    block sizes other than 16."""
+    w = workloads.make_workload(4, batch=batch, len_range=(1, 150), prefix_tokens=prefix_tokens,
+                                block_size=bs, num_q_heads=hq, num_kv_heads=hkv, seed=77)
+    pb = prefix_tokens // bs
+    S = w.num_seqs
+    groups = [(list(range(0, S - 1)), pb), ([S - 1], max(pb // 3, 1))]
+    offsets = np.cumsum([0] + [len(m) for m, _ in groups])
+    members = np.concatenate([m for m, _ in groups])
+    kp, vp, ek, ev = appended(w)
+    q = w.q.cuda()
+    out = torch.empty_like(q)
+    pkv.paged_decode_attention_cascade(out, q, kp, vp, i32(w.tables), i32(w.lens), i32(offsets),
+                                       i32(members), i32([p for _, p in groups]),
+                                       max_group_size=S - 1, scale=w.scale)
+    torch.cuda.synchronize()
+    ref = o_attn.decode_attention(f64(w.q), ek, ev, w.tables, w.lens, w.block_size, w.scale)
+    check_close(out, ref, f"cascade hq={hq} hkv={hkv} B={bs}")
+
+
+def test_cascade_small_max_group_size_still_covers_every_member():
+    """max_group_size only sizes the launch: a value below the real group size
+    still gives every member its result (workgroups stride over members and
+    row blocks)."""
+    w, pb = shared_prefix_case(batch=24)
+    kp, vp, ek, ev = appended(w)
+    q = w.q.cuda()
+    out = torch.empty_like(q)
+    S = w.num_seqs
+    pkv.paged_decode_attention_cascade(out, q, kp, vp, i32(w.tables), i32(w.lens), i32([0, S]),
+                                       i32(np.arange(S)), i32([pb]), max_group_size=1,
+                                       scale=w.scale)
+    torch.cuda.synchronize()
+    ref = o_attn.decode_attention(f64(w.q), ek, ev, w.tables, w.lens, w.block_size, w.scale)
+    check_close(out, ref, "cascade, max_group_size 1")
