@@ -629,11 +629,10 @@ template <typename T>
 __device__ __forceinline__ uint4 expand8(const uint4& v) { return v; }
 template <typename T>
 __device__ __forceinline__ uint4 expand8(const uint2& c) {
-  float f[8];
-  e4m3_decode4(c.x, f);
-  e4m3_decode4(c.y, f + 4);
-  return make_uint4(Pair<T>::pack(f[0], f[1]), Pair<T>::pack(f[2], f[3]),
-                    Pair<T>::pack(f[4], f[5]), Pair<T>::pack(f[6], f[7]));
+  return make_uint4(Fp8Pair<T>::template decode<false>(c.x),
+                    Fp8Pair<T>::template decode<true>(c.x),
+                    Fp8Pair<T>::template decode<false>(c.y),
+                    Fp8Pair<T>::template decode<true>(c.y));
 }
 
 // ---------------------------------------------------------------------------

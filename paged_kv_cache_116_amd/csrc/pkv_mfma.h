@@ -1,6 +1,6 @@
 // pkv_mfma.h - device helpers shared by the attention kernels (gfx950):
 // LDS ordering, compile-time loops, matrix-core wrappers, the transposing LDS
-// read and 16-bit pair packing.
+// read, 16-bit pair packing and FP8 pair decoding.
 #pragma once
 
 #include <type_traits>
@@ -106,6 +106,23 @@ template <> struct Pair<F16> {
   }
   __device__ static __forceinline__ float lo(uint32_t w) { return f16_lo(w); }
   __device__ static __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
+};
+
+// Two E4M3FN codes (bytes 2*hi, 2*hi + 1 of w) decoded straight to a pair of
+// the element type: every E4M3FN value is exact in bf16 and f16, and a unit
+// scale leaves it unchanged.
+template <typename T> struct Fp8Pair;
+template <> struct Fp8Pair<BF16> {
+  template <bool kHi>
+  __device__ static __forceinline__ uint32_t decode(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+  }
+};
+template <> struct Fp8Pair<F16> {
+  template <bool kHi>
+  __device__ static __forceinline__ uint32_t decode(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, kHi));
+  }
 };
 
 }  // namespace pkv

@@ -170,3 +170,33 @@ def test_fp8_rejects_what_it_does_not_support():
         pkv.paged_decode_attention_fp8(*args, 0.0, 1.0)                    # scale must be > 0
     with pytest.raises(RuntimeError):
         pkv.paged_decode_attention_fp8(*args, 1.0, 1.0, kernel=pkv.PKV_ATTN_VALU)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+def test_fp8_every_finite_code_decodes_exactly(dtype):
+    """A sequence of length 1 attends to one token with weight exactly 1, so
+    its output is that token's V row times the V scale, and every E4M3FN
+    value times 0.125 is exact in bf16 and f16: the output must equal the
+    oracle's decode of each code bit for bit.  Two sequences carry the 254
+    finite codes (the two NaN codes are replaced by 0) across head_dim 128;
+    the rest of each block holds NaN codes, which must stay masked."""
+    S, Hq, Hkv, D, B = 2, 2, 1, 128, 16
+    all_codes = np.arange(256, dtype=np.uint8).reshape(S, D)
+    v_codes = np.where((all_codes & 0x7F) == 0x7F, 0, all_codes).astype(np.uint8)
+    rng = np.random.default_rng(5)
+    pool_k = np.full((S, B, Hkv, D), 0x7F, np.uint8)
+    pool_v = np.full((S, B, Hkv, D), 0x7F, np.uint8)
+    pool_k[:, 0, 0, :] = rng.integers(0, 0x7F, (S, D))            # finite positive codes
+    pool_v[:, 0, 0, :] = v_codes
+    tables = torch.tensor([[0], [1]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([1, 1], dtype=torch.int32, device="cuda")
+    q = torch.randn(S, Hq, D, generator=torch.Generator().manual_seed(3)).to(dtype).cuda()
+    out = torch.empty_like(q)
+    kp = torch.from_numpy(pool_k).cuda().view(torch.float8_e4m3fn)
+    vp = torch.from_numpy(pool_v).cuda().view(torch.float8_e4m3fn)
+    pkv.paged_decode_attention_fp8(out, q, kp, vp, tables, lens, 0.0625, 0.125)
+    torch.cuda.synchronize()
+    want = o_fp8.dequantise(v_codes, 0.125)                        # [S, D] float64
+    got = out.double().cpu().numpy()
+    for h in range(Hq):
+        assert np.array_equal(got[:, h, :], want), f"head {h}: decoded values differ"
