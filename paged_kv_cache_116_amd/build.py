@@ -24,7 +24,8 @@ BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 LIB_NAME = "libpagedkv.so"
 ARCH = "gfx950"
 
-HIP_SOURCES = ["kv_cache_ops.hip", "decode_attention.hip", "prefill_attention.hip"]
+HIP_SOURCES = ["kv_cache_ops.hip", "decode_attention.hip", "prefill_attention.hip",
+               "cascade.hip"]
 HOST_SOURCES = ["host_runtime.cpp"]
 
 HIPCC_FLAGS = [

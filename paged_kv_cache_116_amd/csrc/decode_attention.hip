@@ -1457,122 +1457,6 @@ hipError_t launch_merge(const AttnParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// Cascade decode over shared prefixes ([lesson] "Sharing, and the reference
-// counting it needs": sequences with a common prompt prefix share its
-// blocks).  Each group's shared prefix is read once for all its members
-// (attn_prefill_mfma in prefix mode, its tiles split into key ranges), each
-// sequence's private suffix by the decode path above, and the normalised
-// results are combined with their log normalisers:
-//     O = sum_r e^(a_r - M) O_r / sum_r e^(a_r - M),
-// over the prefix ranges and the suffix, a_r their natural log normalisers
-// and M = max_r a_r.
-// ---------------------------------------------------------------------------
-
-// Key ranges a prefix may be split into: at most one per 128 table tokens
-// and at most kMaxPrefixSplits (the workspace holds that many states).
-constexpr int kMaxPrefixSplits = 8;
-int prefix_split_cap(int max_blocks, int block_size) {
-  const long long tokens = (long long)max_blocks * block_size;
-  return (int)std::max<long long>(1, std::min<long long>(kMaxPrefixSplits, (tokens + 127) / 128));
-}
-
-// Suffix tables start as copies of the tables (sequences outside every group
-// keep their whole history); the prefix kernel then rewrites the members'.
-__global__ __launch_bounds__(kThreads) void cascade_tables(const int32_t* __restrict__ tables,
-                                                           const int32_t* __restrict__ lens,
-                                                           int mb, int32_t* __restrict__ suf_tables,
-                                                           int32_t* __restrict__ suf_lens) {
-  const size_t row = (size_t)blockIdx.x * mb;
-  for (int j = threadIdx.x; j < mb; j += kThreads) suf_tables[row + j] = tables[row + j];
-  if (threadIdx.x == 0) suf_lens[blockIdx.x] = lens[blockIdx.x];
-}
-
-// out[s] = combination of the prefix states of `splits` key ranges (o_pre,
-// lse_pre, range r at offset r * state_stride rows) and the suffix output
-// already in out[s] (lse_suf), for every member s; workgroup (z, y) takes
-// the members offsets[z] + y, + gridDim.y, ...; 8 channels per thread.  An
-// empty part (log normaliser -inf) weighs 0; NaN propagates.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void cascade_combine(
-    void* __restrict__ out, const float* __restrict__ o_pre, const float* __restrict__ lse_pre,
-    const float* __restrict__ lse_suf, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ members, int num_q_heads, int head_dim, int splits,
-    size_t state_stride) {
-  using S = typename T::storage;
-  const int z = blockIdx.x;
-  const int row = num_q_heads * head_dim;
-  for (int m = offsets[z] + (int)blockIdx.y; m < offsets[z + 1]; m += gridDim.y) {
-    const int s = members[m];
-    S* o = (S*)out + (size_t)s * row;
-    for (int c = threadIdx.x; c < row / 8; c += kThreads) {
-      const int h = (8 * c) / head_dim;
-      const size_t sh = (size_t)s * num_q_heads + h;
-      const float b = lse_suf[sh];
-      bool nan_in = b != b;
-      float mx = b;
-      for (int r = 0; r < splits; ++r) {
-        const float a = lse_pre[r * state_stride + sh];
-        nan_in |= a != a;
-        mx = fmaxf(mx, a);
-      }
-      float v[8], suf[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-      float den = 0.f;
-      if (mx != -INFINITY) {
-        // A part with weight 0 adds nothing (not 0 * its value, which could be NaN).
-        for (int r = 0; r < splits; ++r) {
-          const float a = lse_pre[r * state_stride + sh];
-          if (a == -INFINITY) continue;
-          const float wa = expf(a - mx);
-          const float* pre = o_pre + (r * state_stride + sh) * head_dim + (8 * c) % head_dim;
-          const float4 p0 = *reinterpret_cast<const float4*>(pre);
-          const float4 p1 = *reinterpret_cast<const float4*>(pre + 4);
-          v[0] += wa * p0.x; v[1] += wa * p0.y; v[2] += wa * p0.z; v[3] += wa * p0.w;
-          v[4] += wa * p1.x; v[5] += wa * p1.y; v[6] += wa * p1.z; v[7] += wa * p1.w;
-          den += wa;
-        }
-        if (b != -INFINITY) {
-          const float wb = expf(b - mx);
-          Cvt<T>::unpack(load16(o + 8 * c), suf);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] += wb * suf[e];
-          den += wb;
-        }
-      }
-      const float inv = den > 0.f ? 1.f / den : 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Cvt<T>::store(o + 8 * c + e, nan_in ? __builtin_nanf("") : v[e] * inv);
-    }
-  }
-}
-
-// Workspace of the cascade: suffix tables and lengths, prefix states of up
-// to prefix_split_cap key ranges, the two log-normaliser arrays, then the
-// decode workspace.
-struct CascadeWs {
-  size_t tables, lens, o_pre, lse_pre, lse_suf, decode, total;
-};
-CascadeWs cascade_layout(int num_seqs, int num_q_heads, int head_dim, int max_blocks,
-                         int block_size) {
-  CascadeWs w;
-  const size_t S = (size_t)num_seqs;
-  const size_t R = (size_t)prefix_split_cap(max_blocks, block_size);
-  w.tables = 0;
-  w.lens = w.tables + align256(S * max_blocks * 4);
-  w.o_pre = w.lens + align256(S * 4);
-  w.lse_pre = w.o_pre + align256(R * S * num_q_heads * head_dim * 4);
-  w.lse_suf = w.lse_pre + align256(R * S * num_q_heads * 4);
-  w.decode = w.lse_suf + align256(S * num_q_heads * 4);
-  w.total = w.decode + align256(paged_decode_workspace_bytes(
-                           num_seqs, num_q_heads, head_dim,
-                           (int)std::min<long long>((long long)max_blocks * block_size, 1 << 30),
-                           0));
-  return w;
-}
-
 int decode_attention_impl(int phase, int kernel, void* out, const void* q, const void* k_pool,
                           const void* v_pool, const int32_t* block_tables, int max_blocks_per_seq,
                           const int32_t* context_lens, int num_seqs, int num_blocks,
@@ -1611,6 +1495,35 @@ int decode_attention_impl(int phase, int kernel, void* out, const void* q, const
 }
 
 }  // namespace
+
+// For the cascade decode (cascade.hip): validate a decode call without
+// launching anything, and run one with log normalisers.
+int decode_attention_check(int kernel, void* out, const void* q, const void* k_pool,
+                           const void* v_pool, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                           int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
+                           int head_dim, float scale, void* workspace, size_t workspace_bytes,
+                           int dtype) {
+  Launch L;
+  return prepare(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
+                 num_seqs, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                 0, workspace, workspace_bytes, dtype, &L);
+}
+
+int decode_attention_with_lse(int kernel, void* out, float* lse, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* context_lens, int num_seqs, int num_blocks,
+                              int block_size, int num_q_heads, int num_kv_heads, int head_dim,
+                              float scale, void* workspace, size_t workspace_bytes, int dtype,
+                              void* stream) {
+  return decode_attention_impl(kPhaseAll, kernel, out, q, k_pool, v_pool, block_tables,
+                               max_blocks_per_seq, context_lens, num_seqs, num_blocks,
+                               block_size, num_q_heads, num_kv_heads, head_dim, scale, 0,
+                               workspace, workspace_bytes, dtype, stream, nullptr, nullptr, false,
+                               1.f, 1.f, lse);
+}
+
 }  // namespace pkv
 
 extern "C" size_t paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
@@ -1719,92 +1632,4 @@ extern "C" int paged_decode_attention_lse(int kernel, float* lse, PKV_ATTN_ARGS)
   if (num_seqs > 0 && !lse) return PKV_ERR_INVALID_ARG;
   return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, PKV_ATTN_PASS, nullptr, nullptr,
                                     false, 1.f, 1.f, lse);
-}
-
-extern "C" size_t paged_decode_cascade_workspace_bytes(int num_seqs, int num_q_heads,
-                                                       int head_dim, int max_blocks_per_seq,
-                                                       int block_size) {
-  if (num_seqs < 0 || num_q_heads < 1 || head_dim < 1 || max_blocks_per_seq < 1 ||
-      block_size < 1)
-    return 0;
-  return pkv::cascade_layout(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size)
-      .total;
-}
-
-extern "C" int paged_decode_attention_cascade(
-    int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
-    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
-    int num_seqs, const int32_t* group_offsets, const int32_t* group_members,
-    const int32_t* group_prefix_blocks, int num_groups, int max_group_size, int num_blocks,
-    int block_size, int num_q_heads, int num_kv_heads, int head_dim, float scale,
-    void* workspace, size_t workspace_bytes, int dtype, void* stream) {
-  using namespace pkv;
-  if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
-  if (head_dim % 32 != 0 || !supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
-  if (num_groups < 0 || num_groups > 65535 || max_group_size < 0 || num_seqs < 0)
-    return PKV_ERR_INVALID_ARG;
-  if (num_groups > 0 && (!group_offsets || !group_members || !group_prefix_blocks))
-    return PKV_ERR_INVALID_ARG;
-  if (num_seqs == 0) return PKV_OK;
-  if (max_blocks_per_seq < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
-      num_q_heads % num_kv_heads != 0 || num_kv_heads > 65535)
-    return PKV_ERR_INVALID_ARG;
-  const CascadeWs w =
-      cascade_layout(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size);
-  if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255) != 0)
-    return PKV_ERR_WORKSPACE;
-  char* ws = (char*)workspace;
-  int32_t* suf_tables = (int32_t*)(ws + w.tables);
-  int32_t* suf_lens = (int32_t*)(ws + w.lens);
-  float* o_pre = (float*)(ws + w.o_pre);
-  float* lse_pre = (float*)(ws + w.lse_pre);
-  float* lse_suf = (float*)(ws + w.lse_suf);
-  // Validate the decode call on the suffix tables before launching anything.
-  {
-    Launch L;
-    const int st = prepare(kernel, out, q, k_pool, v_pool, suf_tables, max_blocks_per_seq,
-                           suf_lens, num_seqs, num_blocks, block_size, num_q_heads, num_kv_heads,
-                           head_dim, scale, 0, ws + w.decode, workspace_bytes - w.decode, dtype,
-                           &L, false, 1.f, 1.f);
-    if (st != PKV_OK) return st;
-  }
-  hipStream_t hs = (hipStream_t)stream;
-  hipLaunchKernelGGL(cascade_tables, dim3(num_seqs), dim3(kThreads), 0, hs, block_tables,
-                     context_lens, max_blocks_per_seq, suf_tables, suf_lens);
-  // Key ranges per prefix: enough workgroups for about four per compute unit
-  // (64-row blocks x KV heads x groups x ranges), within the workspace's cap.
-  const long long base = std::max<long long>(
-      1, ((long long)max_group_size * (num_q_heads / num_kv_heads) + 63) / 64 * num_kv_heads *
-             num_groups);
-  const int splits = (int)std::max<long long>(
-      1, std::min<long long>(prefix_split_cap(max_blocks_per_seq, block_size),
-                             (1024 + base - 1) / base));
-  if (num_groups > 0) {
-    const int st = launch_prefix_states(
-        q, k_pool, v_pool, block_tables, context_lens, max_blocks_per_seq, num_seqs, num_blocks,
-        block_size, num_q_heads, num_kv_heads, head_dim, scale, group_offsets, group_members,
-        group_prefix_blocks, num_groups, max_group_size, splits, o_pre, lse_pre, suf_tables,
-        suf_lens, dtype, stream);
-    if (st != PKV_OK) return st;
-  }
-  int st = decode_attention_impl(kPhaseAll, kernel, out, q, k_pool, v_pool, suf_tables,
-                                 max_blocks_per_seq, suf_lens, num_seqs, num_blocks, block_size,
-                                 num_q_heads, num_kv_heads, head_dim, scale, 0, ws + w.decode,
-                                 workspace_bytes - w.decode, dtype, stream, nullptr, nullptr,
-                                 false, 1.f, 1.f, lse_suf);
-  if (st != PKV_OK) return st;
-  if (num_groups > 0) {
-    // Any grid height covers every member (workgroups stride over them).
-    const dim3 grid(num_groups, std::max(1, std::min(max_group_size, 65535)));
-    const size_t stride = (size_t)num_seqs * num_q_heads;
-    if (dtype == PKV_F16)
-      hipLaunchKernelGGL(cascade_combine<F16>, grid, dim3(kThreads), 0, hs, out, o_pre, lse_pre,
-                         lse_suf, group_offsets, group_members, num_q_heads, head_dim, splits,
-                         stride);
-    else
-      hipLaunchKernelGGL(cascade_combine<BF16>, grid, dim3(kThreads), 0, hs, out, o_pre, lse_pre,
-                         lse_suf, group_offsets, group_members, num_q_heads, head_dim, splits,
-                         stride);
-  }
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
