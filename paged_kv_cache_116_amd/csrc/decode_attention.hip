@@ -89,6 +89,8 @@ constexpr int kClaimsPerCu = 16;    // claim descriptors per compute unit
 constexpr int kMinClaimWaveTiles = 6;  // smallest claim: tiles per wave
 constexpr int kMaxStages = 16;      // claim-size stages (sizes halve stage to stage)
 constexpr int kMergeBlock = 8;      // partial states one merge item combines
+constexpr int kMergeWaves = 8;      // waves per merge workgroup
+constexpr int kMergeThreads = 64 * kMergeWaves;
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanLdsCum = 8192;   // prefix sums kept in LDS up to this many sequences
 
@@ -98,7 +100,8 @@ constexpr int kPlanLdsCum = 8192;   // prefix sums kept in LDS up to this many s
 // Header: totals, the claim counter and the stage table; stage k covers
 // claims [C_k, C_k+1) and tiles [X_k, X_k+1), every claim z_k tiles long but
 // the last of the final stage.  Entry ns (= number of stages) is a sentinel.
-constexpr int kPlanGroups = 16;     // workgroups of the plan launch
+constexpr int kPlanGroups = 16;     // workgroups of the plan launch that plan
+constexpr int kAppendGroups = 16;   // further workgroups that do the decode-step append
 constexpr int kHdrWords = 128;
 enum Hdr {
   kHdrTot = 0,      // tiles of one KV-head quad (sum over sequences)
@@ -166,6 +169,7 @@ __device__ __forceinline__ int live_tiles(int L, int max_len) {
 // Plan: kPlanGroups workgroups.  Each one prefix-sums the tile counts and
 // builds the claim schedule for itself (a few microseconds of LDS work), then
 // writes its share of the claim descriptors, merge tasks and empty-row fills.
+// A decode step adds kAppendGroups workgroups that write the new tokens.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
@@ -190,15 +194,17 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
 
   // Decode step: append token L-1 of every sequence with 0 < L <= max_len
   // (the cache append of [pofe] "How it works"), one 16-byte chunk per
-  // thread, spread over the plan workgroups.  The partition launch that
-  // follows on the stream reads it from the pool.
-  if (p.k_new) {
+  // thread, spread over kAppendGroups workgroups of their own, so that it
+  // runs beside the planning rather than ahead of it.  The partition launch
+  // that follows on the stream reads it from the pool.
+  if (b >= kPlanGroups) {
+    const int ab = b - kPlanGroups;
     // One 16-byte chunk of the new row (16 / sizeof(T) elements) per thread;
     // FP8 pools get its codes, encode(x / scale), as in paged_kv_append_fp8.
     constexpr int E = 16 / T::bytes;
     const int row_chunks = p.num_kv_heads * p.head_dim / E;
-    for (long long i = (long long)b * kPlanThreads + tid; i < (long long)S_ * row_chunks;
-         i += kPlanGroups * kPlanThreads) {
+    for (long long i = (long long)ab * kPlanThreads + tid; i < (long long)S_ * row_chunks;
+         i += kAppendGroups * kPlanThreads) {
       const int s = (int)(i / row_chunks);
       const int ch = (int)(i - (long long)s * row_chunks);
       const int L = p.lens[s];
@@ -230,6 +236,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
         store16((char*)p.v_pool + elem * T::bytes, load16(p.v_new + src));
       }
     }
+    return;
   }
 
   // Exclusive prefix sum of tile counts, kPlanThreads sequences per pass.
@@ -1079,11 +1086,11 @@ __device__ __forceinline__ void store4(const AttnParams& p, int s, int head, int
 }
 
 template <typename T>
-__global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
+__global__ __launch_bounds__(kMergeThreads) void attn_merge(const AttnParams p) {
   constexpr int kF4 = kMaxGD / 256;
-  __shared__ float m_lds[kWaves][kMaxGroup];
-  __shared__ float l_lds[kWaves][kMaxGroup];
-  __shared__ __align__(16) float acc_lds[kWaves][kMaxGD];
+  __shared__ float m_lds[kMergeWaves][kMaxGroup];
+  __shared__ float l_lds[kMergeWaves][kMaxGroup];
+  __shared__ __align__(16) float acc_lds[kMergeWaves][kMaxGD];
   const int G = p.gsize, D = p.head_dim, KW = p.kw;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1122,7 +1129,7 @@ __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
     const size_t pair0 = (size_t)c0 + t;
     MergeState st;
     merge_init(st);
-    for (int i0 = wv * kMergeBlock; i0 < n; i0 += kWaves * kMergeBlock)
+    for (int i0 = wv * kMergeBlock; i0 < n; i0 += kMergeWaves * kMergeBlock)
       merge_block(p, pair0 + i0, min(kMergeBlock, n - i0), kw_i, kv.nh, st);
     const float den = head_den(st, G);
     if (lane < kv.nh) {
@@ -1135,15 +1142,15 @@ __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
       if (f < kv.nh * D) *reinterpret_cast<float4*>(&acc_lds[wv][f]) = st.acc[j];
     }
     lds_barrier();
-    for (int f = 4 * threadIdx.x; f < kv.nh * D; f += 4 * kThreads) {
+    for (int f = 4 * threadIdx.x; f < kv.nh * D; f += 4 * kMergeThreads) {
       const int h = f / D;
       float big = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) big = fmaxf(big, m_lds[w][h]);
+      for (int w = 0; w < kMergeWaves; ++w) big = fmaxf(big, m_lds[w][h]);
       float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
       float dsum = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < kMergeWaves; ++w) {
         const float mw = m_lds[w][h];
         const float wt = mw == -INFINITY ? 0.f : fast_exp2(mw - big);
         const float4 a = *reinterpret_cast<const float4*>(&acc_lds[w][f]);
@@ -1165,8 +1172,8 @@ __global__ __launch_bounds__(kThreads) void attn_merge(const AttnParams p) {
   // workgroup down so that they land on workgroups without a long task
   // whenever the grid has room for both.
   const int n_short = __builtin_amdgcn_readfirstlane(__shfl(pre, kPlanGroups - 1)) * KW;
-  for (int it = (gridDim.x - 1 - blockIdx.x) * kWaves + wv; it < n_short;
-       it += gridDim.x * kWaves) {
+  for (int it = (gridDim.x - 1 - blockIdx.x) * kMergeWaves + wv; it < n_short;
+       it += gridDim.x * kMergeWaves) {
     const int ti = it / KW;
     const int kw_i = it - ti * KW;
     const int4 e = entry(p.off_short, 0, ti);
@@ -1447,13 +1454,15 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
 
 template <typename T>
 hipError_t launch_plan(const AttnParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(attn_plan<T>, dim3(kPlanGroups), dim3(kPlanThreads), 0, st, p);
+  // The append workgroups only when there is a token to append.
+  const int groups = kPlanGroups + (p.k_new ? kAppendGroups : 0);
+  hipLaunchKernelGGL(attn_plan<T>, dim3(groups), dim3(kPlanThreads), 0, st, p);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_merge(const AttnParams& p, hipStream_t st) {
-  hipLaunchKernelGGL(attn_merge<T>, dim3(p.grid), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL(attn_merge<T>, dim3(p.grid), dim3(kMergeThreads), 0, st, p);
   return hipGetLastError();
 }
 
