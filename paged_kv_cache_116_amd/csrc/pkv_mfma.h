@@ -108,6 +108,32 @@ template <> struct Pair<F16> {
   __device__ static __forceinline__ float hi(uint32_t w) { return f16_hi(w); }
 };
 
+// Cross-row exchanges without LDS (gfx950 v_permlane16_swap /
+// v_permlane32_swap): swapping a register with itself leaves, in every lane l,
+// the values of lanes l and l ^ 16 (l ^ 32) in the two results, in some
+// order (checked on the GPU).  Max and sum are symmetric, so each lane gets
+// the combination of its pair.
+__device__ __forceinline__ float max_xor16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Two E4M3FN codes (bytes 2*hi, 2*hi + 1 of w) decoded straight to a pair of
 // the element type: every E4M3FN value is exact in bf16 and f16, and a unit
 // scale leaves it unchanged.

@@ -14,10 +14,11 @@
 // 0 .. p, the decode rule applied to every token of the chunk:
 //     out[j, h] = sum_{t <= p} softmax_t(scale * q[j, h] . K[t, h / g]) V[t, h / g]
 //
-// Work decomposition: one workgroup per (64-row block, KV head, sequence),
+// Work decomposition: one workgroup per (row block, KV head, sequence),
 // where a row is a (chunk token, query head of the KV head's group) pair,
 // token-major, so the g heads of a token sit in consecutive rows.  Each of
-// the 4 waves owns 16 rows.  The workgroup streams 16-token K/V tiles from
+// the 4 waves owns two groups of 16 rows (one for D = 256 and in the
+// shared-prefix mode), so a block holds 128 rows (64).  The workgroup streams 16-token K/V tiles from
 // position 0 to the causal limit of its last row through two LDS buffers
 // (loads of tile k+1 in flight while tile k is used); every wave reads the
 // shared tiles.  Per wave and tile, as in the decode kernel:
@@ -47,7 +48,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 16;
-constexpr int kRows = 16 * kWaves;        // rows per workgroup
+// Row groups of 16 per wave: two for prefill with D <= 128 (the groups share
+// every K and V operand read and interleave two MFMA chains); one for
+// D = 256, whose registers would not hold two accumulators, and for the
+// shared-prefix states, whose short key ranges want more workgroups instead.
+constexpr int row_groups(int d, bool prefix) { return (!prefix && d <= 128) ? 2 : 1; }
+constexpr int rows_per_block(int d, bool prefix) { return 16 * kWaves * row_groups(d, prefix); }
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -90,13 +96,20 @@ struct PrefillParams {
 // group, blockIdx.x = row block * splits + key range; writes float states
 // instead of the output.
 template <typename T, int D, bool kPrefix>
-__global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParams p) {
+// Two workgroups per compute unit (one for D = 256, whose accumulator would
+// not fit): this also keeps the MFMA accumulators in ordinary vector
+// registers (with a looser bound the compiler places them in the
+// accumulation registers and copies all of them out and back every tile).
+__global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
+    const PrefillParams p) {
   using S = typename T::storage;
   constexpr int LPR = D / 8;                  // 16-byte chunks per K/V row
   constexpr int KCH = D / 32;                 // MFMA k-chunks of 32 channels
   constexpr int VP = D + 16;                  // V tile row pitch (elements)
   constexpr int NCH = kTile * LPR;            // chunks per tile and pool
   constexpr int CPT = (NCH + kThreads - 1) / kThreads;
+  constexpr int kRG = row_groups(D, kPrefix);
+  constexpr int kRows = rows_per_block(D, kPrefix);   // rows per workgroup
   static_assert(D % 32 == 0 && D <= 256, "head size");
 
   // K tiles: chunk c of row r at c ^ kswz(r), conflict-free for the row-wise
@@ -173,19 +186,30 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
         }
       }
     }
-    // This lane's row (column `col` of the wave's 16).
-    const int r = rb * kRows + w * 16 + col;
-    const bool row_ok = r < rows;
-    const int i = row_ok ? r / g : 0;
-    const int hh = row_ok ? r - i * g : 0;
-    const int h = kvh * g + hh;
-    const int pos = pos_of(i);              // the row's position; keys 0 .. pos
-    // The row of q (and of the output): packed token cu0 + i, or member i's
-    // sequence.
-    const size_t qi = kPrefix ? (size_t)(row_ok ? p.members[cu0 + i] : 0) : (size_t)(cu0 + i);
-    S* orow = (S*)p.out + (qi * p.num_q_heads + h) * D;
-    const size_t state = (size_t)split * p.num_seqs * p.num_q_heads + qi * p.num_q_heads + h;
-    float* srow = kPrefix ? p.o_states + state * D : nullptr;
+    // This lane's rows: column `col` of each of the wave's kRG groups of 16.
+    int pos[kRG];
+    bool row_ok[kRG];
+    size_t state[kRG];
+    S* orow[kRG];
+    float* srow[kRG];
+    size_t qoff[kRG];
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+      const int r = rb * kRows + (w * kRG + rg) * 16 + col;
+      row_ok[rg] = r < rows;
+      const int i = row_ok[rg] ? r / g : 0;
+      const int hh = row_ok[rg] ? r - i * g : 0;
+      const int h = kvh * g + hh;
+      pos[rg] = pos_of(i);                  // the row's position; keys 0 .. pos
+      // The row of q (and of the output): packed token cu0 + i, or member
+      // i's sequence.
+      const size_t qi =
+          kPrefix ? (size_t)(row_ok[rg] ? p.members[cu0 + i] : 0) : (size_t)(cu0 + i);
+      qoff[rg] = (qi * p.num_q_heads + h) * D;
+      orow[rg] = (S*)p.out + qoff[rg];
+      state[rg] = (size_t)split * p.num_seqs * p.num_q_heads + qi * p.num_q_heads + h;
+      srow[rg] = kPrefix ? p.o_states + state[rg] * D : nullptr;
+    }
     // Prefix mode: this workgroup's key range, tiles kt_lo .. kt_hi - 1.
     const int all_tiles = (L + kTile - 1) / kTile;
     const int span = kPrefix ? (all_tiles + p.splits - 1) / p.splits : all_tiles;
@@ -193,13 +217,15 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
     const int kt_hi = kPrefix ? min(kt_lo + span, all_tiles) : 0;
 
     if (invalid || (kPrefix && kt_lo == kt_hi)) {   // uniform across the workgroup
-      if (row_ok) {
+#pragma unroll
+      for (int rg = 0; rg < kRG; ++rg) {
+        if (!row_ok[rg]) continue;
         if constexpr (kPrefix) {   // NaN, or an empty key range: sum 0, log 0
           const float v = invalid ? __builtin_nanf("") : 0.f;
-          for (int d = kgrp; d < D; d += 4) srow[d] = v;
-          if (kgrp == 0) p.lse[state] = invalid ? __builtin_nanf("") : -INFINITY;
+          for (int d = kgrp; d < D; d += 4) srow[rg][d] = v;
+          if (kgrp == 0) p.lse[state[rg]] = invalid ? __builtin_nanf("") : -INFINITY;
         } else {
-          for (int d = kgrp; d < D; d += 4) Cvt<T>::store(orow + d, __builtin_nanf(""));
+          for (int d = kgrp; d < D; d += 4) Cvt<T>::store(orow[rg] + d, __builtin_nanf(""));
         }
       }
       continue;
@@ -209,17 +235,19 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
     // each wave computes up to its own last row's.
     const int last_row = min(rb * kRows + kRows, rows) - 1;
     const int tiles = kPrefix ? kt_hi : pos_of(last_row / g) / kTile + 1;
-    const int w_first = rb * kRows + w * 16;
-    const int w_last = min(w_first + 16, rows) - 1;
+    const int w_first = rb * kRows + w * 16 * kRG;
+    const int w_last = min(w_first + 16 * kRG, rows) - 1;
     const int w_tiles = w_first >= rows ? 0 : kPrefix ? kt_hi : pos_of(w_last / g) / kTile + 1;
 
-    // B operand of the score product: row `col`, channels 32j + 8*kgrp .. +7.
-    uint4 qop[KCH];
-    {
-      const S* qrow = (const S*)p.q + (qi * p.num_q_heads + h) * D + kgrp * 8;
+    // B operands of the score products: row `col` of each group, channels
+    // 32j + 8*kgrp .. +7.
+    uint4 qop[kRG][KCH];
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+      const S* qrow = (const S*)p.q + qoff[rg] + kgrp * 8;
 #pragma unroll
       for (int j = 0; j < KCH; ++j)
-        qop[j] = row_ok ? load16(qrow + 32 * j) : make_uint4(0, 0, 0, 0);
+        qop[rg][j] = row_ok[rg] ? load16(qrow + 32 * j) : make_uint4(0, 0, 0, 0);
     }
 
     // Tile loads: thread tid takes chunks tid + 256u of the tile, the same
@@ -259,11 +287,16 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
       }
     };
 
-    float m_run = -INFINITY;   // running maximum of row `col` (log2 units)
-    float l_run = 0.f;         // normaliser partial: keys of C row group kgrp
-    f32x4_t acc[D / 16];       // O^T: block j holds channels 16j + 4*kgrp .. +3
+    float m_run[kRG], l_run[kRG];   // per group: running maximum (log2 units) of
+                                    // row `col`, normaliser partial of C row group kgrp
+    f32x4_t acc[kRG][D / 16];       // O^T: block j holds channels 16j + 4*kgrp .. +3
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rg = 0; rg < kRG; ++rg) {
+      m_run[rg] = -INFINITY;
+      l_run[rg] = 0.f;
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) acc[rg][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
 
     if (tid == 0) bad_lds = 0;
     load_tile(kt_lo);
@@ -275,69 +308,85 @@ __global__ __launch_bounds__(kThreads) void attn_prefill_mfma(const PrefillParam
       lds_barrier();
       if (kt + 1 < tiles) load_tile(kt + 1);
       if (kt < w_tiles) {
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
+        // The groups' score products share each K operand read.
+        f32x4_t sc[kRG];
 #pragma unroll
-        for (int j = 0; j < KCH; ++j)
-          sc = Mfma<T>::run(k_lds[buf][col * LPR + ((4 * j + kgrp) ^ kswz(col))], qop[j], sc);
-        // Lane (col, kgrp) holds keys 16kt + 4*kgrp + e of row col.
+        for (int rg = 0; rg < kRG; ++rg) sc[rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) {
+          const uint4 ka = k_lds[buf][col * LPR + ((4 * j + kgrp) ^ kswz(col))];
+#pragma unroll
+          for (int rg = 0; rg < kRG; ++rg) sc[rg] = Mfma<T>::run(ka, qop[rg][j], sc[rg]);
+        }
+        // Lane (col, kgrp) holds keys 16kt + 4*kgrp + e of each group's row col.
         const int t0 = kt * kTile + 4 * kgrp;
-        float sv[4];
-        float mt = -INFINITY;
+        uint2 pop[kRG];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sv[e] = (row_ok && t0 + e <= pos) ? sc[e] * p.scale_log2 : -INFINITY;
-          mt = fmaxf(mt, sv[e]);
+        for (int rg = 0; rg < kRG; ++rg) {
+          float sv[4];
+          float mt = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[e] = (row_ok[rg] && t0 + e <= pos[rg]) ? sc[rg][e] * p.scale_log2 : -INFINITY;
+            mt = fmaxf(mt, sv[e]);
+          }
+          mt = max_xor32(max_xor16(mt));
+          // Every row's first tile holds key 0, so m_run is finite from then
+          // on (rows past the chunk stay at -inf and are never written).
+          if (__any(mt > m_run[rg] + kRescaleThreshold)) {
+            const float mn = fmaxf(m_run[rg], mt);
+            const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_run[rg] - mn);
+            m_run[rg] = mn;
+            l_run[rg] *= alpha;
+#pragma unroll
+            for (int j = 0; j < D / 16; ++j) acc[rg][j] *= alpha;
+          }
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pv[e] = m_run[rg] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run[rg]);
+          // P rounded to the element type; l sums the same rounded values.
+          const uint32_t q01 = Pair<T>::pack(pv[0], pv[1]);
+          const uint32_t q23 = Pair<T>::pack(pv[2], pv[3]);
+          l_run[rg] +=
+              (Pair<T>::lo(q01) + Pair<T>::hi(q01)) + (Pair<T>::lo(q23) + Pair<T>::hi(q23));
+          pop[rg] = make_uint2(q01, q23);
         }
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        // Every row's first tile holds key 0, so m_run is finite from then on
-        // (rows past the chunk stay at -inf and are never written).
-        if (__any(mt > m_run + kRescaleThreshold)) {
-          const float mn = fmaxf(m_run, mt);
-          const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_run - mn);
-          m_run = mn;
-          l_run *= alpha;
-#pragma unroll
-          for (int j = 0; j < D / 16; ++j) acc[j] *= alpha;
-        }
-        float pv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) pv[e] = m_run == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run);
-        // P rounded to the element type; l sums the same rounded values.
-        const uint32_t q01 = Pair<T>::pack(pv[0], pv[1]);
-        const uint32_t q23 = Pair<T>::pack(pv[2], pv[3]);
-        l_run += (Pair<T>::lo(q01) + Pair<T>::hi(q01)) + (Pair<T>::lo(q23) + Pair<T>::hi(q23));
-        const uint2 pop = make_uint2(q01, q23);
-        // A operand of block j: V[4*kgrp + e][16j + col], one transposed read.
+        // A operand of block j: V[4*kgrp + e][16j + col], one transposed read
+        // shared by the groups.
         const uint16_t* vt = &v_lds[buf][(4 * kgrp + (col >> 2)) * VP + 4 * (col & 3)];
 #pragma unroll
-        for (int j = 0; j < D / 16; ++j)
-          acc[j] = Mfma16<T>::run(lds_read_tr16(vt + 16 * j), pop, acc[j]);
+        for (int j = 0; j < D / 16; ++j) {
+          const s16x4_t va = lds_read_tr16(vt + 16 * j);
+#pragma unroll
+          for (int rg = 0; rg < kRG; ++rg) acc[rg][j] = Mfma16<T>::run(va, pop[rg], acc[rg][j]);
+        }
       }
     }
     if (bad) bad_lds = 1;
     lds_barrier();
     const bool any_bad = bad_lds != 0;
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
-    if (row_ok) {
-      const float inv = 1.f / l_run;
+#pragma unroll
+    for (int rg = 0; rg < kRG; ++rg) {
+      const float lsum = sum_xor32(sum_xor16(l_run[rg]));
+      if (!row_ok[rg]) continue;
+      const float inv = 1.f / lsum;
       const float nan = __builtin_nanf("");
       if constexpr (kPrefix) {
 #pragma unroll
         for (int j = 0; j < D / 16; ++j)
-          *reinterpret_cast<float4*>(srow + 16 * j + 4 * kgrp) =
+          *reinterpret_cast<float4*>(srow[rg] + 16 * j + 4 * kgrp) =
               any_bad ? make_float4(nan, nan, nan, nan)
-                      : make_float4(acc[j][0] * inv, acc[j][1] * inv, acc[j][2] * inv,
-                                    acc[j][3] * inv);
+                      : make_float4(acc[rg][j][0] * inv, acc[rg][j][1] * inv,
+                                    acc[rg][j][2] * inv, acc[rg][j][3] * inv);
         if (kgrp == 0)   // ln(l * 2^m), m and l in log2 units
-          p.lse[state] = any_bad ? nan : (m_run + log2f(l_run)) * 0.69314718055994531f;
+          p.lse[state[rg]] = any_bad ? nan : (m_run[rg] + log2f(lsum)) * 0.69314718055994531f;
       } else {
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
-          S* o = orow + 16 * j + 4 * kgrp;
+          S* o = orow[rg] + 16 * j + 4 * kgrp;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) Cvt<T>::store(o + e, any_bad ? nan : acc[j][e] * inv);
+          for (int e = 0; e < 4; ++e) Cvt<T>::store(o + e, any_bad ? nan : acc[rg][j][e] * inv);
         }
       }
     }
@@ -406,7 +455,8 @@ extern "C" int paged_prefill_attention(void* out, const void* q, const void* k_p
   p.scale_log2 = scale * kLog2e;
   // The grid's width only sets the parallelism: workgroups loop over any
   // further row blocks of their (KV head, sequence).
-  const long long row_blocks = ((long long)max_chunk_tokens * p.group + kRows - 1) / kRows;
+  const int rpb = head_dim <= 128 ? rows_per_block(128, false) : rows_per_block(256, false);
+  const long long row_blocks = ((long long)max_chunk_tokens * p.group + rpb - 1) / rpb;
   const dim3 grid((unsigned)std::min<long long>(row_blocks, 65535), num_kv_heads, num_seqs);
   const hipError_t e =
       dtype == PKV_F16 ? launch_prefill<F16, false>(p, head_dim, grid, (hipStream_t)stream)
@@ -453,7 +503,8 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
   if (splits < 1 || splits > 65535) return PKV_ERR_INVALID_ARG;
   // blockIdx.x = row block * splits + key range; workgroups loop over any
   // further row blocks.
-  const long long row_blocks = ((long long)max_group_size * p.group + kRows - 1) / kRows;
+  const int rpb = rows_per_block(head_dim, true);
+  const long long row_blocks = ((long long)max_group_size * p.group + rpb - 1) / rpb;
   const long long rbx = std::max<long long>(1, std::min<long long>(row_blocks, 65535 / splits));
   const dim3 grid((unsigned)(rbx * splits), num_kv_heads, num_groups);
   const hipError_t e =
