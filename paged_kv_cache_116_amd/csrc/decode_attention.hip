@@ -797,8 +797,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
         sv[i] = (tb + 4 * kgrp + i < L) ? sc[i] * p.scale_log2 : -INFINITY;
         mt = fmaxf(mt, sv[i]);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_xor32(max_xor16(mt));
 
       // Every lane holds its own head's maximum, so the rescale is lane-local.
       if (__any(mt > m_run + kRescaleThreshold)) {
@@ -851,8 +850,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
     }
 
     // Wave totals: l over the four C row groups; o is complete per lane.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run = sum_xor32(sum_xor16(l_run));
     if (col < G) {
 #pragma unroll
       for (int j = 0; j < D / 16; ++j)
