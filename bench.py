@@ -64,6 +64,11 @@ def parse_args(argv=None):
                          "and back")
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--block-size", type=int, default=None)
+    ap.add_argument("--batch", type=int, default=None,
+                    help="cascade workload: sequences sharing the prefix (default: config 4's 128)")
+    ap.add_argument("--prefix-tokens", type=int, default=1024,
+                    help="cascade workload: shared prefix length in tokens (default: config 4's "
+                         "1024; a multiple of the block size)")
     ap.add_argument("--partition-tokens", type=int, default=0,
                     help="0 = balanced ranges; > 0 = also cap each range at this many tokens")
     ap.add_argument("--kernel", choices=["auto", "valu", "mfma"], default="auto")
@@ -640,12 +645,16 @@ def run_cascade(args, torch, pkv, workloads, dev) -> int:
     decode attention (cache-retaining loads).  `value` is logical KV bytes per
     second (every sequence's whole history, as for decode); the roofline
     prices the distinct bytes the cascade has to read (the prefix once, every
-    private suffix once, q, out) over the cascade call."""
+    private suffix once, q, out) over the cascade call.  --batch and
+    --prefix-tokens draw the same structure at other sizes (suffixes U[1,512])."""
     if args.config != 4:
         print("--workload cascade runs on the shared-prefix config (--config 4)", file=sys.stderr)
         return 2
     t0 = time.time()
-    w = workloads.make_workload(4, device=dev)
+    literal = args.batch is None and args.prefix_tokens == 1024
+    kw = {} if literal else dict(batch=args.batch or 128, len_range=(1, 512),
+                                 prefix_tokens=args.prefix_tokens)
+    w = workloads.make_workload(4, device=dev, **kw)
     torch.cuda.synchronize()
     S, Hq, Hkv, D, B = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
     npre = len(w.shared_blocks)
@@ -750,7 +759,11 @@ def run_cascade(args, torch, pkv, workloads, dev) -> int:
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "cascade decode over " + WORKLOAD_DESC[4], "name": w.name,
+        "config": {"workload": "cascade decode over " + (
+                       WORKLOAD_DESC[4] if literal else
+                       f"shared-prefix GQA fp16: 32 q / 8 kv heads, D 128, B 16, batch {S}, "
+                       f"{args.prefix_tokens}-token shared prefix + U[1,512] private"),
+                   "name": w.name,
                    "batch": S, "prefix_blocks": npre, "block_size": B, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "tokens": int(lens64.sum())},
         "seq_layer_steps_per_s": round(S / (ms_step * 1e-3), 1),

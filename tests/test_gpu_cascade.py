@@ -209,3 +209,26 @@ def test_cascade_small_max_group_size_still_covers_every_member():
     torch.cuda.synchronize()
     ref = o_attn.decode_attention(f64(w.q), ek, ev, w.tables, w.lens, w.block_size, w.scale)
     check_close(out, ref, "cascade, max_group_size 1")
+
+
+def test_cascade_long_prefix_sampled():
+    """A 4096-token prefix shared by 48 sequences: every prefix workgroup walks
+    a key range of many tiles (the split count is capped at 8).  Checked on
+    sampled sequences against the decode oracle."""
+    w = workloads.make_workload(4, batch=48, len_range=(1, 512), prefix_tokens=4096, seed=99,
+                                device="cuda")
+    pb = 4096 // w.block_size
+    sample = [0, 23, 47]
+    host = workloads.extract_sequences(w, sample)
+    pkv.paged_kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, i32(w.tables), i32(w.lens_pre))
+    out = torch.empty_like(w.q)
+    S = w.num_seqs
+    pkv.paged_decode_attention_cascade(out, w.q, w.k_pool, w.v_pool, i32(w.tables), i32(w.lens),
+                                       i32([0, S]), i32(np.arange(S)), i32([pb]), scale=w.scale)
+    torch.cuda.synchronize()
+    ek, ev = o_cache.append_token(host["k_pool"], host["v_pool"], host["k_new"], host["v_new"],
+                                  host["tables"], host["lens_pre"], w.block_size)
+    ref = o_attn.decode_attention(host["q"], ek, ev, host["tables"], host["lens"], w.block_size,
+                                  w.scale)
+    check_close(out[torch.as_tensor(sample, device="cuda")], ref, "cascade, 4096-token prefix")
+    assert torch.isfinite(out.float()).all()
