@@ -114,3 +114,33 @@ def append_token_fp8(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
         k_out[physical, offset] = quantise(k_new[s], k_scale)
         v_out[physical, offset] = quantise(v_new[s], v_scale)
     return k_out, v_out
+
+
+def append_tokens_fp8(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
+                      v_new: np.ndarray, tables: np.ndarray, lens_pre, cu_seqlens,
+                      block_size: int, k_scale: float, v_scale: float):
+    """The multi-token append of prefill chunks into uint8 code pools: sequence
+    s writes the packed rows k_new[cu_seqlens[s] + j], j < n_s, at positions
+    lens_pre[s] + j ([pofe] "How it works": prefill writes the prompt into its
+    blocks), each row quantised as in append_token_fp8.  A negative lens_pre
+    marks a padding row.
+
+    k_new, v_new: [T, H_kv, D] packed (float32-representable values); pools
+    uint8 [N, B, H_kv, D]; lens_pre [S]; cu_seqlens [S + 1].
+    """
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    num_blocks = k_pool.shape[0]
+    cu = [int(x) for x in cu_seqlens]
+    for s, start in enumerate(lens_pre):
+        start = int(start)
+        if start < 0:
+            continue
+        for j in range(cu[s + 1] - cu[s]):
+            physical, offset = resolve(tables[s], block_size, start + j)
+            if not (0 <= physical < num_blocks):
+                raise IndexError(f"sequence {s}: block id {physical} outside the pool")
+            k_out[physical, offset] = quantise(k_new[cu[s] + j], k_scale)
+            v_out[physical, offset] = quantise(v_new[cu[s] + j], v_scale)
+    return k_out, v_out
+

@@ -115,3 +115,37 @@ def test_planted_encoder_mistakes_fail():
         return lo + 1 if a - mags[lo] >= mags[lo + 1] - a else lo
     assert half_up(1.0 + 1 / 16) != fp8.encode_e4m3(1.0 + 1 / 16)
     assert fp8.encode_e4m3(500.0) != 0x7F
+
+
+def test_fp8_append_tokens_equals_repeated_single_appends_and_plain_slots():
+    """Multi-token FP8 append: (1) the same codes as appending the chunk one
+    token at a time with append_token_fp8 (pinned above), and (2) the same
+    slots as the plain multi-token append, holding quantise() of the rows."""
+    rng = np.random.default_rng(21)
+    N, B, H, D = 12, 4, 2, 8
+    tables = np.array([[3, 7, 1, -1], [0, 5, 9, 2], [11, -1, -1, -1]], np.int32)
+    lens_pre = np.array([2, 5, -1])
+    chunks = np.array([7, 6, 3])                       # the padding row's chunk writes nothing
+    cu = np.concatenate([[0], np.cumsum(chunks)])
+    T = int(cu[-1])
+    k_new = rng.normal(0, 40, (T, H, D)).astype(np.float32)
+    v_new = rng.normal(0, 0.3, (T, H, D)).astype(np.float32)
+    pool = rng.integers(0, 256, (N, B, H, D)).astype(np.uint8)
+    ks, vs = 0.5, 0.0625
+    kc, vc = fp8.append_tokens_fp8(pool, pool, k_new, v_new, tables, lens_pre, cu, B, ks, vs)
+    # (1) one token at a time
+    ek, ev = pool.copy(), pool.copy()
+    for s in range(len(chunks)):
+        if lens_pre[s] < 0:
+            continue
+        for j in range(chunks[s]):
+            t = cu[s] + j
+            ek, ev = fp8.append_token_fp8(ek, ev, k_new[t:t + 1], v_new[t:t + 1], tables[s:s + 1],
+                                          [lens_pre[s] + j], B, ks, vs)
+    assert np.array_equal(kc, ek) and np.array_equal(vc, ev)
+    # (2) the plain append's slots, holding the quantised rows
+    pk, pv = cache_ops.append_tokens(pool.astype(np.float64), pool.astype(np.float64),
+                                     fp8.quantise(k_new, ks).astype(np.float64),
+                                     fp8.quantise(v_new, vs).astype(np.float64),
+                                     tables, lens_pre, cu, B)
+    assert np.array_equal(kc, pk.astype(np.uint8)) and np.array_equal(vc, pv.astype(np.uint8))
