@@ -416,11 +416,34 @@ def run_prefill(args, torch, pkv, workloads, dev) -> int:
     print(f"# workload {w.name}: {S} prompts, {T} tokens, blocks={w.num_blocks}, "
           f"drawn in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
+    # FP8 pools: E4M3FN codes drawn field by field (exponents 3..10) for the
+    # history, the NaN code in every slot that holds no token yet.
+    fp8 = args.kv_dtype == "fp8"
+    ks, vs = 0.0625, 0.125
+    if fp8:
+        g = torch.Generator(device=dev)
+        g.manual_seed(2001)
+        empty = torch.isnan(w.k_pool.float()).any(dim=-1).any(dim=-1)
+
+        def codes():
+            shp = tuple(w.k_pool.shape)
+            c = ((torch.randint(0, 2, shp, generator=g, device=dev) << 7) |
+                 (torch.randint(3, 11, shp, generator=g, device=dev) << 3) |
+                 torch.randint(0, 8, shp, generator=g, device=dev)).to(torch.uint8)
+            c[empty] = 0x7F
+            return c.view(torch.float8_e4m3fn)
+        k_pool, v_pool = codes(), codes()
+    else:
+        k_pool, v_pool = w.k_pool, w.v_pool
+
     # Host copies for the oracle, before any library call writes the pools.
     rng = np.random.default_rng(7)
     check = sorted(rng.choice(S, size=2, replace=False).tolist())
     host = {k: getattr(w, k).detach().to("cpu").to(torch.float64).numpy()
             for k in ("k_pool", "v_pool", "k_new", "v_new", "q")} if not args.no_check else None
+    if host is not None and fp8:
+        host["k_pool"] = k_pool.view(torch.uint8).cpu().numpy()
+        host["v_pool"] = v_pool.view(torch.uint8).cpu().numpy()
 
     pre_len = (w.lens - w.chunks).astype(np.int64)
     visible = sum(int(((pre_len[s] + np.arange(w.chunks[s]) + 1)).sum()) for s in range(S))
@@ -434,12 +457,21 @@ def run_prefill(args, torch, pkv, workloads, dev) -> int:
     stream = torch.cuda.current_stream()
 
     def append():
-        pkv.paged_kv_append_tokens(w.k_pool, w.v_pool, w.k_new, w.v_new, cu, tables, lens_pre,
-                                   stream=stream)
+        if fp8:
+            pkv.paged_kv_append_tokens_fp8(k_pool, v_pool, w.k_new, w.v_new, cu, tables,
+                                           lens_pre, ks, vs, stream=stream)
+        else:
+            pkv.paged_kv_append_tokens(k_pool, v_pool, w.k_new, w.v_new, cu, tables, lens_pre,
+                                       stream=stream)
 
     def attention():
-        pkv.paged_prefill_attention(out, w.q, w.k_pool, w.v_pool, cu, tables, lens,
-                                    max_chunk_tokens=max_chunk, scale=w.scale, stream=stream)
+        if fp8:
+            pkv.paged_prefill_attention_fp8(out, w.q, k_pool, v_pool, cu, tables, lens, ks, vs,
+                                            max_chunk_tokens=max_chunk, scale=w.scale,
+                                            stream=stream)
+        else:
+            pkv.paged_prefill_attention(out, w.q, k_pool, v_pool, cu, tables, lens,
+                                        max_chunk_tokens=max_chunk, scale=w.scale, stream=stream)
 
     def step():
         append()
@@ -475,14 +507,26 @@ def run_prefill(args, torch, pkv, workloads, dev) -> int:
     if host is not None or args.cpu_seconds > 0:
         from oracle import attention as o_attn
         from oracle import cache_ops as o_cache
+        from oracle import fp8 as o_fp8
+
+        def oracle_pools(s, sl):
+            """Prompt s's tokens appended to host copies of the pools (FP8
+            pools: quantised codes, returned decoded)."""
+            if not fp8:
+                return o_cache.append_tokens(host["k_pool"], host["v_pool"], host["k_new"][sl],
+                                             host["v_new"][sl], w.tables[s:s + 1],
+                                             w.lens_pre[s:s + 1], [0, int(w.chunks[s])], B)
+            kc, vc = o_fp8.append_tokens_fp8(host["k_pool"], host["v_pool"], host["k_new"][sl],
+                                             host["v_new"][sl], w.tables[s:s + 1],
+                                             w.lens_pre[s:s + 1], [0, int(w.chunks[s])], B, ks,
+                                             vs)
+            return o_fp8.dequantise(kc, ks), o_fp8.dequantise(vc, vs)
 
         def oracle_token(s, j):
             """Output of chunk token j of prompt s, as a one-token chunk over
             its p + 1 visible positions."""
             sl = slice(int(w.cu[s]), int(w.cu[s + 1]))
-            kp, vp = o_cache.append_tokens(host["k_pool"], host["v_pool"], host["k_new"][sl],
-                                           host["v_new"][sl], w.tables[s:s + 1],
-                                           w.lens_pre[s:s + 1], [0, int(w.chunks[s])], B)
+            kp, vp = oracle_pools(s, sl)
             p = int(pre_len[s] + j)
             q1 = host["q"][int(w.cu[s]) + j: int(w.cu[s]) + j + 1]
             return o_attn.prefill_attention(q1, kp, vp, w.tables[s:s + 1], [p + 1], [0, 1], B,
@@ -508,9 +552,7 @@ def run_prefill(args, torch, pkv, workloads, dev) -> int:
             spent, passes = 0.0, 0
             while spent < args.cpu_seconds:
                 t = time.perf_counter()
-                kp, vp = o_cache.append_tokens(host["k_pool"], host["v_pool"], host["k_new"][sl],
-                                               host["v_new"][sl], w.tables[s:s + 1],
-                                               w.lens_pre[s:s + 1], [0, int(w.chunks[s])], B)
+                kp, vp = oracle_pools(s, sl)
                 o_attn.prefill_attention(host["q"][sl], kp, vp, w.tables[s:s + 1],
                                          w.lens[s:s + 1], [0, int(w.chunks[s])], B, w.scale)
                 spent += time.perf_counter() - t
@@ -538,9 +580,11 @@ def run_prefill(args, torch, pkv, workloads, dev) -> int:
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": "prefill: 16 whole prompts, log-normal lengths (median 584, p95 "
-                               "2155, at most 4096), 32 q / 8 kv heads, D 128, B 16, bf16",
+                               "2155, at most 4096), 32 q / 8 kv heads, D 128, B 16, bf16" +
+                               (", FP8 (E4M3FN) pools" if fp8 else ""),
                    "name": w.name, "prompts": S, "tokens": T, "block_size": B,
-                   "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D},
+                   "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                   "kv_dtype": "fp8_e4m3" if fp8 else w.dtype},
         "us": {"step": round(ms_step * 1e3, 2), "append": round(t_app * 1e3, 2),
                "attention": round(attn_ms * 1e3, 2),
                "attention_p10": round(float(np.percentile(t_attn, 10)) * 1e3, 2),

@@ -452,7 +452,8 @@ int paged_kv_append_tokens(void* k_pool, void* v_pool, const void* k_new, const 
  * implicit; this is the decode rule applied to every chunk token):
  *     out[j, h] = sum_{t <= p} softmax_t(scale * q[j, h] . K[t, h / g]) V[t, h / g]
  *   q, out : device [num_tokens, num_q_heads, head_dim], dtype F16 or BF16
- *            (F32 and FP8 pools give PKV_ERR_UNSUPPORTED), head_dim % 32 == 0.
+ *            (F32 gives PKV_ERR_UNSUPPORTED; FP8 pools take
+ *            paged_prefill_attention_fp8), head_dim % 32 == 0.
  *   max_chunk_tokens : host upper bound on n_s used to size the launch; any
  *            value >= 1 computes every row (a smaller one only runs with
  *            less parallelism).
@@ -465,6 +466,34 @@ int paged_prefill_attention(void* out, const void* q, const void* k_pool, const 
                             int max_chunk_tokens, int num_blocks, int block_size,
                             int num_q_heads, int num_kv_heads, int head_dim, float scale,
                             int dtype, void* stream);
+
+/* paged_kv_append_tokens_fp8 - paged_kv_append_tokens into FP8 pools: the
+ * packed rows k_new, v_new [num_tokens, num_kv_heads, head_dim] of new_dtype
+ * (F32, F16 or BF16) are quantised as paged_kv_append_fp8 does, code =
+ * encode(fp32(x) / fp32(scale)).  Same positions, padding rows and skips as
+ * paged_kv_append_tokens; k_scale, v_scale finite and > 0. */
+int paged_kv_append_tokens_fp8(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                               const int32_t* cu_seqlens, int num_tokens,
+                               const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens_pre, int num_seqs, int num_blocks,
+                               int block_size, int num_kv_heads, int head_dim, int new_dtype,
+                               float k_scale, float v_scale, void* stream);
+
+/* paged_prefill_attention_fp8 - paged_prefill_attention over FP8 pools: the
+ * key of position t is decode(code) * k_scale, its value decode(code) *
+ * v_scale ([pofe] "Fine-tuned models and adapters": an FP8 cache changes
+ * nothing else about paging).  q and out have element type dtype (F16 or
+ * BF16); codes are decoded exactly into the 16-bit operands, k_scale is
+ * folded into the softmax scale and v_scale applied to the weighted sum,
+ * both in fp32.  Other arguments, results and error rows as
+ * paged_prefill_attention. */
+int paged_prefill_attention_fp8(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* cu_seqlens, const int32_t* block_tables,
+                                int max_blocks_per_seq, const int32_t* context_lens,
+                                int num_seqs, int max_chunk_tokens, int num_blocks,
+                                int block_size, int num_q_heads, int num_kv_heads, int head_dim,
+                                float scale, float k_scale, float v_scale, int dtype,
+                                void* stream);
 
 /* ------------------------------------------------------------------------- */
 /* Host block manager (CPU only; no device calls)                            */

@@ -79,6 +79,11 @@ _sig("paged_kv_append_tokens", _i32,
      [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("paged_prefill_attention", _i32,
      [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p])
+_sig("paged_kv_append_tokens_fp8", _i32,
+     [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _p])
+_sig("paged_prefill_attention_fp8", _i32,
+     [_p, _p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _f32,
+      _i32, _p])
 _sig("paged_decode_attention_lse", _i32, [_i32, _p] + _ATTN_ARGS)
 _sig("paged_decode_cascade_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32])
 _sig("paged_decode_attention_cascade", _i32,
@@ -648,3 +653,57 @@ def paged_decode_step_fp8(out, q, k_pool, v_pool, k_new, v_new, block_tables, co
                                       _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype),
                                       *a[4:14], float(k_scale), float(v_scale), *a[14:]),
            "paged_decode_step_fp8")
+
+
+def paged_kv_append_tokens_fp8(k_pool, v_pool, k_new, v_new, cu_seqlens, block_tables,
+                               context_lens_pre, k_scale, v_scale, *, stream=None):
+    """paged_kv_append_tokens into FP8 pools: packed rows of k_new / v_new
+    (float32, float16 or bfloat16 [T, kv_heads, head_dim]) quantised as
+    paged_kv_append_fp8 does."""
+    _fp8_pools(k_pool, v_pool)
+    n, b, h, d, _ = _pool_dims(k_pool, v_pool)
+    t = k_new.shape[0]
+    if k_new.shape != (t, h, d) or v_new.shape != (t, h, d) or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must be [num_tokens, kv_heads, head_dim] of one dtype")
+    if k_new.dtype not in _DTYPE_CODE or _DTYPE_CODE[k_new.dtype] == PKV_FP8_E4M3:
+        raise TypeError(f"new-token dtype {k_new.dtype} is not supported")
+    s = block_tables.shape[0]
+    if block_tables.dim() != 2 or context_lens_pre.shape != (s,) or cu_seqlens.shape != (s + 1,):
+        raise ValueError("block_tables [num_seqs, max_blocks], context_lens_pre [num_seqs], "
+                         "cu_seqlens [num_seqs + 1]")
+    _check(_lib.paged_kv_append_tokens_fp8(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+        _dev(v_new, "v_new"), _dev(cu_seqlens, "cu_seqlens", torch.int32), t,
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens_pre, "context_lens_pre", torch.int32), s, n, b, h, d,
+        _DTYPE_CODE[k_new.dtype], float(k_scale), float(v_scale), _stream(stream)),
+        "paged_kv_append_tokens_fp8")
+
+
+def paged_prefill_attention_fp8(out, q, k_pool, v_pool, cu_seqlens, block_tables, context_lens,
+                                k_scale, v_scale, *, max_chunk_tokens=None, scale=None,
+                                stream=None):
+    """paged_prefill_attention over FP8 pools (value = code * scale); q and out
+    are float16 or bfloat16."""
+    _fp8_pools(k_pool, v_pool)
+    n, b, h, d, _ = _pool_dims(k_pool, v_pool)
+    t, hq, dq = q.shape
+    if dq != d or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q / out must be [num_tokens, q_heads, head_dim] of one dtype")
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("q / out must be float16 or bfloat16")
+    s = block_tables.shape[0]
+    if block_tables.dim() != 2 or context_lens.shape != (s,) or cu_seqlens.shape != (s + 1,):
+        raise ValueError("block_tables [num_seqs, max_blocks], context_lens [num_seqs], "
+                         "cu_seqlens [num_seqs + 1]")
+    if max_chunk_tokens is None:
+        max_chunk_tokens = t
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(_lib.paged_prefill_attention_fp8(
+        _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+        _dev(cu_seqlens, "cu_seqlens", torch.int32),
+        _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), s, int(max_chunk_tokens), n, b, hq, h, d,
+        scale, float(k_scale), float(v_scale), _DTYPE_CODE[q.dtype], _stream(stream)),
+        "paged_prefill_attention_fp8")
+

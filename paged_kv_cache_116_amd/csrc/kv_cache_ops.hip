@@ -122,6 +122,61 @@ __global__ __launch_bounds__(kThreads) void append_tokens_kernel(
   store16(v_pool + dst + 16 * (size_t)c, load16(v_new + src + 16 * (size_t)c));
 }
 
+// Several new tokens per sequence into FP8 pools: thread i quantises 8
+// elements (chunk i % row_chunks) of packed token i / row_chunks, as
+// append_fp8_kernel does for one token, at the position append_tokens_kernel
+// gives it.  T is the element type of k_new / v_new.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void append_tokens_fp8_kernel(
+    uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, const char* __restrict__ k_new,
+    const char* __restrict__ v_new, const int32_t* __restrict__ cu, int num_tokens,
+    const int32_t* __restrict__ tables, int max_blocks, const int32_t* __restrict__ lens_pre,
+    int num_seqs, int num_blocks, int log2_b, int num_kv_heads, int head_dim, float k_scale,
+    float v_scale) {
+  const int row = num_kv_heads * head_dim;           // elements, a multiple of 16
+  const int row_chunks = row / 8;
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;
+  if (i >= (long long)num_tokens * row_chunks) return;
+  const int tok = (int)(i / row_chunks);
+  const int c = (int)(i - (long long)tok * row_chunks);
+  if (tok < cu[0] || tok >= cu[num_seqs]) return;           // not in any chunk
+  int lo = 0, hi = num_seqs - 1;                            // last s with cu[s] <= tok
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= tok) lo = mid;
+    else hi = mid - 1;
+  }
+  const int s = lo;
+  const int start = lens_pre[s];
+  if (start < 0) return;                                    // padding row
+  const int pos = start + (tok - cu[s]);
+  const int lb = logical_block(pos, log2_b);
+  if (pos < 0 || lb >= max_blocks) return;                  // past the table row: skip
+  const int blk = tables[(size_t)s * max_blocks + lb];
+  if (!valid_block(blk, num_blocks)) return;                // id outside the pool: skip
+  const size_t dst = row_offset(blk, pos, log2_b, num_kv_heads, 0, head_dim) + 8 * (size_t)c;
+  const size_t src = ((size_t)tok * row + 8 * (size_t)c) * T::bytes;
+  float kf[8], vf[8];
+  if constexpr (T::bytes == 4) {
+    Cvt<T>::unpack(load16(k_new + src), kf);
+    Cvt<T>::unpack(load16(k_new + src + 16), kf + 4);
+    Cvt<T>::unpack(load16(v_new + src), vf);
+    Cvt<T>::unpack(load16(v_new + src + 16), vf + 4);
+  } else {
+    Cvt<T>::unpack(load16(k_new + src), kf);
+    Cvt<T>::unpack(load16(v_new + src), vf);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    kf[e] = kf[e] / k_scale;
+    vf[e] = vf[e] / v_scale;
+  }
+  *reinterpret_cast<uint2*>(k_pool + dst) = make_uint2(e4m3_encode4(kf[0], kf[1], kf[2], kf[3]),
+                                                       e4m3_encode4(kf[4], kf[5], kf[6], kf[7]));
+  *reinterpret_cast<uint2*>(v_pool + dst) = make_uint2(e4m3_encode4(vf[0], vf[1], vf[2], vf[3]),
+                                                       e4m3_encode4(vf[4], vf[5], vf[6], vf[7]));
+}
+
 // blockIdx.x = pair, blockIdx.y = slice of the block's chunks.
 __global__ __launch_bounds__(kThreads) void copy_blocks_kernel(
     char* __restrict__ k_pool, char* __restrict__ v_pool, const int32_t* __restrict__ src,
@@ -264,6 +319,42 @@ extern "C" int paged_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new
                        (const char*)k_new, (const char*)v_new, block_tables, max_blocks_per_seq,
                        context_lens_pre, num_blocks, log2_b, num_kv_heads, head_dim, k_scale,
                        v_scale);
+  };
+  if (new_dtype == PKV_F32) launch(F32{});
+  else if (new_dtype == PKV_F16) launch(F16{});
+  else launch(BF16{});
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+extern "C" int paged_kv_append_tokens_fp8(void* k_pool, void* v_pool, const void* k_new,
+                                          const void* v_new, const int32_t* cu_seqlens,
+                                          int num_tokens, const int32_t* block_tables,
+                                          int max_blocks_per_seq,
+                                          const int32_t* context_lens_pre, int num_seqs,
+                                          int num_blocks, int block_size, int num_kv_heads,
+                                          int head_dim, int new_dtype, float k_scale,
+                                          float v_scale, void* stream) {
+  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, PKV_FP8_E4M3);
+  if (st != PKV_OK) return st;
+  if (!supported_dtype(new_dtype)) return PKV_ERR_UNSUPPORTED;
+  if (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == INFINITY || v_scale == INFINITY)
+    return PKV_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_tokens < 0 || max_blocks_per_seq < 1) return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !cu_seqlens || !block_tables ||
+      !context_lens_pre)
+    return PKV_ERR_INVALID_ARG;
+  const long long row_chunks = (long long)num_kv_heads * head_dim / 8;
+  const long long blocks = (num_tokens * row_chunks + kThreads - 1) / kThreads;
+  if (blocks > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  const int log2_b = log2_exact(block_size);
+  auto launch = [&](auto tag) {
+    using T = decltype(tag);
+    hipLaunchKernelGGL(append_tokens_fp8_kernel<T>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       (hipStream_t)stream, (uint8_t*)k_pool, (uint8_t*)v_pool,
+                       (const char*)k_new, (const char*)v_new, cu_seqlens, num_tokens,
+                       block_tables, max_blocks_per_seq, context_lens_pre, num_seqs, num_blocks,
+                       log2_b, num_kv_heads, head_dim, k_scale, v_scale);
   };
   if (new_dtype == PKV_F32) launch(F32{});
   else if (new_dtype == PKV_F16) launch(F16{});

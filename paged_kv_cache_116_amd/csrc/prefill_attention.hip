@@ -38,6 +38,8 @@
 // them with the suffix result by the log-sum-exp rule.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_common.h"
 #include "pkv_host.h"
 #include "pkv_mfma.h"
@@ -71,7 +73,8 @@ struct PrefillParams {
   int num_q_heads;
   int num_kv_heads;
   int group;          // g = Hq / Hkv
-  float scale_log2;   // scale * log2(e)
+  float scale_log2;   // scale * log2(e) (* k_scale for FP8 pools)
+  float v_scale;      // multiplies the weighted V sum (1 unless FP8)
   // Shared-prefix states (the kPrefix kernel): group z has members
   // members[offsets[z] .. offsets[z+1]) sharing their first prefix_blocks[z]
   // table entries; key range r of the prefix gives each member's rows the
@@ -90,12 +93,22 @@ struct PrefillParams {
   int32_t* suf_lens;
 };
 
+// 8 pool elements as 8 elements of T: the identity for 16-bit pools, the
+// exact decode of 8 E4M3FN codes for FP8 pools.
+template <typename T>
+__device__ __forceinline__ uint4 widen8_impl(const uint4& v) { return v; }
+template <typename T>
+__device__ __forceinline__ uint4 widen8_impl(const uint2& c) {
+  return make_uint4(Fp8Pair<T>::template decode<false>(c.x), Fp8Pair<T>::template decode<true>(c.x),
+                    Fp8Pair<T>::template decode<false>(c.y), Fp8Pair<T>::template decode<true>(c.y));
+}
+
 // kPrefix = false: causal chunked prefill, blockIdx.z = sequence.
 // kPrefix = true: attention of every member's query over its group's shared
 // prefix (no mask; all prefix positions precede the query), blockIdx.z =
 // group, blockIdx.x = row block * splits + key range; writes float states
 // instead of the output.
-template <typename T, int D, bool kPrefix>
+template <typename T, int D, bool kPrefix, bool kF8 = false>
 // Two workgroups per compute unit (one for D = 256, whose accumulator would
 // not fit): this also keeps the MFMA accumulators in ordinary vector
 // registers (with a looser bound the compiler places them in the
@@ -252,8 +265,12 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
 
     // Tile loads: thread tid takes chunks tid + 256u of the tile, the same
     // chunk of K and of V; rows past L - 1 read row L - 1 (masked anyway).
+    // FP8 pools: a chunk is 8 codes (8 bytes), decoded to T when stored to
+    // LDS, so the loads stay in flight until then.
+    using KvReg = typename std::conditional<kF8, uint2, uint4>::type;
+    constexpr int KVB = kF8 ? 1 : T::bytes;   // bytes per pool element
     int bad = 0;
-    uint4 kreg[CPT], vreg[CPT];
+    KvReg kreg[CPT], vreg[CPT];
     auto load_tile = [&](int kt) {
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
@@ -268,9 +285,14 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
             blk = 0;
           }
           const size_t off =
-              row_offset(blk, t, p.log2_b, p.num_kv_heads, kvh, D) * T::bytes + ch * 16;
-          kreg[u] = load16(p.k_pool + off);
-          vreg[u] = load16(p.v_pool + off);
+              row_offset(blk, t, p.log2_b, p.num_kv_heads, kvh, D) * KVB + ch * 8 * KVB;
+          if constexpr (kF8) {
+            kreg[u] = *reinterpret_cast<const uint2*>(p.k_pool + off);
+            vreg[u] = *reinterpret_cast<const uint2*>(p.v_pool + off);
+          } else {
+            kreg[u] = load16(p.k_pool + off);
+            vreg[u] = load16(p.v_pool + off);
+          }
         }
       }
     };
@@ -281,8 +303,8 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
         if (NCH % kThreads == 0 || c < NCH) {
           const int row = c / LPR;
           const int ch = c - row * LPR;
-          k_lds[buf][row * LPR + (ch ^ kswz(row))] = kreg[u];
-          *reinterpret_cast<uint4*>(&v_lds[buf][row * VP + ch * 8]) = vreg[u];
+          k_lds[buf][row * LPR + (ch ^ kswz(row))] = widen8_impl<T>(kreg[u]);
+          *reinterpret_cast<uint4*>(&v_lds[buf][row * VP + ch * 8]) = widen8_impl<T>(vreg[u]);
         }
       }
     };
@@ -370,7 +392,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     for (int rg = 0; rg < kRG; ++rg) {
       const float lsum = sum_xor32(sum_xor16(l_run[rg]));
       if (!row_ok[rg]) continue;
-      const float inv = 1.f / lsum;
+      const float inv = p.v_scale / lsum;
       const float nan = __builtin_nanf("");
       if constexpr (kPrefix) {
 #pragma unroll
@@ -395,44 +417,46 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
   }
 }
 
-template <typename T, bool kPrefix>
+template <typename T, bool kPrefix, bool kF8>
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, dim3 grid, hipStream_t st) {
   switch (head_dim) {
     case 32:
-      hipLaunchKernelGGL((attn_prefill_mfma<T, 32, kPrefix>), grid, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((attn_prefill_mfma<T, 32, kPrefix, kF8>), grid, dim3(kThreads), 0, st, p);
       break;
     case 64:
-      hipLaunchKernelGGL((attn_prefill_mfma<T, 64, kPrefix>), grid, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((attn_prefill_mfma<T, 64, kPrefix, kF8>), grid, dim3(kThreads), 0, st, p);
       break;
     case 128:
-      hipLaunchKernelGGL((attn_prefill_mfma<T, 128, kPrefix>), grid, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((attn_prefill_mfma<T, 128, kPrefix, kF8>), grid, dim3(kThreads), 0, st,
+                         p);
       break;
     default:
-      hipLaunchKernelGGL((attn_prefill_mfma<T, 256, kPrefix>), grid, dim3(kThreads), 0, st, p);
+      hipLaunchKernelGGL((attn_prefill_mfma<T, 256, kPrefix, kF8>), grid, dim3(kThreads), 0, st,
+                         p);
       break;
   }
   return hipGetLastError();
 }
 
-}  // namespace
-}  // namespace pkv
-
-using namespace pkv;
-
-extern "C" int paged_prefill_attention(void* out, const void* q, const void* k_pool,
-                                       const void* v_pool, const int32_t* cu_seqlens,
-                                       const int32_t* block_tables, int max_blocks_per_seq,
-                                       const int32_t* context_lens, int num_seqs,
-                                       int max_chunk_tokens, int num_blocks, int block_size,
-                                       int num_q_heads, int num_kv_heads, int head_dim,
-                                       float scale, int dtype, void* stream) {
-  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, dtype);
+// Causal chunked prefill over 16-bit pools (kv_fp8 = false) or FP8 pools,
+// whose K scale folds into the score scale and V scale into the output.
+int prefill_attention_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                           const int32_t* cu_seqlens, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                           int max_chunk_tokens, int num_blocks, int block_size,
+                           int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                           int dtype, void* stream, bool kv_fp8, float k_scale, float v_scale) {
+  int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim,
+                            kv_fp8 ? PKV_FP8_E4M3 : dtype);
   if (st != PKV_OK) return st;
   if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (head_dim % 32 != 0) return PKV_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_seqs > 65535 || max_chunk_tokens < 0 || max_blocks_per_seq < 1 ||
       num_q_heads < 1 || num_kv_heads > 65535 || num_q_heads % num_kv_heads != 0 ||
       !(scale > 0.f) || scale == INFINITY)
+    return PKV_ERR_INVALID_ARG;
+  if (kv_fp8 && (!(k_scale > 0.f) || !(v_scale > 0.f) || k_scale == INFINITY ||
+                 v_scale == INFINITY))
     return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0 || max_chunk_tokens == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !cu_seqlens || !block_tables || !context_lens)
@@ -452,16 +476,54 @@ extern "C" int paged_prefill_attention(void* out, const void* q, const void* k_p
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
-  p.scale_log2 = scale * kLog2e;
+  p.scale_log2 = scale * kLog2e * (kv_fp8 ? k_scale : 1.f);
+  p.v_scale = kv_fp8 ? v_scale : 1.f;
   // The grid's width only sets the parallelism: workgroups loop over any
   // further row blocks of their (KV head, sequence).
   const int rpb = head_dim <= 128 ? rows_per_block(128, false) : rows_per_block(256, false);
   const long long row_blocks = ((long long)max_chunk_tokens * p.group + rpb - 1) / rpb;
   const dim3 grid((unsigned)std::min<long long>(row_blocks, 65535), num_kv_heads, num_seqs);
-  const hipError_t e =
-      dtype == PKV_F16 ? launch_prefill<F16, false>(p, head_dim, grid, (hipStream_t)stream)
-                       : launch_prefill<BF16, false>(p, head_dim, grid, (hipStream_t)stream);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e;
+  if (kv_fp8)
+    e = dtype == PKV_F16 ? launch_prefill<F16, false, true>(p, head_dim, grid, hs)
+                         : launch_prefill<BF16, false, true>(p, head_dim, grid, hs);
+  else
+    e = dtype == PKV_F16 ? launch_prefill<F16, false, false>(p, head_dim, grid, hs)
+                         : launch_prefill<BF16, false, false>(p, head_dim, grid, hs);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int paged_prefill_attention(void* out, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* cu_seqlens,
+                                       const int32_t* block_tables, int max_blocks_per_seq,
+                                       const int32_t* context_lens, int num_seqs,
+                                       int max_chunk_tokens, int num_blocks, int block_size,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       float scale, int dtype, void* stream) {
+  return prefill_attention_impl(out, q, k_pool, v_pool, cu_seqlens, block_tables,
+                                max_blocks_per_seq, context_lens, num_seqs, max_chunk_tokens,
+                                num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
+                                scale, dtype, stream, false, 1.f, 1.f);
+}
+
+extern "C" int paged_prefill_attention_fp8(void* out, const void* q, const void* k_pool,
+                                           const void* v_pool, const int32_t* cu_seqlens,
+                                           const int32_t* block_tables, int max_blocks_per_seq,
+                                           const int32_t* context_lens, int num_seqs,
+                                           int max_chunk_tokens, int num_blocks, int block_size,
+                                           int num_q_heads, int num_kv_heads, int head_dim,
+                                           float scale, float k_scale, float v_scale, int dtype,
+                                           void* stream) {
+  return prefill_attention_impl(out, q, k_pool, v_pool, cu_seqlens, block_tables,
+                                max_blocks_per_seq, context_lens, num_seqs, max_chunk_tokens,
+                                num_blocks, block_size, num_q_heads, num_kv_heads, head_dim,
+                                scale, dtype, stream, true, k_scale, v_scale);
 }
 
 namespace pkv {
@@ -491,6 +553,7 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
   p.scale_log2 = scale * kLog2e;
+  p.v_scale = 1.f;
   p.splits = splits;
   p.num_seqs = num_seqs;
   p.suf_tables = suf_tables;
@@ -508,8 +571,8 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
   const long long rbx = std::max<long long>(1, std::min<long long>(row_blocks, 65535 / splits));
   const dim3 grid((unsigned)(rbx * splits), num_kv_heads, num_groups);
   const hipError_t e =
-      dtype == PKV_F16 ? launch_prefill<F16, true>(p, head_dim, grid, (hipStream_t)stream)
-                       : launch_prefill<BF16, true>(p, head_dim, grid, (hipStream_t)stream);
+      dtype == PKV_F16 ? launch_prefill<F16, true, false>(p, head_dim, grid, (hipStream_t)stream)
+                       : launch_prefill<BF16, true, false>(p, head_dim, grid, (hipStream_t)stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -200,3 +200,108 @@ def test_fp8_every_finite_code_decodes_exactly(dtype):
     got = out.double().cpu().numpy()
     for h in range(Hq):
         assert np.array_equal(got[:, h, :], want), f"head {h}: decoded values differ"
+
+
+# --- FP8 prefill: multi-token quantising append + causal chunk attention -------
+
+def fp8_prefill_workload(seed, lens, chunks, B, hq, hkv, D, dtype="bf16"):
+    """A prefill workload whose pools hold E4M3FN codes: finite codes drawn
+    field by field (exponents 3..10) for the history, the NaN code 0x7F in
+    every slot that holds no token yet.  q and the new rows keep the 16-bit
+    type."""
+    w = workloads.make_prefill_workload(seed, lens=lens, chunks=chunks, block_size=B,
+                                        num_q_heads=hq, num_kv_heads=hkv, head_dim=D,
+                                        dtype=dtype)
+    rng = np.random.default_rng(seed + 1)
+    shape = tuple(w.k_pool.shape)
+    def codes():
+        c = (rng.integers(0, 2, shape) << 7) | (rng.integers(3, 11, shape) << 3) | \
+            rng.integers(0, 8, shape)
+        return c.astype(np.uint8)
+    empty = torch.isnan(w.k_pool.float()).any(dim=-1).any(dim=-1).numpy()    # [N, B]
+    kc, vc = codes(), codes()
+    kc[empty] = 0x7F
+    vc[empty] = 0x7F
+    return w, kc, vc
+
+
+def fp8_prefill_oracle(w, kc, vc, ks, vs):
+    ek, ev = o_fp8.append_tokens_fp8(kc, vc, f64(w.k_new), f64(w.v_new), w.tables, w.lens_pre,
+                                     w.cu, w.block_size, ks, vs)
+    ref = o_attn.prefill_attention(f64(w.q), o_fp8.dequantise(ek, ks), o_fp8.dequantise(ev, vs),
+                                   w.tables, w.lens, w.cu, w.block_size)
+    return ek, ev, ref
+
+
+def to_fp8(a):
+    return torch.from_numpy(a).cuda().view(torch.float8_e4m3fn)
+
+
+@pytest.mark.parametrize("src", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("B", [4, 16])
+def test_append_tokens_fp8_codes_are_bit_exact(src, B):
+    w, kc, vc = fp8_prefill_workload(71 + B, [5, 40, 17, 64, 9], [5, 7, 0, 33, 1], B, 4, 2, 32,
+                                     dtype=src)
+    kp, vp = to_fp8(kc), to_fp8(vc)
+    pkv.paged_kv_append_tokens_fp8(kp, vp, w.k_new.cuda(), w.v_new.cuda(),
+                                   torch.as_tensor(w.cu, device="cuda"),
+                                   torch.as_tensor(w.tables, device="cuda"),
+                                   torch.as_tensor(w.lens_pre, device="cuda"), 0.25, 0.125)
+    torch.cuda.synchronize()
+    ek, ev = o_fp8.append_tokens_fp8(kc, vc, f64(w.k_new), f64(w.v_new), w.tables, w.lens_pre,
+                                     w.cu, B, 0.25, 0.125)
+    assert np.array_equal(codes(kp), ek)
+    assert np.array_equal(codes(vp), ev)
+
+
+FP8_PREFILL_CASES = [
+    # Hq, Hkv, D, B, dtype, lens, chunks
+    (8, 1, 128, 16, "bf16", [1, 17, 300, 40, 1000], [1, 5, 64, 33, 1]),
+    (32, 8, 128, 16, "bf16", [129, 64, 700], [129, 16, 80]),
+    (8, 2, 64, 8, "f16", [100, 37, 250], [100, 37, 17]),
+    (6, 3, 128, 4, "bf16", [50, 123], [50, 1]),
+    (16, 2, 256, 16, "f16", [200, 33], [70, 33]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FP8_PREFILL_CASES)))
+def test_prefill_fp8_matches_oracle(case):
+    Hq, Hkv, D, B, dtype, lens, chunks = FP8_PREFILL_CASES[case]
+    w, kc, vc = fp8_prefill_workload(300 + case, lens, chunks, B, Hq, Hkv, D, dtype=dtype)
+    ks, vs = 0.0625, 0.125
+    ek, ev, ref = fp8_prefill_oracle(w, kc, vc, ks, vs)
+    kp, vp = to_fp8(kc), to_fp8(vc)
+    cu = torch.as_tensor(w.cu, device="cuda")
+    tables = torch.as_tensor(w.tables, device="cuda")
+    pkv.paged_kv_append_tokens_fp8(kp, vp, w.k_new.cuda(), w.v_new.cuda(), cu, tables,
+                                   torch.as_tensor(w.lens_pre, device="cuda"), ks, vs)
+    q = w.q.cuda()
+    out = torch.empty_like(q)
+    pkv.paged_prefill_attention_fp8(out, q, kp, vp, cu, tables,
+                                    torch.as_tensor(w.lens, device="cuda"), ks, vs,
+                                    max_chunk_tokens=int(max(chunks)))
+    torch.cuda.synchronize()
+    assert np.array_equal(codes(kp), ek) and np.array_equal(codes(vp), ev)
+    check_close(out, ref, f"fp8 prefill case {case}")
+
+
+def test_prefill_fp8_one_token_chunks_equal_fp8_decode():
+    """A chunk of one token is a decode step: FP8 prefill and FP8 decode
+    attention over the same pools agree to the 16-bit tolerance."""
+    w, kc, vc = fp8_prefill_workload(401, [33, 200, 517], [1, 1, 1], 16, 16, 2, 128)
+    ks, vs = 0.0625, 0.125
+    kp, vp = to_fp8(kc), to_fp8(vc)
+    cu = torch.as_tensor(w.cu, device="cuda")
+    tables = torch.as_tensor(w.tables, device="cuda")
+    lens = torch.as_tensor(w.lens, device="cuda")
+    pkv.paged_kv_append_tokens_fp8(kp, vp, w.k_new.cuda(), w.v_new.cuda(), cu, tables,
+                                   torch.as_tensor(w.lens_pre, device="cuda"), ks, vs)
+    q = w.q.cuda()
+    a = torch.empty_like(q)
+    b = torch.empty_like(q)
+    pkv.paged_prefill_attention_fp8(a, q, kp, vp, cu, tables, lens, ks, vs, max_chunk_tokens=1)
+    pkv.paged_decode_attention_fp8(b, q, kp, vp, tables, lens, ks, vs)
+    torch.cuda.synchronize()
+    _, _, ref = fp8_prefill_oracle(w, kc, vc, ks, vs)
+    check_close(a, ref, "fp8 prefill, one-token chunks")
+    check_close(b, ref, "fp8 decode, same pools")

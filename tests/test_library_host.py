@@ -159,6 +159,52 @@ def test_append_tokens_validates_arguments(args, code):
     assert lib.paged_kv_append_tokens(*args) == code
 
 
+def prefill_fp8(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, cu=FAKE, tables=FAKE, mb=4, lens=FAKE, s=2, mc=8,
+             n=16, b=16, hq=8, hkv=2, d=128, scale=0.1, ks=0.5, vs=0.25, dt=2, stream=None)
+    a.update(kw)
+    return lib.paged_prefill_attention_fp8(a["out"], a["q"], a["k"], a["v"], a["cu"],
+                                           a["tables"], a["mb"], a["lens"], a["s"], a["mc"],
+                                           a["n"], a["b"], a["hq"], a["hkv"], a["d"], a["scale"],
+                                           a["ks"], a["vs"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=0), pkv.PKV_ERR_UNSUPPORTED),         # q / out F32
+    (dict(dt=3), pkv.PKV_ERR_UNSUPPORTED),         # q / out cannot be FP8
+    (dict(d=16), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(b=12), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(hq=7, hkv=2), pkv.PKV_ERR_INVALID_ARG),
+    (dict(ks=0.0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(vs=float("inf")), pkv.PKV_ERR_INVALID_ARG),
+    (dict(vs=float("nan")), pkv.PKV_ERR_INVALID_ARG),
+    (dict(q=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(s=0, q=None), pkv.PKV_OK),
+])
+def test_prefill_fp8_rejects_bad_arguments(kw, code):
+    assert prefill_fp8(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 16, 16, 2, 128, 2, 0.5, 0.5, None),
+     pkv.PKV_OK),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, FAKE, 0, 16, 16, 2, 128, 2, 0.5, 0.5, None),
+     pkv.PKV_OK),
+    ((FAKE, FAKE, FAKE, FAKE, None, 4, FAKE, 4, FAKE, 2, 16, 16, 2, 128, 2, 0.5, 0.5, None),
+     pkv.PKV_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 16, 16, 2, 128, 2, 0.0, 0.5, None),
+     pkv.PKV_ERR_INVALID_ARG),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 16, 16, 2, 128, 3, 0.5, 0.5, None),
+     pkv.PKV_ERR_UNSUPPORTED),                       # new tokens cannot be FP8 codes
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 4, FAKE, 2, 16, 12, 2, 128, 2, 0.5, 0.5, None),
+     pkv.PKV_ERR_UNSUPPORTED),
+])
+def test_append_tokens_fp8_validates_arguments(args, code):
+    if code == pkv.PKV_OK and args[9] != 0:
+        args = args[:1] + (FAKE,) + args[2:5] + (0,) + args[6:]   # num_tokens 0: no launch
+    assert lib.paged_kv_append_tokens_fp8(*args) == code
+
+
 def test_zero_sequences_is_a_noop():
     assert attn(s=0) == pkv.PKV_OK
     assert lib.paged_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 0, 16, 16, 2, 128, 2, None) == 0
