@@ -328,6 +328,24 @@ int paged_decode_attention_cascade(int kernel, void* out, const void* q, const v
                                    void* workspace, size_t workspace_bytes, int dtype,
                                    void* stream);
 
+/* paged_decode_attention_cascade_fp8 - paged_decode_attention_cascade over
+ * FP8 pools (the key of token t is decode(code) * k_scale, its value
+ * decode(code) * v_scale, as for paged_decode_attention_fp8): the prefix
+ * states and the suffix decode both decode the codes into 16-bit operands.
+ * q and out have element type dtype (F16 or BF16); k_scale and v_scale
+ * finite and > 0.  Workspace: paged_decode_cascade_workspace_bytes. */
+int paged_decode_attention_cascade_fp8(int kernel, void* out, const void* q, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_tables,
+                                       int max_blocks_per_seq, const int32_t* context_lens,
+                                       int num_seqs, const int32_t* group_offsets,
+                                       const int32_t* group_members,
+                                       const int32_t* group_prefix_blocks, int num_groups,
+                                       int max_group_size, int num_blocks, int block_size,
+                                       int num_q_heads, int num_kv_heads, int head_dim,
+                                       float scale, float k_scale, float v_scale,
+                                       void* workspace, size_t workspace_bytes, int dtype,
+                                       void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* FP8 cache blocks                                                           */
 /* ------------------------------------------------------------------------- */

@@ -89,6 +89,9 @@ _sig("paged_decode_cascade_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32]
 _sig("paged_decode_attention_cascade", _i32,
      [_i32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
       _i32, _f32, _p, _sz, _i32, _p])
+_sig("paged_decode_attention_cascade_fp8", _i32,
+     [_i32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
+      _i32, _f32, _f32, _f32, _p, _sz, _i32, _p])
 _sig("paged_kv_swap_out", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("paged_kv_swap_in", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("pkv_bm_seq_swap_out", _i32, [_p, _i32, _p, _i32, _intp])
@@ -706,4 +709,42 @@ def paged_prefill_attention_fp8(out, q, k_pool, v_pool, cu_seqlens, block_tables
         _dev(context_lens, "context_lens", torch.int32), s, int(max_chunk_tokens), n, b, hq, h, d,
         scale, float(k_scale), float(v_scale), _DTYPE_CODE[q.dtype], _stream(stream)),
         "paged_prefill_attention_fp8")
+
+
+def paged_decode_attention_cascade_fp8(out, q, k_pool, v_pool, block_tables, context_lens,
+                                       group_offsets, group_members, group_prefix_blocks,
+                                       k_scale, v_scale, *, max_group_size=None, scale=None,
+                                       workspace=None, stream=None, kernel=PKV_ATTN_AUTO):
+    """paged_decode_attention_cascade over FP8 pools (value = code * scale);
+    q and out are float16 or bfloat16."""
+    _fp8_pools(k_pool, v_pool)
+    n, b, h, d, _ = _pool_dims(k_pool, v_pool)
+    s, hq, dq = q.shape
+    if dq != d or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q / out must be [num_seqs, num_q_heads, head_dim] of one dtype")
+    if q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("q / out must be float16 or bfloat16")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens.shape != (s,):
+        raise ValueError("block_tables [num_seqs, max_blocks] and context_lens [num_seqs]")
+    g = group_prefix_blocks.shape[0]
+    if group_offsets.shape != (g + 1,) or group_members.dim() != 1:
+        raise ValueError("group_offsets [G + 1], group_members [M], group_prefix_blocks [G]")
+    mb = block_tables.shape[1]
+    if max_group_size is None:
+        max_group_size = group_members.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        need = paged_decode_cascade_workspace_bytes(s, hq, d, mb, b)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(_lib.paged_decode_attention_cascade_fp8(
+        int(kernel), _dev(out, "out", q.dtype), _dev(q, "q"), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32), mb,
+        _dev(context_lens, "context_lens", torch.int32), s,
+        _dev(group_offsets, "group_offsets", torch.int32),
+        _dev(group_members, "group_members", torch.int32),
+        _dev(group_prefix_blocks, "group_prefix_blocks", torch.int32), g, int(max_group_size),
+        n, b, hq, h, d, float(scale), float(k_scale), float(v_scale),
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _DTYPE_CODE[q.dtype],
+        _stream(stream)), "paged_decode_attention_cascade_fp8")
 

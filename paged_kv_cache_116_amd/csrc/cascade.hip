@@ -168,14 +168,18 @@ extern "C" size_t paged_decode_cascade_workspace_bytes(int num_seqs, int num_q_h
       .total;
 }
 
-extern "C" int paged_decode_attention_cascade(
-    int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
-    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
-    int num_seqs, const int32_t* group_offsets, const int32_t* group_members,
-    const int32_t* group_prefix_blocks, int num_groups, int max_group_size, int num_blocks,
-    int block_size, int num_q_heads, int num_kv_heads, int head_dim, float scale,
-    void* workspace, size_t workspace_bytes, int dtype, void* stream) {
-  using namespace pkv;
+namespace pkv {
+namespace {
+
+// The cascade over 16-bit pools (kv_fp8 = false) or FP8 pools.
+int cascade_impl(int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
+                 const int32_t* block_tables, int max_blocks_per_seq,
+                 const int32_t* context_lens, int num_seqs, const int32_t* group_offsets,
+                 const int32_t* group_members, const int32_t* group_prefix_blocks,
+                 int num_groups, int max_group_size, int num_blocks, int block_size,
+                 int num_q_heads, int num_kv_heads, int head_dim, float scale, void* workspace,
+                 size_t workspace_bytes, int dtype, void* stream, bool kv_fp8, float k_scale,
+                 float v_scale) {
   if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (head_dim % 32 != 0 || !supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (num_groups < 0 || num_groups > 65535 || max_group_size < 0 || num_seqs < 0)
@@ -201,7 +205,8 @@ extern "C" int paged_decode_attention_cascade(
     const int st = decode_attention_check(kernel, out, q, k_pool, v_pool, suf_tables,
                                           max_blocks_per_seq, suf_lens, num_seqs, num_blocks,
                                           block_size, num_q_heads, num_kv_heads, head_dim, scale,
-                                          ws + w.decode, workspace_bytes - w.decode, dtype);
+                                          ws + w.decode, workspace_bytes - w.decode, dtype,
+                                          kv_fp8, k_scale, v_scale);
     if (st != PKV_OK) return st;
   }
   hipStream_t hs = (hipStream_t)stream;
@@ -220,13 +225,14 @@ extern "C" int paged_decode_attention_cascade(
         q, k_pool, v_pool, block_tables, context_lens, max_blocks_per_seq, num_seqs, num_blocks,
         block_size, num_q_heads, num_kv_heads, head_dim, scale, group_offsets, group_members,
         group_prefix_blocks, num_groups, max_group_size, splits, o_pre, lse_pre, suf_tables,
-        suf_lens, dtype, stream);
+        suf_lens, dtype, stream, kv_fp8, k_scale, v_scale);
     if (st != PKV_OK) return st;
   }
   int st = decode_attention_with_lse(kernel, out, lse_suf, q, k_pool, v_pool, suf_tables,
                                      max_blocks_per_seq, suf_lens, num_seqs, num_blocks,
                                      block_size, num_q_heads, num_kv_heads, head_dim, scale,
-                                     ws + w.decode, workspace_bytes - w.decode, dtype, stream);
+                                     ws + w.decode, workspace_bytes - w.decode, dtype, stream,
+                                     kv_fp8, k_scale, v_scale);
   if (st != PKV_OK) return st;
   if (num_groups > 0) {
     // Any grid height covers every member (workgroups stride over them).
@@ -242,4 +248,35 @@ extern "C" int paged_decode_attention_cascade(
                          stride);
   }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int paged_decode_attention_cascade(
+    int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+    int num_seqs, const int32_t* group_offsets, const int32_t* group_members,
+    const int32_t* group_prefix_blocks, int num_groups, int max_group_size, int num_blocks,
+    int block_size, int num_q_heads, int num_kv_heads, int head_dim, float scale,
+    void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  return pkv::cascade_impl(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                           context_lens, num_seqs, group_offsets, group_members,
+                           group_prefix_blocks, num_groups, max_group_size, num_blocks,
+                           block_size, num_q_heads, num_kv_heads, head_dim, scale, workspace,
+                           workspace_bytes, dtype, stream, false, 1.f, 1.f);
+}
+
+extern "C" int paged_decode_attention_cascade_fp8(
+    int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+    int num_seqs, const int32_t* group_offsets, const int32_t* group_members,
+    const int32_t* group_prefix_blocks, int num_groups, int max_group_size, int num_blocks,
+    int block_size, int num_q_heads, int num_kv_heads, int head_dim, float scale, float k_scale,
+    float v_scale, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  return pkv::cascade_impl(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
+                           context_lens, num_seqs, group_offsets, group_members,
+                           group_prefix_blocks, num_groups, max_group_size, num_blocks,
+                           block_size, num_q_heads, num_kv_heads, head_dim, scale, workspace,
+                           workspace_bytes, dtype, stream, true, k_scale, v_scale);
 }

@@ -1510,11 +1510,11 @@ int decode_attention_check(int kernel, void* out, const void* q, const void* k_p
                            int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
                            int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
                            int head_dim, float scale, void* workspace, size_t workspace_bytes,
-                           int dtype) {
+                           int dtype, bool kv_fp8, float k_scale, float v_scale) {
   Launch L;
   return prepare(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq, context_lens,
                  num_seqs, num_blocks, block_size, num_q_heads, num_kv_heads, head_dim, scale,
-                 0, workspace, workspace_bytes, dtype, &L);
+                 0, workspace, workspace_bytes, dtype, &L, kv_fp8, k_scale, v_scale);
 }
 
 int decode_attention_with_lse(int kernel, void* out, float* lse, const void* q,
@@ -1523,12 +1523,12 @@ int decode_attention_with_lse(int kernel, void* out, float* lse, const void* q,
                               const int32_t* context_lens, int num_seqs, int num_blocks,
                               int block_size, int num_q_heads, int num_kv_heads, int head_dim,
                               float scale, void* workspace, size_t workspace_bytes, int dtype,
-                              void* stream) {
+                              void* stream, bool kv_fp8, float k_scale, float v_scale) {
   return decode_attention_impl(kPhaseAll, kernel, out, q, k_pool, v_pool, block_tables,
                                max_blocks_per_seq, context_lens, num_seqs, num_blocks,
                                block_size, num_q_heads, num_kv_heads, head_dim, scale, 0,
-                               workspace, workspace_bytes, dtype, stream, nullptr, nullptr, false,
-                               1.f, 1.f, lse);
+                               workspace, workspace_bytes, dtype, stream, nullptr, nullptr, kv_fp8,
+                               k_scale, v_scale, lse);
 }
 
 }  // namespace pkv

@@ -40,24 +40,25 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
                          int num_kv_heads, int head_dim, float scale, const int32_t* offsets,
                          const int32_t* members, const int32_t* prefix_blocks, int num_groups,
                          int max_group_size, int splits, float* o_states, float* lse,
-                         int32_t* suf_tables, int32_t* suf_lens, int dtype, void* stream);
+                         int32_t* suf_tables, int32_t* suf_lens, int dtype, void* stream,
+                         bool kv_fp8, float k_scale, float v_scale);
 
 // Defined in decode_attention.hip; used by the cascade decode.  The first
 // validates a decode call without launching anything (PKV_OK or an error),
 // the second runs one with log normalisers (paged_decode_attention_lse with
-// balanced claims).
+// balanced claims); both over 16-bit or FP8 pools.
 int decode_attention_check(int kernel, void* out, const void* q, const void* k_pool,
                            const void* v_pool, const int32_t* block_tables,
                            int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
                            int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
                            int head_dim, float scale, void* workspace, size_t workspace_bytes,
-                           int dtype);
+                           int dtype, bool kv_fp8, float k_scale, float v_scale);
 int decode_attention_with_lse(int kernel, void* out, float* lse, const void* q,
                               const void* k_pool, const void* v_pool,
                               const int32_t* block_tables, int max_blocks_per_seq,
                               const int32_t* context_lens, int num_seqs, int num_blocks,
                               int block_size, int num_q_heads, int num_kv_heads, int head_dim,
                               float scale, void* workspace, size_t workspace_bytes, int dtype,
-                              void* stream);
+                              void* stream, bool kv_fp8, float k_scale, float v_scale);
 
 }  // namespace pkv

@@ -532,14 +532,16 @@ namespace pkv {
 // group and each of `splits` key ranges of the group's shared prefix, the
 // normalised attention output over that range (float [splits, S, Hq, D]) and
 // its natural log normaliser ([splits, S, Hq]); also the members' suffix
-// tables and lengths.
+// tables and lengths.  FP8 pools: codes decoded, k_scale in the score scale,
+// v_scale in the states.
 int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* tables, const int32_t* lens, int max_blocks,
                          int num_seqs, int num_blocks, int block_size, int num_q_heads,
                          int num_kv_heads, int head_dim, float scale, const int32_t* offsets,
                          const int32_t* members, const int32_t* prefix_blocks, int num_groups,
                          int max_group_size, int splits, float* o_states, float* lse,
-                         int32_t* suf_tables, int32_t* suf_lens, int dtype, void* stream) {
+                         int32_t* suf_tables, int32_t* suf_lens, int dtype, void* stream,
+                         bool kv_fp8, float k_scale, float v_scale) {
   PrefillParams p{};
   p.q = q;
   p.k_pool = (const char*)k_pool;
@@ -552,8 +554,8 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
   p.group = num_q_heads / num_kv_heads;
-  p.scale_log2 = scale * kLog2e;
-  p.v_scale = 1.f;
+  p.scale_log2 = scale * kLog2e * (kv_fp8 ? k_scale : 1.f);
+  p.v_scale = kv_fp8 ? v_scale : 1.f;
   p.splits = splits;
   p.num_seqs = num_seqs;
   p.suf_tables = suf_tables;
@@ -570,9 +572,14 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
   const long long row_blocks = ((long long)max_group_size * p.group + rpb - 1) / rpb;
   const long long rbx = std::max<long long>(1, std::min<long long>(row_blocks, 65535 / splits));
   const dim3 grid((unsigned)(rbx * splits), num_kv_heads, num_groups);
-  const hipError_t e =
-      dtype == PKV_F16 ? launch_prefill<F16, true, false>(p, head_dim, grid, (hipStream_t)stream)
-                       : launch_prefill<BF16, true, false>(p, head_dim, grid, (hipStream_t)stream);
+  hipStream_t hs = (hipStream_t)stream;
+  hipError_t e;
+  if (kv_fp8)
+    e = dtype == PKV_F16 ? launch_prefill<F16, true, true>(p, head_dim, grid, hs)
+                         : launch_prefill<BF16, true, true>(p, head_dim, grid, hs);
+  else
+    e = dtype == PKV_F16 ? launch_prefill<F16, true, false>(p, head_dim, grid, hs)
+                         : launch_prefill<BF16, true, false>(p, head_dim, grid, hs);
   return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

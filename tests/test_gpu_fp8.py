@@ -305,3 +305,31 @@ def test_prefill_fp8_one_token_chunks_equal_fp8_decode():
     _, _, ref = fp8_prefill_oracle(w, kc, vc, ks, vs)
     check_close(a, ref, "fp8 prefill, one-token chunks")
     check_close(b, ref, "fp8 decode, same pools")
+
+
+@pytest.mark.parametrize("prefix_tokens,batch", [(256, 10), (1024, 24)])
+def test_cascade_fp8_matches_oracle(prefix_tokens, batch):
+    """Cascade decode over FP8 pools: the prefix states and the suffix decode
+    both decode the codes; checked against float64 attention over the
+    decoded pools, with one group holding every sequence and a second group
+    sharing only part of the prefix."""
+    w = workloads.make_workload(4, kv_fp8=True, batch=batch, len_range=(1, 150),
+                                prefix_tokens=prefix_tokens, seed=55)
+    dev = to_dev(w)
+    ref, kc, vc = oracle_step(w)
+    pkv.paged_kv_append_fp8(dev["k_pool"], dev["v_pool"], dev["k_new"], dev["v_new"],
+                            dev["tables"], dev["lens_pre"], w.k_scale, w.v_scale)
+    pb = prefix_tokens // w.block_size
+    S = w.num_seqs
+    groups = [(list(range(0, S - 2)), pb), ([S - 2, S - 1], pb // 2)]
+    offsets = np.cumsum([0] + [len(m) for m, _ in groups]).astype(np.int32)
+    members = np.concatenate([m for m, _ in groups]).astype(np.int32)
+    out = torch.empty_like(dev["q"])
+    pkv.paged_decode_attention_cascade_fp8(
+        out, dev["q"], dev["k_pool"], dev["v_pool"], dev["tables"], dev["lens"],
+        torch.as_tensor(offsets, device="cuda"), torch.as_tensor(members, device="cuda"),
+        torch.as_tensor(np.array([p for _, p in groups], np.int32), device="cuda"),
+        w.k_scale, w.v_scale, max_group_size=S - 2, scale=w.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(codes(dev["k_pool"]), kc)
+    check_close(out, ref, f"fp8 cascade prefix={prefix_tokens}")
