@@ -18,17 +18,20 @@
 // where a row is a (chunk token, query head of the KV head's group) pair,
 // token-major, so the g heads of a token sit in consecutive rows.  Each of
 // the 4 waves owns two groups of 16 rows (one for D = 256 and in the
-// shared-prefix mode), so a block holds 128 rows (64).  The workgroup streams 16-token K/V tiles from
-// position 0 to the causal limit of its last row through two LDS buffers
-// (loads of tile k+1 in flight while tile k is used); every wave reads the
-// shared tiles.  Per wave and tile, as in the decode kernel:
-//   S^T[16 keys x 16 rows] = K . Q^T   (D/32 v_mfma_f32_16x16x32)
-//   causal mask per row, running max with lazy rescale, exp2
-//   O^T[D x 16 rows] += V^T . P^T      (D/16 v_mfma_f32_16x16x16; P stays in
-//                                       registers, V^T comes from
-//                                       transposing LDS reads)
-// Workgroups loop over further row blocks with stride gridDim.x, so any grid
-// width covers every chunk.
+// shared-prefix mode), so a block holds 128 rows (64).  The workgroup
+// streams 32-token K/V tiles from position 0 to the causal limit of its last
+// row through two LDS buffers (loads of tile k+1 in flight while tile k is
+// used); every wave reads the shared tiles.  Per wave and tile:
+//   S^T[16 keys x 16 rows] = K . Q^T   for each 16-key half
+//                                      (D/32 v_mfma_f32_16x16x32 each)
+//   causal mask per row, one running max over the 32 keys with lazy
+//   rescale, exp2
+//   O^T[D x 16 rows] += V^T . P^T      (D/16 v_mfma_f32_16x16x32 over all
+//                                       32 keys; P stays in registers, V^T
+//                                       comes from transposing LDS reads)
+// Row blocks are taken from the last (heaviest) one down; workgroups loop
+// over further row blocks with stride gridDim.x, so any grid width covers
+// every chunk.
 //
 // Shared-prefix mode (for the cascade decode): the rows are (member, query
 // head) pairs of a group whose members share their first blocks; every row
@@ -49,7 +52,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kTile = 16;
+// Keys per tile: two halves of 16, whose score products are separate
+// 16-key MFMAs and whose P.V products run as one 32-deep MFMA.
+constexpr int kTile = 32;
 // Row groups of 16 per wave: two for prefill with D <= 128 (the groups share
 // every K and V operand read and interleave two MFMA chains); one for
 // D = 256, whose registers would not hold two accumulators, and for the
@@ -137,12 +142,35 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     else return (r >> 2) & 3;
   };
 
-  const int z = blockIdx.z;
-  // Prefix mode: key range `split` of the prefix's tiles.
+  // Prefix mode: key range `split` of the prefix's tiles, every workgroup
+  // the same amount of work.  Prefill: a row block's work grows with its
+  // index (its rows see more keys), so row blocks are dispatched from the
+  // last one down.  The linear workgroup index i gives row block
+  // gx - 1 - (8 * (i / 8 / P) + i % 8), (KV head, sequence) pair (i / 8) % P
+  // (P pairs, gx a multiple of 8): heavy blocks start first and light ones
+  // fill in at the end, and eight consecutive workgroups, which the
+  // dispatcher places on the eight XCDs in turn, take eight row blocks of
+  // one pair, so that the workgroups running on one XCD at a time belong to
+  // many pairs.  (Giving all of a pair's row blocks to one XCD raised its L2
+  // hit rate from 80 to 86 % and made the kernel 23 % slower: the
+  // workgroups of a pair read the same tiles at the same time.)
+  int z, kvh, rb_first;
+  if constexpr (kPrefix) {
+    z = blockIdx.z;
+    kvh = blockIdx.y;
+    rb_first = (int)(blockIdx.x / p.splits);
+  } else {
+    const uint64_t per = (uint64_t)gridDim.y * gridDim.z;
+    const uint64_t lin =
+        blockIdx.x + (uint64_t)gridDim.x * (blockIdx.y + (uint64_t)gridDim.y * blockIdx.z);
+    const uint64_t slot = lin >> 3;
+    const uint64_t rest = slot % per;
+    rb_first = (int)(gridDim.x - 1 - ((slot / per) * 8 + (lin & 7)));
+    z = (int)(rest / gridDim.y);
+    kvh = (int)(rest % gridDim.y);
+  }
   const int split = kPrefix ? (int)(blockIdx.x % p.splits) : 0;
-  const int rb_first = kPrefix ? (int)(blockIdx.x / p.splits) : (int)blockIdx.x;
   const int rb_stride = kPrefix ? (int)(gridDim.x / p.splits) : (int)gridDim.x;
-  const int kvh = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -202,27 +230,28 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     // This lane's rows: column `col` of each of the wave's kRG groups of 16.
     int pos[kRG];
     bool row_ok[kRG];
-    size_t state[kRG];
-    S* orow[kRG];
-    float* srow[kRG];
-    size_t qoff[kRG];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
       const int r = rb * kRows + (w * kRG + rg) * 16 + col;
       row_ok[rg] = r < rows;
-      const int i = row_ok[rg] ? r / g : 0;
-      const int hh = row_ok[rg] ? r - i * g : 0;
-      const int h = kvh * g + hh;
-      pos[rg] = pos_of(i);                  // the row's position; keys 0 .. pos
-      // The row of q (and of the output): packed token cu0 + i, or member
-      // i's sequence.
-      const size_t qi =
-          kPrefix ? (size_t)(row_ok[rg] ? p.members[cu0 + i] : 0) : (size_t)(cu0 + i);
-      qoff[rg] = (qi * p.num_q_heads + h) * D;
-      orow[rg] = (S*)p.out + qoff[rg];
-      state[rg] = (size_t)split * p.num_seqs * p.num_q_heads + qi * p.num_q_heads + h;
-      srow[rg] = kPrefix ? p.o_states + state[rg] * D : nullptr;
+      pos[rg] = pos_of(row_ok[rg] ? r / g : 0);   // the row's position; keys 0 .. pos
     }
+    // Where this lane's row of group rg lives: its element offset in q and
+    // in the output (packed token cu0 + i, or member i's sequence) and its
+    // state index.  Recomputed where needed instead of held in registers
+    // through the tile loop.
+    struct RowAddr {
+      size_t qoff, state;
+    };
+    auto row_addr = [&](int rg) {
+      const int r = rb * kRows + (w * kRG + rg) * 16 + col;
+      const bool ok = r < rows;
+      const int i = ok ? r / g : 0;
+      const int h = kvh * g + (ok ? r - i * g : 0);
+      const size_t qi = kPrefix ? (size_t)(ok ? p.members[cu0 + i] : 0) : (size_t)(cu0 + i);
+      return RowAddr{(qi * p.num_q_heads + h) * D,
+                     (size_t)split * p.num_seqs * p.num_q_heads + qi * p.num_q_heads + h};
+    };
     // Prefix mode: this workgroup's key range, tiles kt_lo .. kt_hi - 1.
     const int all_tiles = (L + kTile - 1) / kTile;
     const int span = kPrefix ? (all_tiles + p.splits - 1) / p.splits : all_tiles;
@@ -233,12 +262,14 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
 #pragma unroll
       for (int rg = 0; rg < kRG; ++rg) {
         if (!row_ok[rg]) continue;
+        const RowAddr ra = row_addr(rg);
         if constexpr (kPrefix) {   // NaN, or an empty key range: sum 0, log 0
           const float v = invalid ? __builtin_nanf("") : 0.f;
-          for (int d = kgrp; d < D; d += 4) srow[rg][d] = v;
-          if (kgrp == 0) p.lse[state[rg]] = invalid ? __builtin_nanf("") : -INFINITY;
+          for (int d = kgrp; d < D; d += 4) p.o_states[ra.state * D + d] = v;
+          if (kgrp == 0) p.lse[ra.state] = invalid ? __builtin_nanf("") : -INFINITY;
         } else {
-          for (int d = kgrp; d < D; d += 4) Cvt<T>::store(orow[rg] + d, __builtin_nanf(""));
+          S* orow = (S*)p.out + ra.qoff;
+          for (int d = kgrp; d < D; d += 4) Cvt<T>::store(orow + d, __builtin_nanf(""));
         }
       }
       continue;
@@ -257,7 +288,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     uint4 qop[kRG][KCH];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
-      const S* qrow = (const S*)p.q + qoff[rg] + kgrp * 8;
+      const S* qrow = (const S*)p.q + row_addr(rg).qoff + kgrp * 8;
 #pragma unroll
       for (int j = 0; j < KCH; ++j)
         qop[rg][j] = row_ok[rg] ? load16(qrow + 32 * j) : make_uint4(0, 0, 0, 0);
@@ -269,19 +300,32 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     // LDS, so the loads stay in flight until then.
     using KvReg = typename std::conditional<kF8, uint2, uint4>::type;
     constexpr int KVB = kF8 ? 1 : T::bytes;   // bytes per pool element
-    int bad = 0;
+    // bad: a tile the workgroup used held an invalid block id; bad_ld: the
+    // tile loaded last did.
+    int bad = 0, bad_ld = 0;
     KvReg kreg[CPT], vreg[CPT];
+    // Block ids of the tile loaded next, fetched one tile ahead of its data
+    // so that the data loads never wait for them.
+    int blk_nx[CPT];
+    auto chunk_pos = [&](int kt, int c) { return min(kt * kTile + c / LPR, L - 1); };
+    auto load_ids = [&](int kt) {
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = tid + kThreads * u;
+        blk_nx[u] = (NCH % kThreads == 0 || c < NCH) ? trow[chunk_pos(kt, c) >> p.log2_b] : 0;
+      }
+    };
     auto load_tile = [&](int kt) {
+      bad_ld = 0;
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
         const int c = tid + kThreads * u;
         if (NCH % kThreads == 0 || c < NCH) {
-          const int row = c / LPR;
-          const int ch = c - row * LPR;
-          const int t = min(kt * kTile + row, L - 1);
-          int blk = trow[t >> p.log2_b];
+          const int ch = c % LPR;
+          const int t = chunk_pos(kt, c);
+          int blk = blk_nx[u];
           if (!valid_block(blk, p.num_blocks)) {
-            bad = 1;
+            bad_ld = 1;
             blk = 0;
           }
           const size_t off =
@@ -309,79 +353,119 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
       }
     };
 
-    float m_run[kRG], l_run[kRG];   // per group: running maximum (log2 units) of
-                                    // row `col`, normaliser partial of C row group kgrp
-    f32x4_t acc[kRG][D / 16];       // O^T: block j holds channels 16j + 4*kgrp .. +3
+    // Per group: running maximum of row `col` (scaled, log2 units); the
+    // row's normaliser, accumulated by the matrix cores as the product of a
+    // ones operand with P^T, so every entry holds the sum of the same
+    // rounded weights the P.V product uses; O^T, block j holding channels
+    // 16j + 4*kgrp .. +3.
+    float m_run[kRG];
+    f32x4_t l_acc[kRG];
+    f32x4_t acc[kRG][D / 16];
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
       m_run[rg] = -INFINITY;
-      l_run[rg] = 0.f;
+      l_acc[rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) acc[rg][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    const uint32_t one2 = Pair<T>::pack(1.f, 1.f);
+    const uint4 ones = make_uint4(one2, one2, one2, one2);
+    // Tiles wholly at or before the position of the wave's first row need no
+    // causal mask (rows past the chunk then compute values from zero queries
+    // that are never written).
+    const int w_pos0 = w_first >= rows ? -1 : pos_of(w_first / g);
 
     if (tid == 0) bad_lds = 0;
+    load_ids(kt_lo);
     load_tile(kt_lo);
+    load_ids(kt_lo + 1);
     for (int kt = kt_lo; kt < tiles; ++kt) {
       const int buf = (kt - kt_lo) & 1;
       store_tile(buf);
+      bad |= bad_ld;
       // Tile kt visible to every wave; also, every wave is done with buffer
       // buf ^ 1 (read in iteration kt - 1) before it is written next.
       lds_barrier();
-      if (kt + 1 < tiles) load_tile(kt + 1);
+      // Loads of tile kt + 1 and the block ids of kt + 2, unconditional so
+      // that the compiler's counted waits stay exact; past the last tile
+      // they read clamped positions and are never stored.
+      load_tile(kt + 1);
+      load_ids(kt + 2);
       if (kt < w_tiles) {
-        // The groups' score products share each K operand read.
-        f32x4_t sc[kRG];
+        // Scores of the tile's two 16-key halves; the groups' products share
+        // each K operand read.
+        f32x4_t sc[2][kRG];
 #pragma unroll
-        for (int rg = 0; rg < kRG; ++rg) sc[rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int hf = 0; hf < 2; ++hf) {
+          const int kr = 16 * hf + col;
 #pragma unroll
-        for (int j = 0; j < KCH; ++j) {
-          const uint4 ka = k_lds[buf][col * LPR + ((4 * j + kgrp) ^ kswz(col))];
+          for (int rg = 0; rg < kRG; ++rg) sc[hf][rg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int rg = 0; rg < kRG; ++rg) sc[rg] = Mfma<T>::run(ka, qop[rg][j], sc[rg]);
+          for (int j = 0; j < KCH; ++j) {
+            const uint4 ka = k_lds[buf][kr * LPR + ((4 * j + kgrp) ^ kswz(kr))];
+#pragma unroll
+            for (int rg = 0; rg < kRG; ++rg) sc[hf][rg] = Mfma<T>::run(ka, qop[rg][j], sc[hf][rg]);
+          }
         }
-        // Lane (col, kgrp) holds keys 16kt + 4*kgrp + e of each group's row col.
-        const int t0 = kt * kTile + 4 * kgrp;
-        uint2 pop[kRG];
+        // Lane (col, kgrp) holds keys 32kt + 16hf + 4*kgrp + e of each
+        // group's row col.  Causal mask, where the tile reaches past the
+        // position of the wave's first row: keys after a row's position, and
+        // rows past the chunk, get -inf.
+        if (kt * kTile + kTile - 1 > w_pos0) {
+          const int t0 = kt * kTile + 4 * kgrp;
+#pragma unroll
+          for (int rg = 0; rg < kRG; ++rg) {
+            const int lim = row_ok[rg] ? pos[rg] - t0 : -1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (16 * (e >> 2) + (e & 3) > lim) sc[e >> 2][rg][e & 3] = -INFINITY;
+          }
+        }
+        uint4 pop[kRG];
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg) {
-          float sv[4];
           float mt = -INFINITY;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sv[e] = (row_ok[rg] && t0 + e <= pos[rg]) ? sc[rg][e] * p.scale_log2 : -INFINITY;
-            mt = fmaxf(mt, sv[e]);
-          }
-          mt = max_xor32(max_xor16(mt));
-          // Every row's first tile holds key 0, so m_run is finite from then
-          // on (rows past the chunk stay at -inf and are never written).
+          for (int e = 0; e < 8; ++e) mt = fmaxf(mt, sc[e >> 2][rg][e & 3]);
+          // The scale is positive, so the maximum of the raw scores scales.
+          mt = max_xor32(max_xor16(mt)) * p.scale_log2;
+          // Every row's first tile holds a visible key, so m_run is finite
+          // from then on (rows past the chunk stay at -inf and are never
+          // written).
           if (__any(mt > m_run[rg] + kRescaleThreshold)) {
             const float mn = fmaxf(m_run[rg], mt);
             const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_run[rg] - mn);
             m_run[rg] = mn;
-            l_run[rg] *= alpha;
+            l_acc[rg] *= alpha;
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) acc[rg][j] *= alpha;
           }
-          float pv[4];
+          // Weights exp2(scale * s - m), rounded to the element type (0 for
+          // masked keys; a row with no visible key yet subtracts 0).  B
+          // operand of the P.V product: k index 8*kgrp + e is key 4*kgrp + e
+          // of the first half (e < 4), of the second (e >= 4).
+          const float neg_m = m_run[rg] == -INFINITY ? 0.f : -m_run[rg];
+          float pv[8];
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pv[e] = m_run[rg] == -INFINITY ? 0.f : fast_exp2(sv[e] - m_run[rg]);
-          // P rounded to the element type; l sums the same rounded values.
-          const uint32_t q01 = Pair<T>::pack(pv[0], pv[1]);
-          const uint32_t q23 = Pair<T>::pack(pv[2], pv[3]);
-          l_run[rg] +=
-              (Pair<T>::lo(q01) + Pair<T>::hi(q01)) + (Pair<T>::lo(q23) + Pair<T>::hi(q23));
-          pop[rg] = make_uint2(q01, q23);
+          for (int e = 0; e < 8; ++e)
+            pv[e] = fast_exp2(fmaf(sc[e >> 2][rg][e & 3], p.scale_log2, neg_m));
+          pop[rg] = make_uint4(Pair<T>::pack(pv[0], pv[1]), Pair<T>::pack(pv[2], pv[3]),
+                               Pair<T>::pack(pv[4], pv[5]), Pair<T>::pack(pv[6], pv[7]));
         }
-        // A operand of block j: V[4*kgrp + e][16j + col], one transposed read
-        // shared by the groups.
+        // Row sums of the rounded weights.
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg) l_acc[rg] = Mfma<T>::run(ones, pop[rg], l_acc[rg]);
+        // A operand of block j: V[4*kgrp + e][16j + col] and
+        // V[16 + 4*kgrp + e][16j + col], two transposed reads shared by the
+        // groups, the same key order as P's.
         const uint16_t* vt = &v_lds[buf][(4 * kgrp + (col >> 2)) * VP + 4 * (col & 3)];
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
-          const s16x4_t va = lds_read_tr16(vt + 16 * j);
+          const uint2 v0 = __builtin_bit_cast(uint2, lds_read_tr16(vt + 16 * j));
+          const uint2 v1 = __builtin_bit_cast(uint2, lds_read_tr16(vt + 16 * VP + 16 * j));
+          const uint4 va = make_uint4(v0.x, v0.y, v1.x, v1.y);
 #pragma unroll
-          for (int rg = 0; rg < kRG; ++rg) acc[rg][j] = Mfma16<T>::run(va, pop[rg], acc[rg][j]);
+          for (int rg = 0; rg < kRG; ++rg) acc[rg][j] = Mfma<T>::run(va, pop[rg], acc[rg][j]);
         }
       }
     }
@@ -390,23 +474,25 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     const bool any_bad = bad_lds != 0;
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
-      const float lsum = sum_xor32(sum_xor16(l_run[rg]));
+      const float lsum = l_acc[rg][0];
       if (!row_ok[rg]) continue;
       const float inv = p.v_scale / lsum;
       const float nan = __builtin_nanf("");
+      const RowAddr ra = row_addr(rg);
       if constexpr (kPrefix) {
+        float* srow = p.o_states + ra.state * D;
 #pragma unroll
         for (int j = 0; j < D / 16; ++j)
-          *reinterpret_cast<float4*>(srow[rg] + 16 * j + 4 * kgrp) =
+          *reinterpret_cast<float4*>(srow + 16 * j + 4 * kgrp) =
               any_bad ? make_float4(nan, nan, nan, nan)
                       : make_float4(acc[rg][j][0] * inv, acc[rg][j][1] * inv,
                                     acc[rg][j][2] * inv, acc[rg][j][3] * inv);
         if (kgrp == 0)   // ln(l * 2^m), m and l in log2 units
-          p.lse[state[rg]] = any_bad ? nan : (m_run[rg] + log2f(lsum)) * 0.69314718055994531f;
+          p.lse[ra.state] = any_bad ? nan : (m_run[rg] + log2f(lsum)) * 0.69314718055994531f;
       } else {
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
-          S* o = orow[rg] + 16 * j + 4 * kgrp;
+          S* o = (S*)p.out + ra.qoff + 16 * j + 4 * kgrp;
 #pragma unroll
           for (int e = 0; e < 4; ++e) Cvt<T>::store(o + e, any_bad ? nan : acc[rg][j][e] * inv);
         }
@@ -482,7 +568,9 @@ int prefill_attention_impl(void* out, const void* q, const void* k_pool, const v
   // further row blocks of their (KV head, sequence).
   const int rpb = head_dim <= 128 ? rows_per_block(128, false) : rows_per_block(256, false);
   const long long row_blocks = ((long long)max_chunk_tokens * p.group + rpb - 1) / rpb;
-  const dim3 grid((unsigned)std::min<long long>(row_blocks, 65535), num_kv_heads, num_seqs);
+  // A multiple of 8 row blocks, which the kernel's dispatch order needs.
+  const dim3 grid((unsigned)std::min<long long>((row_blocks + 7) / 8 * 8, 65528), num_kv_heads,
+                  num_seqs);
   hipStream_t hs = (hipStream_t)stream;
   hipError_t e;
   if (kv_fp8)
