@@ -50,6 +50,8 @@
 namespace pkv {
 namespace {
 
+typedef const __attribute__((address_space(4))) int32_t cint;   // read with scalar loads
+
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 // Keys per tile: two halves of 16, whose score products are separate
@@ -108,12 +110,14 @@ __device__ __forceinline__ uint4 widen8_impl(const uint2& c) {
                     Fp8Pair<T>::template decode<false>(c.y), Fp8Pair<T>::template decode<true>(c.y));
 }
 
+// kWB: blocks of at least 512 / D tokens, so that the rows a wave loads
+// for one chunk of a tile lie in one block (see the tile loads).
 // kPrefix = false: causal chunked prefill, blockIdx.z = sequence.
 // kPrefix = true: attention of every member's query over its group's shared
 // prefix (no mask; all prefix positions precede the query), blockIdx.z =
 // group, blockIdx.x = row block * splits + key range; writes float states
 // instead of the output.
-template <typename T, int D, bool kPrefix, bool kF8 = false>
+template <typename T, int D, bool kPrefix, bool kF8, bool kWB>
 // Two workgroups per compute unit (one for D = 256, whose accumulator would
 // not fit): this also keeps the MFMA accumulators in ordinary vector
 // registers (with a looser bound the compiler places them in the
@@ -304,6 +308,24 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     // tile loaded last did.
     int bad = 0, bad_ld = 0;
     KvReg kreg[CPT], vreg[CPT];
+    // Chunk u of a tile is row c / LPR, channels 8 * (c % LPR) .. +7, read
+    // from position t = min(32 kt + row, L - 1) (rows past the history read
+    // a written position, whose values the mask discards): in the pools at
+    // byte blk * blk_bytes + (t mod B) * tok_bytes + lane_off.  A block's
+    // bytes stay below 2^32 (at most 128 * 65535 * 256 * 2), so only the
+    // block's own offset needs 64 bits.
+    const uint64_t tok_bytes = (uint64_t)p.num_kv_heads * D * KVB;
+    const uint64_t blk_bytes = tok_bytes << p.log2_b;
+    const int bmask = (1 << p.log2_b) - 1;
+    const uint32_t lane_off = (uint32_t)(kvh * D + 8 * (lane % LPR)) * KVB;
+    // A wave's lanes cover RPW consecutive rows of each chunk, starting at a
+    // multiple of RPW; with B >= RPW (kWB) they lie in one block, whose id is
+    // then uniform over the wave: a scalar load, and loads addressed as a
+    // scalar base plus a 32-bit lane offset.  Smaller blocks take per-lane
+    // ids.
+    constexpr int RPW = 64 / LPR;
+    static_assert(64 % LPR == 0, "lane layout");
+    auto wave_row0 = [&](int u) { return (64 * w + kThreads * u) / LPR; };
     // Block ids of the tile loaded next, fetched one tile ahead of its data
     // so that the data loads never wait for them.
     int blk_nx[CPT];
@@ -311,8 +333,12 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     auto load_ids = [&](int kt) {
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
-        const int c = tid + kThreads * u;
-        blk_nx[u] = (NCH % kThreads == 0 || c < NCH) ? trow[chunk_pos(kt, c) >> p.log2_b] : 0;
+        if (NCH % kThreads == 0 || 64 * w + kThreads * u < NCH) {
+          if constexpr (kWB)
+            blk_nx[u] = ((cint*)trow)[min(kt * kTile + wave_row0(u), L - 1) >> p.log2_b];
+          else
+            blk_nx[u] = trow[chunk_pos(kt, tid + kThreads * u) >> p.log2_b];
+        }
       }
     };
     auto load_tile = [&](int kt) {
@@ -320,22 +346,21 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
 #pragma unroll
       for (int u = 0; u < CPT; ++u) {
         const int c = tid + kThreads * u;
-        if (NCH % kThreads == 0 || c < NCH) {
-          const int ch = c % LPR;
-          const int t = chunk_pos(kt, c);
+        if (NCH % kThreads == 0 || 64 * w + kThreads * u < NCH) {
+          const uint32_t off =
+              (uint32_t)(chunk_pos(kt, c) & bmask) * (uint32_t)tok_bytes + lane_off;
           int blk = blk_nx[u];
           if (!valid_block(blk, p.num_blocks)) {
             bad_ld = 1;
             blk = 0;
           }
-          const size_t off =
-              row_offset(blk, t, p.log2_b, p.num_kv_heads, kvh, D) * KVB + ch * 8 * KVB;
+          const uint64_t boff = (uint64_t)(uint32_t)blk * blk_bytes;
           if constexpr (kF8) {
-            kreg[u] = *reinterpret_cast<const uint2*>(p.k_pool + off);
-            vreg[u] = *reinterpret_cast<const uint2*>(p.v_pool + off);
+            kreg[u] = *reinterpret_cast<const uint2*>(p.k_pool + boff + off);
+            vreg[u] = *reinterpret_cast<const uint2*>(p.v_pool + boff + off);
           } else {
-            kreg[u] = load16(p.k_pool + off);
-            vreg[u] = load16(p.v_pool + off);
+            kreg[u] = load16(p.k_pool + boff + off);
+            vreg[u] = load16(p.v_pool + boff + off);
           }
         }
       }
@@ -503,23 +528,24 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
   }
 }
 
+template <typename T, int D, bool kPrefix, bool kF8>
+void launch_prefill_d(const PrefillParams& p, dim3 grid, hipStream_t st) {
+  // Blocks of at least 512 / D tokens: a wave's rows of a chunk share a block.
+  if ((1 << p.log2_b) * D >= 512)
+    hipLaunchKernelGGL((attn_prefill_mfma<T, D, kPrefix, kF8, true>), grid, dim3(kThreads), 0, st,
+                       p);
+  else
+    hipLaunchKernelGGL((attn_prefill_mfma<T, D, kPrefix, kF8, false>), grid, dim3(kThreads), 0,
+                       st, p);
+}
+
 template <typename T, bool kPrefix, bool kF8>
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, dim3 grid, hipStream_t st) {
   switch (head_dim) {
-    case 32:
-      hipLaunchKernelGGL((attn_prefill_mfma<T, 32, kPrefix, kF8>), grid, dim3(kThreads), 0, st, p);
-      break;
-    case 64:
-      hipLaunchKernelGGL((attn_prefill_mfma<T, 64, kPrefix, kF8>), grid, dim3(kThreads), 0, st, p);
-      break;
-    case 128:
-      hipLaunchKernelGGL((attn_prefill_mfma<T, 128, kPrefix, kF8>), grid, dim3(kThreads), 0, st,
-                         p);
-      break;
-    default:
-      hipLaunchKernelGGL((attn_prefill_mfma<T, 256, kPrefix, kF8>), grid, dim3(kThreads), 0, st,
-                         p);
-      break;
+    case 32: launch_prefill_d<T, 32, kPrefix, kF8>(p, grid, st); break;
+    case 64: launch_prefill_d<T, 64, kPrefix, kF8>(p, grid, st); break;
+    case 128: launch_prefill_d<T, 128, kPrefix, kF8>(p, grid, st); break;
+    default: launch_prefill_d<T, 256, kPrefix, kF8>(p, grid, st); break;
   }
   return hipGetLastError();
 }

@@ -170,7 +170,8 @@ def test_cascade_full_size_config4_sampled():
     (12, 2, 16, 40, 400),     # g = 6: members straddle 64-row blocks; 4 row blocks
     (32, 8, 8, 70, 200),      # block size 8, 25 prefix blocks, 5 row blocks
     (32, 8, 32, 30, 512),     # block size 32
-    (16, 16, 4, 9, 36),       # block size 4: the prefix ends inside a 16-token tile
+    (16, 16, 4, 9, 36),       # block size 4: the prefix ends inside a 32-token tile
+    (16, 4, 2, 12, 62),       # block size 2: per-lane block ids in the prefix loads
 ])
 def test_cascade_key_ranges_and_row_blocks(hq, hkv, bs, batch, prefix_tokens):
     """Prefix states split into several key ranges (some empty when the prefix

@@ -261,6 +261,7 @@ FP8_PREFILL_CASES = [
     (8, 2, 64, 8, "f16", [100, 37, 250], [100, 37, 17]),
     (6, 3, 128, 4, "bf16", [50, 123], [50, 1]),
     (16, 2, 256, 16, "f16", [200, 33], [70, 33]),
+    (8, 2, 128, 2, "bf16", [70, 9], [30, 9]),   # per-lane block ids
 ]
 
 

@@ -105,6 +105,11 @@ PREFILL_CASES = [
     (4, 4, 32, 32, "bf16", [90, 3, 257], [45, 3, 256]),
     (16, 2, 256, 16, "f16", [200, 33], [70, 33]),
     (6, 3, 128, 4, "bf16", [50, 123], [50, 1]),
+    # blocks smaller than 512 / D tokens: per-lane block ids in the tile loads
+    (8, 2, 128, 2, "bf16", [70, 9], [30, 9]),
+    (4, 2, 64, 4, "f16", [45, 20], [45, 7]),
+    (4, 1, 32, 8, "bf16", [33, 5], [10, 5]),
+    (4, 2, 128, 1, "f16", [19, 4], [7, 4]),
 ]
 
 
