@@ -446,25 +446,37 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
               if (16 * (e >> 2) + (e & 3) > lim) sc[e >> 2][rg][e & 3] = -INFINITY;
           }
         }
-        uint4 pop[kRG];
+        // Row maxima of both groups first, then one wave-uniform rescale
+        // branch for both: the exps and the P.V products after it form one
+        // straight stretch in which one group's MFMAs can overlap the other
+        // group's vector work.
+        float mt[kRG];
+        bool jump = false;
 #pragma unroll
         for (int rg = 0; rg < kRG; ++rg) {
-          float mt = -INFINITY;
+          float x = -INFINITY;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) mt = fmaxf(mt, sc[e >> 2][rg][e & 3]);
+          for (int e = 0; e < 8; ++e) x = fmaxf(x, sc[e >> 2][rg][e & 3]);
           // The scale is positive, so the maximum of the raw scores scales.
-          mt = max_xor32(max_xor16(mt)) * p.scale_log2;
-          // Every row's first tile holds a visible key, so m_run is finite
-          // from then on (rows past the chunk stay at -inf and are never
-          // written).
-          if (__any(mt > m_run[rg] + kRescaleThreshold)) {
-            const float mn = fmaxf(m_run[rg], mt);
+          mt[rg] = max_xor32(max_xor16(x)) * p.scale_log2;
+          jump |= mt[rg] > m_run[rg] + kRescaleThreshold;
+        }
+        // Every row's first tile holds a visible key, so m_run is finite from
+        // then on (rows past the chunk stay at -inf and are never written).
+        if (__any(jump)) {
+#pragma unroll
+          for (int rg = 0; rg < kRG; ++rg) {
+            const float mn = fmaxf(m_run[rg], mt[rg]);
             const float alpha = mn == -INFINITY ? 1.f : fast_exp2(m_run[rg] - mn);
             m_run[rg] = mn;
             l_acc[rg] *= alpha;
 #pragma unroll
             for (int j = 0; j < D / 16; ++j) acc[rg][j] *= alpha;
           }
+        }
+        uint4 pop[kRG];
+#pragma unroll
+        for (int rg = 0; rg < kRG; ++rg) {
           // Weights exp2(scale * s - m), rounded to the element type (0 for
           // masked keys; a row with no visible key yet subtracts 0).  B
           // operand of the P.V product: k index 8*kgrp + e is key 4*kgrp + e
