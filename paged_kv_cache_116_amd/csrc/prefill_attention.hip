@@ -24,18 +24,19 @@
 // used); every wave reads the shared tiles.  Per wave and tile:
 //   S^T[16 keys x 16 rows] = K . Q^T   for each 16-key half
 //                                      (D/32 v_mfma_f32_16x16x32 each)
-//   causal mask per row, one running max over the 32 keys with lazy
-//   rescale, exp2
+//   causal mask per row (on tiles that reach past a row's position), one
+//   running max over the 32 keys with lazy rescale, exp2
 //   O^T[D x 16 rows] += V^T . P^T      (D/16 v_mfma_f32_16x16x32 over all
 //                                       32 keys; P stays in registers, V^T
 //                                       comes from transposing LDS reads)
+//   l[16 rows] += 1 . P^T               (one more MFMA: the row sums)
 // Row blocks are taken from the last (heaviest) one down; workgroups loop
 // over further row blocks with stride gridDim.x, so any grid width covers
 // every chunk.
 //
 // Shared-prefix mode (for the cascade decode): the rows are (member, query
 // head) pairs of a group whose members share their first blocks; every row
-// sees the whole prefix, so nothing is masked.  The prefix's tiles are split
+// sees the whole prefix, so only keys past its end are masked.  The prefix's tiles are split
 // into `splits` contiguous key ranges, one per workgroup, each producing a
 // normalised state and its log normaliser; the cascade's combine step merges
 // them with the suffix result by the log-sum-exp rule.
@@ -114,7 +115,7 @@ __device__ __forceinline__ uint4 widen8_impl(const uint2& c) {
 // for one chunk of a tile lie in one block (see the tile loads).
 // kPrefix = false: causal chunked prefill, blockIdx.z = sequence.
 // kPrefix = true: attention of every member's query over its group's shared
-// prefix (no mask; all prefix positions precede the query), blockIdx.z =
+// prefix (no causal mask; all prefix positions precede the query), blockIdx.z =
 // group, blockIdx.x = row block * splits + key range; writes float states
 // instead of the output.
 template <typename T, int D, bool kPrefix, bool kF8, bool kWB>
