@@ -40,7 +40,13 @@ Modules:
 
 Every function in this package is pinned by a ``-m "not gpu"`` test against
 values printed on the pages, closed forms, brute force or an independent
-library routine; none is "parity unpinned".
+library routine.  The FP8 scale convention (a code stands for
+decode(code) * scale) is a reading, not a page's statement; it is pinned by
+the round trip that any scale convention must satisfy (a stored code gives
+back the value it was written for, within half an E4M3 step, at scales other
+than 1), which an inverted scale fails.  Planted mistakes in each function
+(wrong index, sign, term, operand, rounding, order or threshold) were checked
+to fail at least one pin.
 """
 
 from . import paging, attention, cache_ops, block_manager, allocator_toy, fp8  # noqa: F401

@@ -5,8 +5,8 @@ Test infrastructure only; see the package docstring for who may use it.
 [lesson] "Developer — The allocator, both strategies" runs four requests,
 each a (prompt tokens, generated tokens) pair, through two allocators on a
 pool of 64 blocks of 16 slots and prints what each one holds.  The functions
-here recompute those quantities: the contiguous one from the reservation
-rule, the paged one by driving :class:`oracle.block_manager.OracleSequence`
+here recompute those quantities: the contiguous one in closed form from the
+reservation rule (not by replaying the page's loop), the paged one by driving :class:`oracle.block_manager.OracleSequence`
 (prompt blocks at admission, one more block whenever the last fills), so that
 the page's printed numbers pin the block manager's allocation rule.
 """
@@ -17,23 +17,27 @@ from .block_manager import NoFreeBlock, OracleBlockPool, OracleSequence
 
 
 def contiguous_reservation(requests: dict, pool_slots: int, max_len: int) -> dict:
-    """Each request reserves ``max_len`` slots if they still fit, else it is
-    rejected.  Returns per-request (reserved, used, wasted) and the totals."""
-    used_slots = 0
+    """Reservation rule: every request asks for the same ``max_len`` slots, so
+    in arrival order the first ``pool_slots // max_len`` requests fit and the
+    rest are turned away.  A served request wastes ``max_len`` minus the
+    tokens it ends up holding (prompt + generated); the pool's waste is the
+    share of the reserved slots that hold no token.  Returns per-request
+    (reserved, used, wasted), or the free slots a rejected request found, and
+    the totals."""
+    names = list(requests)
+    admitted = names[:min(len(names), pool_slots // max_len)]
+    reserved = len(admitted) * max_len
+    used = {n: requests[n][0] + requests[n][1] for n in names}
     per_request = {}
-    served = []
-    for name, (prompt, gen) in requests.items():
-        if used_slots + max_len <= pool_slots:
-            used_slots += max_len
-            served.append(name)
-            per_request[name] = {"reserved": max_len, "used": prompt + gen,
-                                 "wasted": max_len - (prompt + gen)}
+    for n in names:
+        if n in admitted:
+            per_request[n] = {"reserved": max_len, "used": used[n], "wasted": max_len - used[n]}
         else:
-            per_request[name] = {"rejected": True, "free_slots": pool_slots - used_slots}
-    needed = sum(p + g for n, (p, g) in requests.items() if n in served)
-    return {"per_request": per_request, "served": len(served), "reserved": used_slots,
-            "needed": needed,
-            "waste_pct": 100.0 * (used_slots - needed) / used_slots if used_slots else 0.0}
+            per_request[n] = {"rejected": True, "free_slots": pool_slots - reserved}
+    needed = sum(used[n] for n in admitted)
+    waste_pct = 100.0 * (1.0 - needed / reserved) if reserved else 0.0
+    return {"per_request": per_request, "served": len(admitted), "reserved": reserved,
+            "needed": needed, "waste_pct": waste_pct}
 
 
 def paged_on_demand(requests: dict, pool_blocks: int, block_size: int) -> dict:

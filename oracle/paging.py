@@ -10,8 +10,6 @@ per-layer slice of [pofe] "Minimal implementation" (``BlockPool.k``).
 
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 
@@ -128,6 +126,3 @@ def utilisation_reserve(mean_len: float, s_max: int) -> float:
     """Utilisation under per-request reservation of S_max: mean / S_max."""
     return mean_len / s_max
 
-
-def ceil_div(a: int, b: int) -> int:
-    return int(math.ceil(a / b))

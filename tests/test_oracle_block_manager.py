@@ -47,6 +47,18 @@ def test_lesson_toy_contiguous_and_paged():
     assert round(p["waste_pct"]) == g["paged"]["waste_pct_rounded"]
     assert p["free_blocks"] == g["paged"]["free_blocks"]
 
+    # The reservation rule at other pool sizes: a pool one slot short of
+    # four reservations serves three and shows the fourth the slots left; a
+    # bigger pool serves all four and wastes the same share of what they
+    # reserved (the unreserved slots are free, not wasted).
+    short = allocator_toy.contiguous_reservation(reqs, 4 * g["max_len"] - 1, g["max_len"])
+    assert short["served"] == 3 and short["reserved"] == 3 * g["max_len"]
+    assert short["per_request"]["r4"] == {"rejected": True, "free_slots": g["max_len"] - 1}
+    assert short["needed"] == 52 + 20 + 135
+    big = allocator_toy.contiguous_reservation(reqs, 10 * g["max_len"], g["max_len"])
+    assert big["served"] == 4 and big["reserved"] == 4 * g["max_len"]
+    assert round(big["waste_pct"]) == g["contiguous"]["waste_pct_rounded"]
+
     s = allocator_toy.shared_prompt(g["sharing"]["sys_tokens"], g["sharing"]["users"],
                                     g["block_size"])
     for key in ("copied_blocks", "shared_blocks", "refcount", "saved_slots"):
@@ -65,6 +77,28 @@ def test_arch_driver_shared_prefix_refcount():
     assert r1.table[0] == r2.table[0] and r1.table[1] != r2.table[1]
     assert pool.ref[r1.table[0]] == g["shared_prefix_refcount"]
     assert len(r1.table) == len(r2.table) == 2
+
+
+def test_adopt_and_extend_count_exactly():
+    # Adopting k full blocks adds one reference to each of those k blocks and
+    # to no other; extending to a block-aligned length takes exactly the
+    # blocks that length needs (ceil(len / B)); freeing every sequence gives
+    # every block back ([note] "Useful allocator invariants").
+    pool = OracleBlockPool(16, 4)
+    src = OracleSequence(pool)
+    src.reserve_prompt(14)                       # 4 blocks, the last one half full
+    dst = OracleSequence(pool)
+    dst.adopt_prefix(src, 2)
+    assert [pool.ref[i] for i in src.table] == [2, 2, 1, 1]
+    assert dst.table == src.table[:2] and dst.len == 8
+    dst.extend_prompt(8)                         # 16 tokens: exactly 4 blocks
+    assert len(dst.table) == 4 and dst.len == 16
+    assert pool.num_free() == 16 - 4 - 2
+    dst.extend_prompt(1)                         # 17 tokens: a fifth block
+    assert len(dst.table) == 5
+    for seq in (src, dst):
+        seq.free_all()
+    assert pool.num_free() == 16 and all(r == 0 for r in pool.ref)
 
 
 def test_copy_on_write_first_appender_copies():

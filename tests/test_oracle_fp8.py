@@ -75,12 +75,86 @@ def test_encode_is_nearest_by_brute_force():
         assert abs(fp8.decode_e4m3(c) - min(max(v, -448), 448)) == best
 
 
+def e4m3_half_step(y: float) -> float:
+    """Half the spacing of E4M3FN values around |y| (|y| <= 448), from the field
+    layout: 3 mantissa bits, so normal numbers in [2^e, 2^(e+1)) are 2^(e-3)
+    apart; below 2^-6 (subnormals) the spacing is 2^-9."""
+    a = abs(y)
+    if a < 2.0 ** -6:
+        return 2.0 ** -10
+    return 2.0 ** (math.floor(math.log2(a)) - 4)
+
+
+SCALES = (0.05, 0.0625, 0.125, 0.7, 3.0)
+
+
+def scale_convention_holds(quantise, dequantise) -> bool:
+    """The scale reading: a code stands for decode(code) * scale, and the code
+    stored for x is the nearest one to x / scale.  Checked without the
+    oracle's formulas: (1) the code of 1.0 (0x38) stands for the scale itself;
+    (2) every finite code survives dequantise -> quantise unchanged; (3) an
+    in-range x comes back within half an E4M3 step of x / scale, times the
+    scale (the closed-form rounding bound)."""
+    rng = np.random.default_rng(17)
+    finite = [c for c in range(256) if not math.isnan(fp8.decode_e4m3(c))]
+    for s in SCALES:
+        s32 = float(np.float32(s))
+        if dequantise(np.array([0x38], np.uint8), s)[0] != s32:
+            return False
+        codes = np.array(finite, np.uint8)
+        if not np.array_equal(quantise(dequantise(codes, s), s), codes):
+            return False
+        x = (rng.uniform(-440, 440, 400) * s32).astype(np.float32)
+        back = dequantise(quantise(x, s), s)
+        for xi, bi in zip(x.astype(np.float64), back):
+            y = xi / s32
+            if abs(bi - xi) > e4m3_half_step(y) * s32 * (1 + 1e-6) + 1e-30:
+                return False
+    return True
+
+
+def test_scale_convention_round_trip():
+    # [pofe] "Fine-tuned models and adapters": FP8 changes the bytes per
+    # block and nothing else, so a stored code must give back the value it
+    # was written for, to within the format's rounding, at any scale.
+    assert scale_convention_holds(fp8.quantise, fp8.dequantise)
+
+
+def test_planted_scale_inversion_fails():
+    # A dequantiser that divides by the scale, or a quantiser that multiplies,
+    # must fail the convention pin at non-unit scales.
+    def dequantise_divides(codes, scale):
+        return fp8.DECODE_TABLE[np.asarray(codes, np.uint8)] / np.float64(np.float32(scale))
+
+    def quantise_multiplies(x, scale):
+        return fp8.quantise(np.asarray(x, np.float64) * float(np.float32(scale)) ** 2, scale)
+
+    assert not scale_convention_holds(fp8.quantise, dequantise_divides)
+    assert not scale_convention_holds(quantise_multiplies, fp8.dequantise)
+
+
 def test_quantise_divides_in_float32():
-    x = np.array([1.1, -3.3, 500.0, 0.0], dtype=np.float32)
-    s = 0.7
-    q = fp8.quantise(x, s)
-    for xi, qi in zip(x, q):
-        assert qi == fp8.encode_e4m3(float(np.float32(xi) / np.float32(s)))
+    # torch divides two float32 tensors in float32 and casts with its own
+    # float8_e4m3fn encoder (an independent routine).  The inputs are chosen
+    # so that the float32 quotient lands exactly on a tie between two codes
+    # while the exact quotient does not: a float64 division would pick the
+    # other code.
+    cases = [(2.5823814868927, 2.430476665496826), (3.468320846557617, 2.9206912517547607),
+             (7.949495315551758, 3.740938901901245), (0.01111726462841034, 0.020926615223288536)]
+    for x, s in cases:
+        x32 = torch.tensor([x], dtype=torch.float32)
+        s32 = torch.tensor([s], dtype=torch.float32)
+        ref = (x32 / s32).to(torch.float8_e4m3fn).view(torch.uint8).item()
+        got = int(fp8.quantise(np.array([x], np.float32), s)[0])
+        assert got == ref
+        assert fp8.encode_e4m3(float(np.float64(np.float32(x)) / np.float64(np.float32(s)))) != ref
+    rng = np.random.default_rng(23)
+    for s in SCALES:
+        x = rng.normal(0, 50 * s, 2000).astype(np.float32)
+        ref = (torch.from_numpy(x) / torch.tensor(s, dtype=torch.float32)).to(
+            torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(fp8.quantise(x, s), ref)
+    q = fp8.quantise(np.array([1.1, -3.3, 500.0, 0.0], np.float32), 0.7)
     assert np.array_equal(fp8.dequantise(q, 1.0), fp8.DECODE_TABLE[q])
 
 

@@ -92,6 +92,14 @@ def test_utilisation_bounds():
     assert math.floor(1000 * up) / 10 == a["u_paged_at_least_pct"]
     assert round(100 * ur, 1) == a["u_reserve_pct"]
     assert round(up / ur) == a["batch_gain_about"]
+    # closed forms of the reservation rule: a reservation filled to S_max is
+    # fully used, one filled to half is half used, and the batch figure is
+    # the mean of the per-request utilisations
+    assert paging.utilisation_reserve(4096, 4096) == 1.0
+    assert paging.utilisation_reserve(2048, 4096) == 0.5
+    lens = [37, 1203, 450]
+    assert math.isclose(paging.utilisation_reserve(sum(lens) / 3, 4096),
+                        sum(paging.eta_naive(n, 4096) for n in lens) / 3, rel_tol=1e-15)
     e = g["arch_eta_bound"]
     assert round(100 * paging.eta_paged_lower_bound(e["s"], e["block_size"]), 2) \
         == e["eta_lower_bound_pct"]

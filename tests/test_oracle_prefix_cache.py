@@ -71,6 +71,27 @@ def test_freed_blocks_stay_cached_until_evicted():
         admit_prompt(d, [1, 2, 3, 4])
 
 
+def test_eviction_takes_the_least_recently_released_block():
+    # LRU eviction ([lesson] "Sharing, and the reference counting it needs"
+    # names it): of two cached blocks whose counts fell to 0, an allocation
+    # under pressure evicts the one released first; the other stays hittable.
+    pool = OraclePrefixPool(3, 2)
+    a, b = OracleSequence(pool), OracleSequence(pool)
+    admit_prompt(a, [1, 2])
+    admit_prompt(b, [3, 4])
+    a.free_all()                                  # released first
+    b.free_all()
+    assert pool.num_cached() == 2 and len(pool.free) == 1
+    c = OracleSequence(pool)
+    admit_prompt(c, [7, 7, 8, 8])                 # needs 2 blocks: the free one + one eviction
+    assert pool.num_cached() == 3                  # [3, 4] stayed, [7, 7] and [7, 7, 8, 8] added
+    e = OracleSequence(pool)
+    assert admit_prompt(e, [3, 4]) == 2            # [3, 4] still cached: a hit, revived
+    d = OracleSequence(pool)
+    with pytest.raises(NoFreeBlock):
+        admit_prompt(d, [1, 2])                    # [1, 2] was evicted: no hit, no block left
+
+
 def test_admission_is_all_or_none():
     pool = OraclePrefixPool(3, 2)
     a = OracleSequence(pool)
