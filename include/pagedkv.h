@@ -277,6 +277,35 @@ int paged_decode_step(int kernel, void* out, const void* q, void* k_pool, void* 
                       int head_dim, float scale, int partition_tokens, void* workspace,
                       size_t workspace_bytes, int dtype, void* stream);
 
+/*
+ * paged_decode_step_noalloc - paged_decode_step with no workspace argument and
+ * no allocation, for callers that cannot allocate device memory: work
+ * recorded under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.
+ *
+ * The plan and the partial softmax states live in a library-owned device
+ * array of PKV_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, reserved when the
+ * library's code is loaded on that GPU and held until the process ends; the
+ * first call on a GPU looks up its address there (with that GPU current).
+ * Arguments and results as paged_decode_step (bit for bit the same outputs
+ * and pool writes) without workspace / workspace_bytes.  A call whose
+ * workspace, as paged_decode_step would lay it out, exceeds the array returns
+ * PKV_ERR_WORKSPACE and launches nothing (the five shapes of the benchmark
+ * need at most 35 MiB without a partition cap).  The array keeps what the
+ * last call left; nothing in it needs clearing, since the plan rewrites
+ * every word a call reads.  Every call on one GPU shares that GPU's array:
+ * calls that may overlap in time on one GPU (different streams, no ordering
+ * between them) race and give wrong results; calls queued on one stream, or
+ * otherwise ordered, are safe.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int paged_decode_step_noalloc(int kernel, void* out, const void* q, void* k_pool, void* v_pool,
+                              const void* k_new, const void* v_new, const int32_t* block_tables,
+                              int max_blocks_per_seq, const int32_t* context_lens, int num_seqs,
+                              int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
+                              int head_dim, float scale, int partition_tokens, int dtype,
+                              void* stream);
+
 /* paged_decode_attention_lse - paged_decode_attention_with that also writes
  * the natural log of each head's softmax normaliser:
  *   lse : device float [num_seqs, num_q_heads],

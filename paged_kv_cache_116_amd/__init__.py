@@ -35,6 +35,7 @@ PKV_ERR_HIP = -5
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 PKV_ATTN_AUTO, PKV_ATTN_VALU, PKV_ATTN_MFMA = 0, 1, 2
 PKV_ATTN_CACHE_KV = 16   # flag: blocks shared between sequences (see include/pagedkv.h)
+PKV_NOALLOC_SCRATCH_BYTES = 64 << 20   # per-GPU scratch of paged_decode_step_noalloc
 
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16,
                torch.float8_e4m3fn: PKV_FP8_E4M3}   # FP8: pools only (E4M3FN codes)
@@ -68,6 +69,9 @@ _sig("paged_decode_attention_plan", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_attention_partitions", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_attention_merge", _i32, [_i32] + _ATTN_ARGS)
 _sig("paged_decode_step", _i32, [_i32, _p, _p, _p, _p, _p, _p] + _ATTN_ARGS[4:])
+# The step without workspace / workspace_bytes.
+_sig("paged_decode_step_noalloc", _i32,
+     [_i32, _p, _p, _p, _p, _p, _p] + _ATTN_ARGS[4:15] + _ATTN_ARGS[17:])
 _f32 = ctypes.c_float
 _sig("paged_kv_append_fp8", _i32,
      [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _p])
@@ -304,6 +308,9 @@ def paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_le
                                                  max_context_len, partition_tokens))
 
 
+_NO_WORKSPACE = object()   # _attn_args: the call takes no workspace (nothing is allocated)
+
+
 def _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partition_tokens,
                workspace, stream, io_dtype=None):
     n, b, h, d, dt = _pool_dims(k_pool, v_pool)
@@ -319,14 +326,17 @@ def _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partit
     mb = block_tables.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if workspace is None:
-        need = paged_decode_workspace_bytes(s, hq, d, mb * b, partition_tokens)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev(workspace, "workspace", torch.uint8)
+    if workspace is _NO_WORKSPACE:
+        ws_ptr, ws_bytes = None, 0
+    else:
+        if workspace is None:
+            need = paged_decode_workspace_bytes(s, hq, d, mb * b, partition_tokens)
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        ws_ptr, ws_bytes = _dev(workspace, "workspace", torch.uint8), workspace.numel()
     return (_dev(out, "out", io_dtype), _dev(q, "q", io_dtype), _dev(k_pool, "k_pool"),
             _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32), mb,
             _dev(context_lens, "context_lens", torch.int32), s, n, b, hq, h, d, float(scale),
-            int(partition_tokens), ws_ptr, workspace.numel(), dt, _stream(stream))
+            int(partition_tokens), ws_ptr, ws_bytes, dt, _stream(stream))
 
 
 def paged_decode_attention_plan(kernel, out, q, k_pool, v_pool, block_tables, context_lens, *,
@@ -444,6 +454,23 @@ def paged_decode_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, contex
                                   _dev(k_new, "k_new", k_pool.dtype),
                                   _dev(v_new, "v_new", k_pool.dtype), *args[4:]),
            "paged_decode_step")
+
+
+def paged_decode_step_noalloc(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens, *,
+                              kernel=0, scale=None, partition_tokens=0, stream=None):
+    """paged_decode_step with the library's own per-GPU scratch instead of a
+    workspace: nothing is allocated, here or in the library.  Calls that may
+    overlap in time on one GPU race on that scratch (see the C header)."""
+    args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
+                      partition_tokens, _NO_WORKSPACE, stream)
+    s, h, d = q.shape[0], k_pool.shape[2], k_pool.shape[3]
+    if k_new.shape != (s, h, d) or v_new.shape != (s, h, d):
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    _check(_lib.paged_decode_step_noalloc(int(kernel), args[0], args[1], args[2], args[3],
+                                          _dev(k_new, "k_new", k_pool.dtype),
+                                          _dev(v_new, "v_new", k_pool.dtype), *args[4:15],
+                                          *args[17:]),
+           "paged_decode_step_noalloc")
 
 
 def pkv_validate_tables(block_tables, context_lens, num_blocks: int, block_size: int):

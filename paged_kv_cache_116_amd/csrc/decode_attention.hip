@@ -1531,6 +1531,36 @@ int decode_attention_with_lse(int kernel, void* out, float* lse, const void* q,
                                k_scale, v_scale, lse);
 }
 
+// Workspace of paged_decode_step_noalloc: one copy per GPU, in the code
+// object's zero-filled data, so it exists from when the library loads on a
+// GPU until the process ends.  Host code never passes this name to a
+// kernel (on the host it is only a stand-in): the device address comes from
+// hipGetSymbolAddress, once per GPU.
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current GPU, looked up on the first
+// call there; PKV_OK or PKV_ERR_HIP.
+int noalloc_scratch(void** out) {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> ptrs;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = ptrs.find(dev);
+  if (it == ptrs.end()) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PKV_ERR_HIP;
+    it = ptrs.emplace(dev, p).first;
+  }
+  *out = it->second;
+  return PKV_OK;
+}
+
+}  // namespace
+
 }  // namespace pkv
 
 extern "C" size_t paged_decode_workspace_bytes(int num_seqs, int num_q_heads, int head_dim,
@@ -1639,4 +1669,30 @@ extern "C" int paged_decode_attention_lse(int kernel, float* lse, PKV_ATTN_ARGS)
   if (num_seqs > 0 && !lse) return PKV_ERR_INVALID_ARG;
   return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, PKV_ATTN_PASS, nullptr, nullptr,
                                     false, 1.f, 1.f, lse);
+}
+
+extern "C" int paged_decode_step_noalloc(int kernel, void* out, const void* q, void* k_pool,
+                                         void* v_pool, const void* k_new, const void* v_new,
+                                         const int32_t* block_tables, int max_blocks_per_seq,
+                                         const int32_t* context_lens, int num_seqs,
+                                         int num_blocks, int block_size, int num_q_heads,
+                                         int num_kv_heads, int head_dim, float scale,
+                                         int partition_tokens, int dtype, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) return PKV_ERR_INVALID_ARG;
+  // Validation first: given no workspace, a valid call stops at the
+  // workspace check and launches nothing.
+  int st = pkv::decode_attention_impl(pkv::kPhaseAll, kernel, out, q, k_pool, v_pool,
+                                      block_tables, max_blocks_per_seq, context_lens, num_seqs,
+                                      num_blocks, block_size, num_q_heads, num_kv_heads,
+                                      head_dim, scale, partition_tokens, nullptr, 0, dtype,
+                                      stream, k_new, v_new);
+  if (st != PKV_ERR_WORKSPACE) return st;
+  void* ws = nullptr;
+  st = pkv::noalloc_scratch(&ws);
+  if (st != PKV_OK) return st;
+  return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, out, q, k_pool, v_pool, block_tables,
+                                    max_blocks_per_seq, context_lens, num_seqs, num_blocks,
+                                    block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                                    partition_tokens, ws, PKV_NOALLOC_SCRATCH_BYTES, dtype,
+                                    stream, k_new, v_new);
 }

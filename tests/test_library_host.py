@@ -78,6 +78,31 @@ def test_attention_rejects_bad_arguments(kw, code):
     assert attn(**kw) == code
 
 
+def noalloc(**kw):
+    a = dict(kernel=0, out=FAKE, q=FAKE, k=FAKE, v=FAKE, kn=FAKE, vn=FAKE, tables=FAKE, mb=4,
+             lens=FAKE, s=2, n=16, b=16, hq=8, hkv=2, d=128, scale=0.1, part=0, dt=2,
+             stream=None)
+    a.update(kw)
+    return lib.paged_decode_step_noalloc(a["kernel"], a["out"], a["q"], a["k"], a["v"], a["kn"],
+                                         a["vn"], a["tables"], a["mb"], a["lens"], a["s"], a["n"],
+                                         a["b"], a["hq"], a["hkv"], a["d"], a["scale"], a["part"],
+                                         a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hq=7, hkv=2), pkv.PKV_ERR_INVALID_ARG),
+    (dict(kn=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(d=96), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(part=24), pkv.PKV_ERR_INVALID_ARG),
+    (dict(kernel=64), pkv.PKV_ERR_INVALID_ARG),
+    (dict(s=0), pkv.PKV_OK),                      # nothing to do, nothing touched
+])
+def test_noalloc_step_rejects_bad_arguments_before_the_device(kw, code):
+    # The scratch-free step validates like paged_decode_step and never needs
+    # a GPU to refuse a call.
+    assert noalloc(**kw) == code
+
+
 def test_decode_step_needs_the_new_tokens():
     a = [FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, 2, 16, 16, 8, 2, 128, 0.1, 0, FAKE, 1 << 30, 2, None]
     lib_step = lib.paged_decode_step
