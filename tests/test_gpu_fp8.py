@@ -140,10 +140,14 @@ def test_fp8_decode_step_equals_two_calls(cid):
     assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
 
 
-def test_fp8_full_size_config3_sampled():
-    w = workloads.make_workload(3, device="cuda", kv_fp8=True)
-    rng = np.random.default_rng(3)
-    seqs = sorted(set([int(np.argmax(w.lens))] + rng.choice(w.num_seqs, 4, replace=False).tolist()))
+@pytest.mark.parametrize("cid,block_size", [(2, None), (3, None), (5, 8), (5, 16), (5, 32)])
+def test_fp8_full_size_sampled(cid, block_size):
+    kw = {} if block_size is None else dict(block_size=block_size)
+    w = workloads.make_workload(cid, device="cuda", kv_fp8=True, **kw)
+    rng = np.random.default_rng(cid)
+    nsample = 2 if cid == 5 else 4
+    seqs = sorted(set([int(np.argmax(w.lens))] +
+                      rng.choice(w.num_seqs, nsample, replace=False).tolist()))
     host = workloads.extract_sequences(w, seqs)
     kc, vc = o_fp8.append_token_fp8(host["k_pool"], host["v_pool"], host["k_new"], host["v_new"],
                                     host["tables"], host["lens_pre"], w.block_size, w.k_scale,
@@ -157,7 +161,8 @@ def test_fp8_full_size_config3_sampled():
                               torch.as_tensor(w.lens, device="cuda"), w.k_scale, w.v_scale,
                               scale=w.scale)
     torch.cuda.synchronize()
-    check_close(out[torch.as_tensor(seqs, device="cuda")], ref, f"fp8 full config3 {seqs}")
+    check_close(out[torch.as_tensor(seqs, device="cuda")], ref,
+                f"fp8 full config{cid} B={w.block_size} {seqs}")
     assert torch.isfinite(out.float()).all()
 
 

@@ -484,7 +484,8 @@ def compact_inputs(w, seqs):
 
 @pytest.mark.parametrize("cid,block_size,nsample,cache_kv",
                          [(2, None, 4, False), (3, None, 6, False), (4, None, 4, True),
-                          (4, None, 4, False), (5, 16, 2, False)])
+                          (4, None, 4, False), (5, 16, 2, False), (5, 8, 2, False),
+                          (5, 32, 2, False)])
 def test_full_size_sampled(cid, block_size, nsample, cache_kv):
     # Config 4 shares a prefix: the bench runs it with PKV_ATTN_CACHE_KV.
     kw = {} if block_size is None else dict(block_size=block_size)
@@ -505,6 +506,16 @@ def test_full_size_sampled(cid, block_size, nsample, cache_kv):
                lens=torch.as_tensor(w.lens, device="cuda"),
                lens_pre=torch.as_tensor(w.lens_pre, device="cuda"))
     k = pkv.PKV_ATTN_CACHE_KV if cache_kv else pkv.PKV_ATTN_AUTO
+    # The benchmark's launch (one decode-step call, balanced claims, no
+    # partition cap), then fixed 512-token split-K partitions (append again:
+    # the same bytes into the same slots).
+    out = torch.empty_like(w.q)
+    pkv.paged_decode_step(out, w.q, w.k_pool, w.v_pool, w.k_new, w.v_new, dev["tables"],
+                          dev["lens"], kernel=k, scale=w.scale)
+    torch.cuda.synchronize()
+    label = f"full config{cid} B={w.block_size} seqs={seqs} cache_kv={cache_kv}"
+    check_close(out[sel.cuda()], ref, w.dtype, label + " step")
+    assert torch.isfinite(out.float()).all()
     out = run_step(w, dev, partition_tokens=w.partition_tokens, kernel=k)
-    check_close(out[sel.cuda()], ref, w.dtype, f"full config{cid} seqs={seqs} cache_kv={cache_kv}")
+    check_close(out[sel.cuda()], ref, w.dtype, label + f" P={w.partition_tokens}")
     assert torch.isfinite(out.float()).all()
