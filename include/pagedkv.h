@@ -329,11 +329,19 @@ int paged_decode_attention_lse(int kernel, float* lse, void* out, const void* q,
  * prefix once per group of sequences ([lesson] "Sharing, and the reference
  * counting it needs": sequences with a common prompt prefix share its
  * blocks; [pofe] "Sharing and copy-on-write").  Group z has the members
- * group_members[group_offsets[z] .. group_offsets[z+1]) (device int32), which
- * share their first group_prefix_blocks[z] table entries (the caller's
- * contract; a sequence belongs to at most one group; max_group_size bounds
- * the member counts and only sizes the launch).  Result: the same attention
- * as paged_decode_attention_with, computed as
+ * group_members[group_offsets[z] .. group_offsets[z+1]) (device int32;
+ * group_members holds num_members ids), which share their first
+ * group_prefix_blocks[z] table entries; a sequence belongs to at most one
+ * group; max_group_size bounds the member counts and only sizes the launch.
+ * pkv_bm_export_cascade_groups produces such groups from the block manager
+ * and pkv_validate_cascade_groups checks them on the host.  The kernels
+ * check the contract too, and never read or write outside the buffers for
+ * a broken one: a group whose offsets leave [0, num_members] or decrease is
+ * skipped (its sequences get plain decode attention), member ids outside
+ * [0, num_seqs) are skipped, and a member listed in two groups, whose table
+ * does not start with the group's first member's prefix entries, or whose
+ * group's first member id is outside the batch, gets NaN rows.  Result: the
+ * same attention as paged_decode_attention_with, computed as
  *   - the group's queries against the prefix blocks, read once (matrix
  *     cores, states in float), the prefix split into up to 8 key ranges
  *     (one per 128 table tokens at most) so that the launch fills the GPU;
@@ -350,7 +358,7 @@ int paged_decode_attention_cascade(int kernel, void* out, const void* q, const v
                                    const void* v_pool, const int32_t* block_tables,
                                    int max_blocks_per_seq, const int32_t* context_lens,
                                    int num_seqs, const int32_t* group_offsets,
-                                   const int32_t* group_members,
+                                   const int32_t* group_members, int num_members,
                                    const int32_t* group_prefix_blocks, int num_groups,
                                    int max_group_size, int num_blocks, int block_size,
                                    int num_q_heads, int num_kv_heads, int head_dim, float scale,
@@ -367,7 +375,7 @@ int paged_decode_attention_cascade_fp8(int kernel, void* out, const void* q, con
                                        const void* v_pool, const int32_t* block_tables,
                                        int max_blocks_per_seq, const int32_t* context_lens,
                                        int num_seqs, const int32_t* group_offsets,
-                                       const int32_t* group_members,
+                                       const int32_t* group_members, int num_members,
                                        const int32_t* group_prefix_blocks, int num_groups,
                                        int max_group_size, int num_blocks, int block_size,
                                        int num_q_heads, int num_kv_heads, int head_dim,
@@ -639,6 +647,32 @@ int pkv_bm_seq_table(const pkv_block_manager* bm, int seq, int32_t* out, int cap
 int pkv_bm_export_tables(const pkv_block_manager* bm, const int* seqs, int n, int32_t* out,
                          int ld, int32_t* lens_out);
 
+/* pkv_bm_export_cascade_groups - groups for paged_decode_attention_cascade,
+ * read off the tables of the batch seqs[0..n) (row i = seqs[i], the row
+ * order of pkv_bm_export_tables).  [lesson] "Sharing, and the reference
+ * counting it needs": sequences with a common prompt prefix (forks, prefix
+ * cache hits) hold the same physical blocks for it.  Rows whose first table
+ * entry is the same block form a candidate group, in order of first
+ * appearance; its prefix is the longest run of leading entries all its
+ * members share, cut to the full blocks of its shortest member (a partial
+ * block may still be written).  A candidate with at least min_members rows
+ * (at least 2) and a prefix of at least min_prefix_tokens tokens is written
+ * out: members_out lists its rows (batch row indices, ascending) from
+ * offsets_out[z] to offsets_out[z+1], prefix_blocks_out[z] its prefix
+ * blocks.  Room: offsets_out n + 1 entries, members_out n,
+ * prefix_blocks_out n.  min_prefix_tokens < 0 takes
+ * PKV_CASCADE_MIN_PREFIX_TOKENS.  Rows in no group get plain decode
+ * attention from the cascade. */
+int pkv_bm_export_cascade_groups(const pkv_block_manager* bm, const int* seqs, int n,
+                                 int min_prefix_tokens, int min_members, int32_t* offsets_out,
+                                 int32_t* members_out, int32_t* prefix_blocks_out,
+                                 int* num_groups_out, int* num_members_out);
+
+/* Shortest shared prefix, in tokens, for which the cascade decode beat
+ * plain decode on MI355X (measured; see pkv_cascade_default_min_prefix_tokens). */
+#define PKV_CASCADE_MIN_PREFIX_TOKENS 2048
+int pkv_cascade_default_min_prefix_tokens(void);
+
 /*
  * pkv_validate_tables - host check of the block-id contract of a batch: every
  * entry below ceil(lens[s] / block_size) lies in [0, num_blocks) and fits in the
@@ -648,6 +682,21 @@ int pkv_bm_export_tables(const pkv_block_manager* bm, const int* seqs, int n, in
 int pkv_validate_tables(const int32_t* block_tables, int max_blocks_per_seq,
                         const int32_t* context_lens, int num_seqs, int num_blocks,
                         int block_size, int* bad_seq_out);
+
+/*
+ * pkv_validate_cascade_groups - host check of the group contract of
+ * paged_decode_attention_cascade (host pointers): offsets rise within
+ * [0, num_members]; member ids lie in [0, num_seqs), each in at most one
+ * group; 0 <= group_prefix_blocks[z] <= max_blocks_per_seq; every member is
+ * at least its group's prefix long, and its first group_prefix_blocks[z]
+ * table entries equal the group's first member's.  Returns PKV_OK, or
+ * PKV_ERR_INVALID_ARG and the first bad group in *bad_group_out (may be NULL).
+ */
+int pkv_validate_cascade_groups(const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int num_seqs, int block_size,
+                                const int32_t* group_offsets, const int32_t* group_members,
+                                int num_members, const int32_t* group_prefix_blocks,
+                                int num_groups, int* bad_group_out);
 
 #ifdef __cplusplus
 }

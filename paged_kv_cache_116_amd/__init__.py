@@ -91,11 +91,16 @@ _sig("paged_prefill_attention_fp8", _i32,
 _sig("paged_decode_attention_lse", _i32, [_i32, _p] + _ATTN_ARGS)
 _sig("paged_decode_cascade_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32])
 _sig("paged_decode_attention_cascade", _i32,
-     [_i32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
-      _i32, _f32, _p, _sz, _i32, _p])
+     [_i32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
+      _i32, _i32, _f32, _p, _sz, _i32, _p])
 _sig("paged_decode_attention_cascade_fp8", _i32,
-     [_i32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32,
-      _i32, _f32, _f32, _f32, _p, _sz, _i32, _p])
+     [_i32, _p, _p, _p, _p, _p, _i32, _p, _i32, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32,
+      _i32, _i32, _f32, _f32, _f32, _p, _sz, _i32, _p])
+_sig("pkv_validate_cascade_groups", _i32,
+     [_p, _i32, _p, _i32, _i32, _p, _p, _i32, _p, _i32, _intp])
+_sig("pkv_bm_export_cascade_groups", _i32,
+     [_p, _p, _i32, _i32, _i32, _p, _p, _p, _intp, _intp])
+_sig("pkv_cascade_default_min_prefix_tokens", _i32, [])
 _sig("paged_kv_swap_out", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("paged_kv_swap_in", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("pkv_bm_seq_swap_out", _i32, [_p, _i32, _p, _i32, _intp])
@@ -430,7 +435,7 @@ def paged_decode_attention_cascade(out, q, k_pool, v_pool, block_tables, context
         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32), mb,
         _dev(context_lens, "context_lens", torch.int32), s,
         _dev(group_offsets, "group_offsets", torch.int32),
-        _dev(group_members, "group_members", torch.int32),
+        _dev(group_members, "group_members", torch.int32), group_members.shape[0],
         _dev(group_prefix_blocks, "group_prefix_blocks", torch.int32), g, int(max_group_size),
         n, b, hq, h, d, float(scale), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
         dt, _stream(stream)), "paged_decode_attention_cascade")
@@ -471,6 +476,34 @@ def paged_decode_step_noalloc(out, q, k_pool, v_pool, k_new, v_new, block_tables
                                           _dev(v_new, "v_new", k_pool.dtype), *args[4:15],
                                           *args[17:]),
            "paged_decode_step_noalloc")
+
+
+def pkv_validate_cascade_groups(block_tables, context_lens, block_size: int, group_offsets,
+                                group_members, group_prefix_blocks):
+    """Host check of the cascade's group contract (see the C header); returns
+    the first bad group or -1."""
+    bt = torch.as_tensor(block_tables, dtype=torch.int32).contiguous()
+    ln = torch.as_tensor(context_lens, dtype=torch.int32).contiguous()
+    go = torch.as_tensor(group_offsets, dtype=torch.int32).contiguous()
+    gm = torch.as_tensor(group_members, dtype=torch.int32).contiguous()
+    gp = torch.as_tensor(group_prefix_blocks, dtype=torch.int32).contiguous()
+    if any(t.is_cuda for t in (bt, ln, go, gm, gp)):
+        raise ValueError("pkv_validate_cascade_groups takes host arrays")
+    if go.numel() != gp.numel() + 1:
+        raise ValueError("group_offsets [G + 1], group_prefix_blocks [G]")
+    bad = ctypes.c_int(-1)
+    st = _lib.pkv_validate_cascade_groups(bt.data_ptr(), bt.shape[1], ln.data_ptr(), bt.shape[0],
+                                          block_size, go.data_ptr(), gm.data_ptr(), gm.numel(),
+                                          gp.data_ptr(), gp.numel(), ctypes.byref(bad))
+    if st == PKV_OK:
+        return -1
+    if bad.value < 0:
+        _check(st, "pkv_validate_cascade_groups")
+    return bad.value
+
+
+def pkv_cascade_default_min_prefix_tokens() -> int:
+    return _lib.pkv_cascade_default_min_prefix_tokens()
 
 
 def pkv_validate_tables(block_tables, context_lens, num_blocks: int, block_size: int):
@@ -626,6 +659,24 @@ class BlockManager:
                                          lens.data_ptr()), "pkv_bm_export_tables")
         return out, lens
 
+    def export_cascade_groups(self, seqs, min_prefix_tokens: int = -1, min_members: int = 2):
+        """(offsets [G + 1], members [M], prefix_blocks [G]) int32 CPU tensors: the
+        shared-prefix groups of the batch seqs (row i = seqs[i]); members are
+        batch rows.  min_prefix_tokens < 0 takes the library's measured
+        crossover."""
+        ids = torch.as_tensor(list(seqs), dtype=torch.int32)
+        n = ids.numel()
+        offsets = torch.zeros(n + 1, dtype=torch.int32)
+        members = torch.zeros(max(n, 1), dtype=torch.int32)
+        prefix = torch.zeros(max(n, 1), dtype=torch.int32)
+        ng, nm = ctypes.c_int(0), ctypes.c_int(0)
+        _check(_lib.pkv_bm_export_cascade_groups(
+            self._h, ids.data_ptr(), n, int(min_prefix_tokens), int(min_members),
+            offsets.data_ptr(), members.data_ptr(), prefix.data_ptr(), ctypes.byref(ng),
+            ctypes.byref(nm)), "pkv_bm_export_cascade_groups")
+        return (offsets[: ng.value + 1].clone(), members[: nm.value].clone(),
+                prefix[: ng.value].clone())
+
 
 # --- FP8 (E4M3FN) pools -----------------------------------------------------------
 
@@ -769,7 +820,7 @@ def paged_decode_attention_cascade_fp8(out, q, k_pool, v_pool, block_tables, con
         _dev(v_pool, "v_pool"), _dev(block_tables, "block_tables", torch.int32), mb,
         _dev(context_lens, "context_lens", torch.int32), s,
         _dev(group_offsets, "group_offsets", torch.int32),
-        _dev(group_members, "group_members", torch.int32),
+        _dev(group_members, "group_members", torch.int32), group_members.shape[0],
         _dev(group_prefix_blocks, "group_prefix_blocks", torch.int32), g, int(max_group_size),
         n, b, hq, h, d, float(scale), float(k_scale), float(v_scale),
         _dev(workspace, "workspace", torch.uint8), workspace.numel(), _DTYPE_CODE[q.dtype],

@@ -47,13 +47,34 @@ int prefix_split_cap(int max_blocks, int block_size) {
 
 // Suffix tables start as copies of the tables (sequences outside every group
 // keep their whole history); the prefix kernel then rewrites the members'.
+// The membership counts start at zero.
 __global__ __launch_bounds__(kThreads) void cascade_tables(const int32_t* __restrict__ tables,
                                                            const int32_t* __restrict__ lens,
                                                            int mb, int32_t* __restrict__ suf_tables,
-                                                           int32_t* __restrict__ suf_lens) {
+                                                           int32_t* __restrict__ suf_lens,
+                                                           int32_t* __restrict__ owners) {
   const size_t row = (size_t)blockIdx.x * mb;
   for (int j = threadIdx.x; j < mb; j += kThreads) suf_tables[row + j] = tables[row + j];
-  if (threadIdx.x == 0) suf_lens[blockIdx.x] = lens[blockIdx.x];
+  if (threadIdx.x == 0) {
+    suf_lens[blockIdx.x] = lens[blockIdx.x];
+    owners[blockIdx.x] = 0;
+  }
+}
+
+// Workgroup z counts the groups each member of group z belongs to.  Only a
+// group whose offsets lie in [0, num_members] and do not decrease counts, and
+// only its member ids in [0, num_seqs); the prefix kernel skips the rest.
+__global__ __launch_bounds__(kThreads) void cascade_count(const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ members,
+                                                          int num_members, int num_seqs,
+                                                          int32_t* __restrict__ owners) {
+  const int lo = offsets[blockIdx.x];
+  const int hi = offsets[blockIdx.x + 1];
+  if (lo < 0 || hi < lo || hi > num_members) return;
+  for (int m = lo + (int)threadIdx.x; m < hi; m += kThreads) {
+    const int s = members[m];
+    if (s >= 0 && s < num_seqs) atomicAdd(&owners[s], 1);
+  }
 }
 
 // out[s] = combination of the prefix states of `splits` key ranges (o_pre,
@@ -65,13 +86,19 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void cascade_combine(
     void* __restrict__ out, const float* __restrict__ o_pre, const float* __restrict__ lse_pre,
     const float* __restrict__ lse_suf, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ members, int num_q_heads, int head_dim, int splits,
-    size_t state_stride) {
+    const int32_t* __restrict__ members, int num_members, int num_seqs, int num_q_heads,
+    int head_dim, int splits, size_t state_stride) {
   using S = typename T::storage;
   const int z = blockIdx.x;
   const int row = num_q_heads * head_dim;
-  for (int m = offsets[z] + (int)blockIdx.y; m < offsets[z + 1]; m += gridDim.y) {
+  // The group and member checks of cascade_count: a group outside
+  // [0, num_members] and member ids outside [0, num_seqs) are skipped.
+  const int lo = offsets[z];
+  const int hi = offsets[z + 1];
+  if (lo < 0 || hi < lo || hi > num_members) return;
+  for (int m = lo + (int)blockIdx.y; m < hi; m += gridDim.y) {
     const int s = members[m];
+    if (s < 0 || s >= num_seqs) continue;
     S* o = (S*)out + (size_t)s * row;
     for (int c = threadIdx.x; c < row / 8; c += kThreads) {
       const int h = (8 * c) / head_dim;
@@ -129,11 +156,11 @@ __global__ __launch_bounds__(kThreads) void cascade_combine(
   }
 }
 
-// Workspace of the cascade: suffix tables and lengths, prefix states of up
-// to prefix_split_cap key ranges, the two log-normaliser arrays, then the
-// decode workspace.
+// Workspace of the cascade: suffix tables and lengths, membership counts,
+// prefix states of up to prefix_split_cap key ranges, the two log-normaliser
+// arrays, then the decode workspace.
 struct CascadeWs {
-  size_t tables, lens, o_pre, lse_pre, lse_suf, decode, total;
+  size_t tables, lens, owners, o_pre, lse_pre, lse_suf, decode, total;
 };
 CascadeWs cascade_layout(int num_seqs, int num_q_heads, int head_dim, int max_blocks,
                          int block_size) {
@@ -142,7 +169,8 @@ CascadeWs cascade_layout(int num_seqs, int num_q_heads, int head_dim, int max_bl
   const size_t R = (size_t)prefix_split_cap(max_blocks, block_size);
   w.tables = 0;
   w.lens = w.tables + align256(S * max_blocks * 4);
-  w.o_pre = w.lens + align256(S * 4);
+  w.owners = w.lens + align256(S * 4);
+  w.o_pre = w.owners + align256(S * 4);
   w.lse_pre = w.o_pre + align256(R * S * num_q_heads * head_dim * 4);
   w.lse_suf = w.lse_pre + align256(R * S * num_q_heads * 4);
   w.decode = w.lse_suf + align256(S * num_q_heads * 4);
@@ -175,16 +203,19 @@ namespace {
 int cascade_impl(int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
                  const int32_t* block_tables, int max_blocks_per_seq,
                  const int32_t* context_lens, int num_seqs, const int32_t* group_offsets,
-                 const int32_t* group_members, const int32_t* group_prefix_blocks,
-                 int num_groups, int max_group_size, int num_blocks, int block_size,
+                 const int32_t* group_members, int num_members,
+                 const int32_t* group_prefix_blocks, int num_groups, int max_group_size,
+                 int num_blocks, int block_size,
                  int num_q_heads, int num_kv_heads, int head_dim, float scale, void* workspace,
                  size_t workspace_bytes, int dtype, void* stream, bool kv_fp8, float k_scale,
                  float v_scale) {
   if (dtype != PKV_F16 && dtype != PKV_BF16) return PKV_ERR_UNSUPPORTED;
   if (head_dim % 32 != 0 || !supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
-  if (num_groups < 0 || num_groups > 65535 || max_group_size < 0 || num_seqs < 0)
+  if (num_groups < 0 || num_groups > 65535 || max_group_size < 0 || num_seqs < 0 ||
+      num_members < 0)
     return PKV_ERR_INVALID_ARG;
-  if (num_groups > 0 && (!group_offsets || !group_members || !group_prefix_blocks))
+  if (num_groups > 0 &&
+      (!group_offsets || !group_prefix_blocks || (num_members > 0 && !group_members)))
     return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
   if (max_blocks_per_seq < 1 || num_q_heads < 1 || num_kv_heads < 1 ||
@@ -197,6 +228,7 @@ int cascade_impl(int kernel, void* out, const void* q, const void* k_pool, const
   char* ws = (char*)workspace;
   int32_t* suf_tables = (int32_t*)(ws + w.tables);
   int32_t* suf_lens = (int32_t*)(ws + w.lens);
+  int32_t* owners = (int32_t*)(ws + w.owners);
   float* o_pre = (float*)(ws + w.o_pre);
   float* lse_pre = (float*)(ws + w.lse_pre);
   float* lse_suf = (float*)(ws + w.lse_suf);
@@ -211,7 +243,10 @@ int cascade_impl(int kernel, void* out, const void* q, const void* k_pool, const
   }
   hipStream_t hs = (hipStream_t)stream;
   hipLaunchKernelGGL(cascade_tables, dim3(num_seqs), dim3(kThreads), 0, hs, block_tables,
-                     context_lens, max_blocks_per_seq, suf_tables, suf_lens);
+                     context_lens, max_blocks_per_seq, suf_tables, suf_lens, owners);
+  if (num_groups > 0)
+    hipLaunchKernelGGL(cascade_count, dim3(num_groups), dim3(kThreads), 0, hs, group_offsets,
+                       group_members, num_members, num_seqs, owners);
   // Key ranges per prefix: enough workgroups for about four per compute unit
   // (64-row blocks x KV heads x groups x ranges), within the workspace's cap.
   const long long base = std::max<long long>(
@@ -224,8 +259,8 @@ int cascade_impl(int kernel, void* out, const void* q, const void* k_pool, const
     const int st = launch_prefix_states(
         q, k_pool, v_pool, block_tables, context_lens, max_blocks_per_seq, num_seqs, num_blocks,
         block_size, num_q_heads, num_kv_heads, head_dim, scale, group_offsets, group_members,
-        group_prefix_blocks, num_groups, max_group_size, splits, o_pre, lse_pre, suf_tables,
-        suf_lens, dtype, stream, kv_fp8, k_scale, v_scale);
+        num_members, group_prefix_blocks, num_groups, max_group_size, splits, o_pre, lse_pre,
+        suf_tables, suf_lens, owners, dtype, stream, kv_fp8, k_scale, v_scale);
     if (st != PKV_OK) return st;
   }
   int st = decode_attention_with_lse(kernel, out, lse_suf, q, k_pool, v_pool, suf_tables,
@@ -240,12 +275,12 @@ int cascade_impl(int kernel, void* out, const void* q, const void* k_pool, const
     const size_t stride = (size_t)num_seqs * num_q_heads;
     if (dtype == PKV_F16)
       hipLaunchKernelGGL(cascade_combine<F16>, grid, dim3(kThreads), 0, hs, out, o_pre, lse_pre,
-                         lse_suf, group_offsets, group_members, num_q_heads, head_dim, splits,
-                         stride);
+                         lse_suf, group_offsets, group_members, num_members, num_seqs,
+                         num_q_heads, head_dim, splits, stride);
     else
       hipLaunchKernelGGL(cascade_combine<BF16>, grid, dim3(kThreads), 0, hs, out, o_pre, lse_pre,
-                         lse_suf, group_offsets, group_members, num_q_heads, head_dim, splits,
-                         stride);
+                         lse_suf, group_offsets, group_members, num_members, num_seqs,
+                         num_q_heads, head_dim, splits, stride);
   }
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -256,12 +291,12 @@ int cascade_impl(int kernel, void* out, const void* q, const void* k_pool, const
 extern "C" int paged_decode_attention_cascade(
     int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
-    int num_seqs, const int32_t* group_offsets, const int32_t* group_members,
+    int num_seqs, const int32_t* group_offsets, const int32_t* group_members, int num_members,
     const int32_t* group_prefix_blocks, int num_groups, int max_group_size, int num_blocks,
     int block_size, int num_q_heads, int num_kv_heads, int head_dim, float scale,
     void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   return pkv::cascade_impl(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
-                           context_lens, num_seqs, group_offsets, group_members,
+                           context_lens, num_seqs, group_offsets, group_members, num_members,
                            group_prefix_blocks, num_groups, max_group_size, num_blocks,
                            block_size, num_q_heads, num_kv_heads, head_dim, scale, workspace,
                            workspace_bytes, dtype, stream, false, 1.f, 1.f);
@@ -270,12 +305,12 @@ extern "C" int paged_decode_attention_cascade(
 extern "C" int paged_decode_attention_cascade_fp8(
     int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
-    int num_seqs, const int32_t* group_offsets, const int32_t* group_members,
+    int num_seqs, const int32_t* group_offsets, const int32_t* group_members, int num_members,
     const int32_t* group_prefix_blocks, int num_groups, int max_group_size, int num_blocks,
     int block_size, int num_q_heads, int num_kv_heads, int head_dim, float scale, float k_scale,
     float v_scale, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   return pkv::cascade_impl(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
-                           context_lens, num_seqs, group_offsets, group_members,
+                           context_lens, num_seqs, group_offsets, group_members, num_members,
                            group_prefix_blocks, num_groups, max_group_size, num_blocks,
                            block_size, num_q_heads, num_kv_heads, head_dim, scale, workspace,
                            workspace_bytes, dtype, stream, true, k_scale, v_scale);

@@ -498,3 +498,105 @@ extern "C" int pkv_bm_num_cached(const pkv_block_manager* bm) {
   if (!bm) return PKV_ERR_INVALID_ARG;
   return (int)bm->cache.size();
 }
+
+// ---------------------------------------------------------------------------
+// Groups for the shared-prefix (cascade) decode.  [lesson] "Sharing, and the
+// reference counting it needs": sequences with a common prompt prefix hold
+// the same physical blocks for it, so the groups can be read off the tables.
+// ---------------------------------------------------------------------------
+
+extern "C" int pkv_validate_cascade_groups(const int32_t* block_tables, int max_blocks_per_seq,
+                                           const int32_t* context_lens, int num_seqs,
+                                           int block_size, const int32_t* group_offsets,
+                                           const int32_t* group_members, int num_members,
+                                           const int32_t* group_prefix_blocks, int num_groups,
+                                           int* bad_group_out) {
+  if (bad_group_out) *bad_group_out = -1;
+  if (num_seqs < 0 || max_blocks_per_seq < 1 || block_size < 1 || num_members < 0 ||
+      num_groups < 0)
+    return PKV_ERR_INVALID_ARG;
+  if (num_groups == 0) return PKV_OK;
+  if (!group_offsets || !group_prefix_blocks || (num_members > 0 && !group_members) ||
+      (num_seqs > 0 && (!block_tables || !context_lens)))
+    return PKV_ERR_INVALID_ARG;
+  std::vector<char> seen((size_t)num_seqs, 0);
+  for (int z = 0; z < num_groups; ++z) {
+    const int lo = group_offsets[z], hi = group_offsets[z + 1];
+    const int pb = group_prefix_blocks[z];
+    bool ok = lo >= 0 && hi >= lo && hi <= num_members && pb >= 0 && pb <= max_blocks_per_seq;
+    const int32_t* ref_row = nullptr;
+    for (int m = lo; ok && m < hi; ++m) {
+      const int s = group_members[m];
+      ok = s >= 0 && s < num_seqs && !seen[s] &&
+           (long long)context_lens[s] >= (long long)pb * block_size;
+      if (!ok) break;
+      seen[s] = 1;
+      const int32_t* row = block_tables + (size_t)s * max_blocks_per_seq;
+      if (!ref_row) ref_row = row;
+      ok = std::equal(row, row + pb, ref_row);
+    }
+    if (!ok) {
+      if (bad_group_out) *bad_group_out = z;
+      return PKV_ERR_INVALID_ARG;
+    }
+  }
+  return PKV_OK;
+}
+
+extern "C" int pkv_cascade_default_min_prefix_tokens(void) { return PKV_CASCADE_MIN_PREFIX_TOKENS; }
+
+extern "C" int pkv_bm_export_cascade_groups(const pkv_block_manager* bm, const int* seqs, int n,
+                                            int min_prefix_tokens, int min_members,
+                                            int32_t* offsets_out, int32_t* members_out,
+                                            int32_t* prefix_blocks_out, int* num_groups_out,
+                                            int* num_members_out) {
+  if (!bm || n < 0 || !num_groups_out || !num_members_out) return PKV_ERR_INVALID_ARG;
+  if (n > 0 && (!seqs || !offsets_out || !members_out || !prefix_blocks_out))
+    return PKV_ERR_INVALID_ARG;
+  for (int i = 0; i < n; ++i)
+    if (!bm->seq_resident(seqs[i])) return PKV_ERR_INVALID_ARG;
+  *num_groups_out = 0;
+  *num_members_out = 0;
+  if (n == 0) return PKV_OK;
+  if (min_prefix_tokens < 0) min_prefix_tokens = PKV_CASCADE_MIN_PREFIX_TOKENS;
+  if (min_members < 2) min_members = 2;
+  const int b = bm->block_size;
+  // Candidate groups: rows whose first table entry is the same block, in
+  // order of first appearance; rows with no full block join none.
+  std::unordered_map<int32_t, int> cand_of;
+  std::vector<std::vector<int>> cand;
+  for (int i = 0; i < n; ++i) {
+    const auto& q = bm->seqs[seqs[i]];
+    if (q.len < b) continue;
+    auto it = cand_of.find(q.table[0]);
+    if (it == cand_of.end()) {
+      cand_of.emplace(q.table[0], (int)cand.size());
+      cand.push_back({i});
+    } else {
+      cand[it->second].push_back(i);
+    }
+  }
+  int groups = 0, members = 0;
+  offsets_out[0] = 0;
+  for (const auto& rows : cand) {
+    if ((int)rows.size() < min_members) continue;
+    // The prefix: leading entries every member shares, cut to the full
+    // blocks of the shortest member (a partial block is still written).
+    const auto& first = bm->seqs[seqs[rows[0]]];
+    int pb = first.len / b;
+    for (int r : rows) {
+      const auto& q = bm->seqs[seqs[r]];
+      pb = std::min(pb, q.len / b);
+      int j = 0;
+      while (j < pb && q.table[j] == first.table[j]) ++j;
+      pb = j;
+    }
+    if (pb < 1 || (long long)pb * b < min_prefix_tokens) continue;
+    for (int r : rows) members_out[members++] = r;
+    prefix_blocks_out[groups] = pb;
+    offsets_out[++groups] = members;
+  }
+  *num_groups_out = groups;
+  *num_members_out = members;
+  return PKV_OK;
+}

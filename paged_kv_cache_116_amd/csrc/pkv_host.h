@@ -38,9 +38,10 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* tables, const int32_t* lens, int max_blocks,
                          int num_seqs, int num_blocks, int block_size, int num_q_heads,
                          int num_kv_heads, int head_dim, float scale, const int32_t* offsets,
-                         const int32_t* members, const int32_t* prefix_blocks, int num_groups,
-                         int max_group_size, int splits, float* o_states, float* lse,
-                         int32_t* suf_tables, int32_t* suf_lens, int dtype, void* stream,
+                         const int32_t* members, int num_members,
+                         const int32_t* prefix_blocks, int num_groups, int max_group_size,
+                         int splits, float* o_states, float* lse, int32_t* suf_tables,
+                         int32_t* suf_lens, const int32_t* owners, int dtype, void* stream,
                          bool kv_fp8, float k_scale, float v_scale);
 
 // Defined in decode_attention.hip; used by the cascade decode.  The first

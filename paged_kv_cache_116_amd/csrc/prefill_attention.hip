@@ -90,8 +90,14 @@ struct PrefillParams {
   // [S, Hq, D]) and its log normaliser (lse + r * S * Hq, [S, Hq]).  The
   // workgroups of range 0 and KV head 0 also write each member's suffix
   // table row (its entries past the prefix, then -1) and suffix length.
+  // Offsets outside [0, num_members] or decreasing skip the group; member
+  // ids outside [0, num_seqs) are skipped; a member whose first table
+  // entries differ from the group's first member's, or that owners[] counts
+  // in more than one group, gets an over-long suffix length (NaN rows).
   const int32_t* offsets;
   const int32_t* members;
+  const int32_t* owners;
+  int num_members;
   const int32_t* prefix_blocks;
   float* o_states;
   float* lse;
@@ -141,6 +147,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
   __shared__ __align__(16) uint4 k_lds[2][kTile * LPR];
   __shared__ __align__(16) uint16_t v_lds[2][kTile * VP];
   __shared__ int bad_lds;
+  __shared__ int mism_lds;
   auto kswz = [](int r) {
     if constexpr (LPR >= 16) return r & 15;
     else if constexpr (LPR == 8) return (r >> 1) & 7;
@@ -190,12 +197,21 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
   bool invalid;
   const int32_t* trow;
   if constexpr (kPrefix) {
-    cu0 = p.offsets[z];
-    n = p.offsets[z + 1] - cu0;
+    // Offsets outside [0, num_members], or decreasing, name no members: the
+    // group is skipped (its sequences keep their whole tables).
+    const int lo = p.offsets[z];
+    const int hi = p.offsets[z + 1];
+    const bool grp_ok = lo >= 0 && hi >= lo && hi <= p.num_members;
+    cu0 = grp_ok ? lo : 0;
+    n = grp_ok ? hi - lo : 0;
     L = p.prefix_blocks[z] << p.log2_b;
-    // A prefix past the table row has no defined result: NaN rows.
-    invalid = p.prefix_blocks[z] < 0 || p.prefix_blocks[z] > p.max_blocks;
-    trow = p.tables + (size_t)(n > 0 ? p.members[cu0] : 0) * p.max_blocks;
+    // The prefix is read through the first member's table row.  A first
+    // member outside the batch, or a prefix past the table row, has no
+    // defined result: NaN rows.
+    const int s0 = n > 0 ? p.members[cu0] : -1;
+    const bool ref_ok = s0 >= 0 && s0 < p.num_seqs;
+    invalid = !ref_ok || p.prefix_blocks[z] < 0 || p.prefix_blocks[z] > p.max_blocks;
+    trow = p.tables + (size_t)(ref_ok ? s0 : 0) * p.max_blocks;
   } else {
     cu0 = p.cu[z];
     n = p.cu[z + 1] - cu0;
@@ -208,6 +224,11 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
   const int rows = n * g;
   // Position of row i's query: keys 0 .. pos(i) are visible.
   auto pos_of = [&](int i) { return kPrefix ? L - 1 : L - n + i; };
+  // Prefix mode: the sequence of member i, or -1 for an id outside the batch.
+  auto member_of = [&](int i) {
+    const int s = p.members[cu0 + i];
+    return (s >= 0 && s < p.num_seqs) ? s : -1;
+  };
 
   for (int rb = rb_first; rb * kRows < rows; rb += rb_stride) {
     if constexpr (kPrefix) {
@@ -217,17 +238,28 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
         const int i0 = (rb * kRows + g - 1) / g;
         const int i1 = min(n, (rb * kRows + kRows + g - 1) / g);
         for (int i = i0; i < i1; ++i) {
-          const int s = p.members[cu0 + i];
+          const int s = member_of(i);   // uniform over the workgroup
+          if (s < 0) continue;
           const size_t row = (size_t)s * p.max_blocks;
+          // Does the member's table start with the group's prefix blocks?
+          if (tid == 0) mism_lds = 0;
+          lds_barrier();
+          bool mism = false;
+          if (!invalid)
+            for (int j = tid; j < pb; j += kThreads) mism |= p.tables[row + j] != trow[j];
+          if (mism) mism_lds = 1;
           for (int j = tid; j < p.max_blocks; j += kThreads)
             p.suf_tables[row + j] = (!invalid && j + pb < p.max_blocks) ? p.tables[row + j + pb]
                                                                         : -1;
+          lds_barrier();
           if (tid == 0) {
-            // A member shorter than the prefix, or a prefix past the table,
-            // gets an over-long length, which the decode path turns into NaN
-            // rows.
+            // A member shorter than the prefix, a prefix past the table, a
+            // member whose table does not start with the prefix or one listed
+            // in several groups gets an over-long length, which the decode
+            // path turns into NaN rows.
             const int Ls = p.lens[s];
-            p.suf_lens[s] = (invalid || Ls < L) ? max_len + 1 : Ls - L;
+            const bool bad = invalid || Ls < L || mism_lds != 0 || p.owners[s] != 1;
+            p.suf_lens[s] = bad ? max_len + 1 : Ls - L;
           }
         }
       }
@@ -238,7 +270,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
 #pragma unroll
     for (int rg = 0; rg < kRG; ++rg) {
       const int r = rb * kRows + (w * kRG + rg) * 16 + col;
-      row_ok[rg] = r < rows;
+      row_ok[rg] = r < rows && (!kPrefix || member_of(r / g) >= 0);
       pos[rg] = pos_of(row_ok[rg] ? r / g : 0);   // the row's position; keys 0 .. pos
     }
     // Where this lane's row of group rg lives: its element offset in q and
@@ -253,7 +285,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
       const bool ok = r < rows;
       const int i = ok ? r / g : 0;
       const int h = kvh * g + (ok ? r - i * g : 0);
-      const size_t qi = kPrefix ? (size_t)(ok ? p.members[cu0 + i] : 0) : (size_t)(cu0 + i);
+      const size_t qi = kPrefix ? (size_t)(ok ? max(member_of(i), 0) : 0) : (size_t)(cu0 + i);
       return RowAddr{(qi * p.num_q_heads + h) * D,
                      (size_t)split * p.num_seqs * p.num_q_heads + qi * p.num_q_heads + h};
     };
@@ -665,9 +697,10 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
                          const int32_t* tables, const int32_t* lens, int max_blocks,
                          int num_seqs, int num_blocks, int block_size, int num_q_heads,
                          int num_kv_heads, int head_dim, float scale, const int32_t* offsets,
-                         const int32_t* members, const int32_t* prefix_blocks, int num_groups,
-                         int max_group_size, int splits, float* o_states, float* lse,
-                         int32_t* suf_tables, int32_t* suf_lens, int dtype, void* stream,
+                         const int32_t* members, int num_members,
+                         const int32_t* prefix_blocks, int num_groups, int max_group_size,
+                         int splits, float* o_states, float* lse, int32_t* suf_tables,
+                         int32_t* suf_lens, const int32_t* owners, int dtype, void* stream,
                          bool kv_fp8, float k_scale, float v_scale) {
   PrefillParams p{};
   p.q = q;
@@ -689,6 +722,8 @@ int launch_prefix_states(const void* q, const void* k_pool, const void* v_pool,
   p.suf_lens = suf_lens;
   p.offsets = offsets;
   p.members = members;
+  p.num_members = num_members;
+  p.owners = owners;
   p.prefix_blocks = prefix_blocks;
   p.o_states = o_states;
   p.lse = lse;

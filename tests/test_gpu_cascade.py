@@ -233,3 +233,108 @@ def test_cascade_long_prefix_sampled():
                                   w.scale)
     check_close(out[torch.as_tensor(sample, device="cuda")], ref, "cascade, 4096-token prefix")
     assert torch.isfinite(out.float()).all()
+
+
+# --- a broken group contract: never a fault, NaN rows where results are undefined ---
+
+@pytest.mark.parametrize("case", ["mismatch", "twice", "id_outside", "first_outside",
+                                  "offsets_decrease", "offsets_past_members"])
+def test_cascade_broken_group_contract(case):
+    w, pb = shared_prefix_case(batch=8)
+    S = w.num_seqs
+    tables = w.tables.copy()
+    offsets, members, prefix = [0, 4, 8], list(range(8)), [pb, pb]
+    nan_rows = []
+    if case == "mismatch":            # row 2's table does not start with the prefix
+        spare = int(np.setdiff1d(np.arange(w.num_blocks), w.tables[w.tables >= 0])[0])
+        tables[2, 1] = spare
+        nan_rows = [2]
+    elif case == "twice":             # row 5 in both groups
+        members = [0, 1, 2, 5, 4, 5, 6, 7]
+        nan_rows = [5]
+    elif case == "id_outside":        # an id past the batch: skipped
+        members = [0, 1, 999, 3, 4, 5, 6, 7]
+    elif case == "first_outside":     # the group's first member is outside: its rows NaN
+        members = [-5, 1, 2, 3, 4, 5, 6, 7]
+        nan_rows = [1, 2, 3]
+    elif case == "offsets_decrease":  # group 1 names nothing: plain decode for rows 4..7
+        offsets = [0, 4, 2]
+    else:                             # group 1 runs past the 8 members: skipped
+        offsets = [0, 4, 9]
+    kp, vp, ek, ev = appended(w)
+    # The oracle attends the tables as given (row 2's spare block holds NaN:
+    # it is never read, the row is expected NaN).
+    keep = [s for s in range(S) if s not in nan_rows]
+    ref = o_attn.decode_attention(f64(w.q[keep]), ek, ev, tables[keep], w.lens[keep],
+                                  w.block_size, w.scale)
+    q = w.q.cuda()
+    out = torch.empty_like(q)
+    print(f"cascade broken contract: {case}", flush=True)
+    pkv.paged_decode_attention_cascade(out, q, kp, vp, i32(tables), i32(w.lens), i32(offsets),
+                                       i32(members), i32(prefix), max_group_size=4,
+                                       scale=w.scale)
+    torch.cuda.synchronize()
+    check_close(out[keep], ref, f"cascade {case}")
+    for s in nan_rows:
+        assert torch.isnan(out[s].float()).all(), s
+
+
+# --- groups read off the block manager, end to end ---
+
+def test_admitted_prompts_exported_groups_cascade_matches_oracle():
+    """Prompts admitted through the prefix cache (a shared 80-token system
+    prompt, private suffixes, an unrelated prompt, a fork), their uncached
+    positions written by the multi-token append, one decode step driven by
+    the block manager (copy-on-write included), the groups exported from the
+    tables, then the cascade against the float64 oracle on its own pools."""
+    B, Hq, Hkv, D, N = 16, 32, 8, 128, 160
+    dt = torch.float16
+    rng = np.random.default_rng(31)
+    gen = torch.Generator().manual_seed(31)
+    bm = pkv.BlockManager(N, B)
+    sysp = rng.integers(0, 1000, 80).tolist()
+    prompts = [sysp + rng.integers(0, 1000, int(n)).tolist() for n in (5, 40, 77, 16)]
+    prompts.append(rng.integers(0, 1000, 50).tolist())
+    seqs, cached = [], []
+    for p in prompts:
+        s = bm.seq_new()
+        cached.append(bm.seq_admit_prompt(s, p))
+        seqs.append(s)
+    assert cached == [0, 80, 80, 80, 0]
+    kpool = torch.full((N, B, Hkv, D), float("nan"), dtype=dt)
+    vpool = torch.full_like(kpool, float("nan"))
+    ek, ev = f64(kpool), f64(vpool)
+    kd, vd = kpool.cuda(), vpool.cuda()
+    # Prefill writes: positions cached .. len - 1 of each prompt.
+    tables, lens = bm.export_tables(seqs, 16)
+    chunks = [len(p) - c for p, c in zip(prompts, cached)]
+    cu = np.concatenate([[0], np.cumsum(chunks)]).astype(np.int32)
+    kn = torch.randn(int(cu[-1]), Hkv, D, generator=gen).to(dt)
+    vn = torch.randn(int(cu[-1]), Hkv, D, generator=gen).to(dt)
+    pkv.paged_kv_append_tokens(kd, vd, kn.cuda(), vn.cuda(), i32(cu), i32(tables.numpy()),
+                               i32(cached))
+    ek, ev = o_cache.append_tokens(ek, ev, f64(kn), f64(vn), tables.numpy(), cached, cu, B)
+    # A fork of the third sequence; then one decode step for all six.
+    seqs.append(bm.seq_fork(seqs[2]))
+    blocks, slots, csrc, cdst = bm.append_batch(seqs)
+    if csrc.numel():
+        pkv.paged_kv_copy_blocks(kd, vd, csrc.cuda(), cdst.cuda())
+        ek, ev = o_cache.copy_blocks(ek, ev, csrc.tolist(), cdst.tolist())
+    tables, lens = bm.export_tables(seqs, 16)
+    t, L = tables.numpy(), lens.numpy()
+    S = len(seqs)
+    k1 = torch.randn(S, Hkv, D, generator=gen).to(dt)
+    v1 = torch.randn(S, Hkv, D, generator=gen).to(dt)
+    pkv.paged_kv_append(kd, vd, k1.cuda(), v1.cuda(), i32(t), i32(L - 1))
+    ek, ev = o_cache.append_token(ek, ev, f64(k1), f64(v1), t, L - 1, B)
+    off, mem, pre = bm.export_cascade_groups(seqs, min_prefix_tokens=0)
+    # The four system-prompt rows and the fork share the system prompt's 5 blocks.
+    assert off.tolist() == [0, 5] and mem.tolist() == [0, 1, 2, 3, 5] and pre.tolist() == [5]
+    assert pkv.pkv_validate_cascade_groups(t, L, B, off, mem, pre) == -1
+    q = torch.randn(S, Hq, D, generator=gen).to(dt)
+    out = torch.empty(S, Hq, D, dtype=dt, device="cuda")
+    pkv.paged_decode_attention_cascade(out, q.cuda(), kd, vd, i32(t), i32(L), off.cuda(),
+                                       mem.cuda(), pre.cuda(), scale=D ** -0.5)
+    torch.cuda.synchronize()
+    ref = o_attn.decode_attention(f64(q), ek, ev, t, L, B, D ** -0.5)
+    check_close(out, ref, "block manager groups -> cascade")

@@ -563,3 +563,143 @@ def test_admit_prompt_validates_arguments():
     with pytest.raises(pkv.PagedKVError):
         bm.seq_admit_prompt(s, [1, 2, 3, 4])    # not an empty sequence
     assert lib.pkv_bm_seq_admit_prompt(None, 0, None, 0, None) == pkv.PKV_ERR_INVALID_ARG
+
+
+# --- shared-prefix (cascade) groups: host validator and block-manager export ---
+
+def cascade_tables():
+    """Six rows, B = 4: rows 0, 2, 3 share blocks [7, 2, 11]; row 1 is private;
+    rows 4, 5 share block 20 only."""
+    t = np.full((6, 6), -1, dtype=np.int32)
+    t[0, :5] = [7, 2, 11, 30, 31]
+    t[1, :3] = [40, 41, 42]
+    t[2, :4] = [7, 2, 11, 32]
+    t[3, :4] = [7, 2, 11, 33]
+    t[4, :2] = [20, 21]
+    t[5, :3] = [20, 22, 23]
+    lens = np.array([19, 10, 14, 13, 6, 9], dtype=np.int32)
+    return t, lens
+
+
+@pytest.mark.parametrize("offsets,members,prefix,bad", [
+    ([0, 3, 5], [0, 2, 3, 4, 5], [3, 1], -1),          # the contract holds
+    ([0, 3], [0, 2, 3], [0], -1),                       # an empty prefix is allowed
+    ([0, 3, 2], [0, 2, 3, 4, 5], [3, 1], 1),            # offsets decrease
+    ([0, 3, 6], [0, 2, 3, 4, 5], [3, 1], 1),            # offset past the members
+    ([1, 3], [0, 2, 3], [3], -1),                       # offsets need not start at 0
+    ([-1, 3], [0, 2, 3], [3], 0),                       # negative offset
+    ([0, 3], [0, 2, 9], [3], 0),                        # id outside the batch
+    ([0, 2, 4], [0, 2, 2, 3], [3, 3], 1),               # a row in two groups
+    ([0, 3], [0, 2, 3], [7], 0),                        # prefix past the table row
+    ([0, 2], [0, 1], [1], 0),                           # row 1 does not start with block 7
+    ([0, 2], [4, 5], [2], 0),                           # rows 4, 5 differ at entry 1
+    ([0, 2], [0, 3], [4], 0),                           # row 3 (13 tokens) shorter than 16
+])
+def test_validate_cascade_groups(offsets, members, prefix, bad):
+    t, lens = cascade_tables()
+    assert pkv.pkv_validate_cascade_groups(t, lens, 4, offsets, members, prefix) == bad
+
+
+def test_cascade_entry_points_reject_bad_group_arguments_on_the_host():
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, tables=FAKE, mb=4, lens=FAKE, s=2,
+                 off=FAKE, mem=FAKE, nmem=2, pre=FAKE, ng=1, mg=2, n=16, b=16, hq=8, hkv=2,
+                 d=128, scale=0.1, ws=FAKE, wsb=1 << 30, dt=2, stream=None)
+        a.update(kw)
+        return lib.paged_decode_attention_cascade(
+            0, a["out"], a["q"], a["k"], a["v"], a["tables"], a["mb"], a["lens"], a["s"],
+            a["off"], a["mem"], a["nmem"], a["pre"], a["ng"], a["mg"], a["n"], a["b"], a["hq"],
+            a["hkv"], a["d"], a["scale"], a["ws"], a["wsb"], a["dt"], a["stream"])
+    assert call(nmem=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert call(mem=None) == pkv.PKV_ERR_INVALID_ARG
+    assert call(off=None) == pkv.PKV_ERR_INVALID_ARG
+    assert call(ng=-1) == pkv.PKV_ERR_INVALID_ARG
+    assert call(ng=70000) == pkv.PKV_ERR_INVALID_ARG
+    assert call(dt=0) == pkv.PKV_ERR_UNSUPPORTED
+
+
+def export_groups(bm, seqs, **kw):
+    off, mem, pre = bm.export_cascade_groups(seqs, **kw)
+    return off.tolist(), mem.tolist(), pre.tolist()
+
+
+def test_export_cascade_groups_from_admitted_prompts_and_forks():
+    B = 4
+    bm = pkv.BlockManager(64, B)
+    sysp = list(range(100, 112))                     # 12 tokens: 3 full blocks
+    ids = []
+    for suffix in ([1, 2, 3, 4, 5], [6, 7], [8, 9, 10, 11, 12, 13]):
+        s = bm.seq_new()
+        bm.seq_admit_prompt(s, sysp + suffix)
+        ids.append(s)
+    other = bm.seq_new()
+    bm.seq_admit_prompt(other, list(range(500, 509)))  # unrelated, 9 tokens
+    short = bm.seq_new()
+    bm.seq_admit_prompt(short, [100, 101, 102])        # a partial block only: in no group
+    child = bm.seq_fork(ids[2])                        # shares all of row 2's blocks
+    batch = [ids[0], other, ids[1], short, ids[2], child]
+    off, mem, pre = export_groups(bm, batch, min_prefix_tokens=0)
+    # rows 0, 2, 4, 5 start with the system prompt's first block; they share
+    # its 3 blocks; row 1 is alone and row 3 holds no full block.
+    assert (off, mem, pre) == ([0, 4], [0, 2, 4, 5], [3])
+    tables, lens = bm.export_tables(batch, 8)
+    assert pkv.pkv_validate_cascade_groups(tables, lens, B, off, mem, pre) == -1
+    # The fork alone with its parent shares every full block (5 of them).
+    off, mem, pre = export_groups(bm, [ids[2], child], min_prefix_tokens=0)
+    assert (off, mem, pre) == ([0, 2], [0, 1], [18 // B])
+    # Thresholds: a 12-token prefix is under 16 tokens; three members needed.
+    assert export_groups(bm, batch, min_prefix_tokens=16) == ([0], [], [])
+    assert export_groups(bm, batch, min_prefix_tokens=12, min_members=5) == ([0], [], [])
+    assert export_groups(bm, [ids[0], ids[1]], min_prefix_tokens=12, min_members=3) == \
+        ([0], [], [])
+    # The library's measured crossover as the default threshold.
+    assert pkv.pkv_cascade_default_min_prefix_tokens() > 0
+    assert export_groups(bm, batch) == ([0], [], [])     # 12 tokens: below the crossover
+    assert export_groups(bm, []) == ([0], [], [])
+    with pytest.raises(pkv.PagedKVError):
+        bm.export_cascade_groups([ids[0], 999])
+
+
+def test_export_cascade_groups_keeps_the_contract_under_random_traffic():
+    rng = np.random.default_rng(8)
+    B = 4
+    bm = pkv.BlockManager(400, B)
+    live = []
+    prompts = [list(rng.integers(0, 50, 8)) for _ in range(3)]
+    for step in range(300):
+        op = rng.integers(0, 4)
+        if op == 0 or len(live) < 2:
+            s = bm.seq_new()
+            p = prompts[rng.integers(0, 3)] + list(rng.integers(0, 50, rng.integers(0, 9)))
+            try:
+                bm.seq_admit_prompt(s, p)
+                live.append(s)
+            except pkv.NoFreeBlockError:
+                bm.seq_free(s)
+        elif op == 1:
+            live.append(bm.seq_fork(live[rng.integers(0, len(live))]))
+        elif op == 2:
+            try:
+                bm.append_batch(live)
+            except pkv.NoFreeBlockError:
+                pass
+        elif len(live) > 2:
+            bm.seq_free(live.pop(rng.integers(0, len(live))))
+        batch = [int(x) for x in rng.permutation(live)]
+        off, mem, pre = export_groups(bm, batch, min_prefix_tokens=0)
+        tables, lens = bm.export_tables(batch, 64)
+        assert pkv.pkv_validate_cascade_groups(tables, lens, B, off, mem, pre) == -1
+        # Every pair of rows with a full first block in common lands in one group.
+        t = tables.numpy()
+        group_of = {r: z for z in range(len(pre)) for r in mem[off[z]:off[z + 1]]}
+        for i in range(len(batch)):
+            for j in range(i + 1, len(batch)):
+                if lens[i] >= B and lens[j] >= B and t[i, 0] == t[j, 0]:
+                    assert group_of.get(i) == group_of.get(j)
+        # and its prefix cannot grow: some member differs at the next entry,
+        # or the next block is not full for some member
+        for z in range(len(pre)):
+            rows = mem[off[z]:off[z + 1]]
+            nxt = pre[z]
+            assert any(lens[r] < (nxt + 1) * B for r in rows) or \
+                len({int(t[r, nxt]) for r in rows}) > 1
