@@ -790,6 +790,12 @@ def run_cascade(args, torch, pkv, workloads, dev) -> int:
               f"ok={ok}", file=sys.stderr, flush=True)
 
     achieved = alg_distinct / (ms_casc * 1e-3) / 1e9
+    # The library's export policy: a group pays when its prefix holds at least
+    # PKV_CASCADE_MIN_PREFIX_TOKENS and members x prefix tokens reach the
+    # measured crossover for this head shape; otherwise plain decode.
+    min_shared = pkv.pkv_cascade_min_shared_tokens(Hkv, D, esize)
+    picks = ("cascade" if npre * B >= pkv.PKV_CASCADE_MIN_PREFIX_TOKENS and
+             S * npre * B >= min_shared else "plain")
     result = {
         "metric": "shared-prefix decode attention, logical KV GB/s + seq-layer steps/s",
         "value": round(kv_logical / (ms_step * 1e-3) / 1e9, 2),
@@ -817,6 +823,8 @@ def run_cascade(args, torch, pkv, workloads, dev) -> int:
                "plain_decode_step": round(ms_dec_step * 1e3, 2),
                "plain_decode_attention": round(ms_dec * 1e3, 2)},
         "speedup_over_plain_decode": round(ms_dec_step / ms_step, 3),
+        "policy": {"picks": picks, "min_shared_tokens": min_shared,
+                   "step_us": round((ms_step if picks == "cascade" else ms_dec_step) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": None,

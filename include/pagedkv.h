@@ -348,7 +348,9 @@ int paged_decode_attention_lse(int kernel, float* lse, void* out, const void* q,
  *   - paged_decode_attention_lse over each sequence's remaining blocks;
  *   - per member, O = sum_r e^(a_r - M) O_r / sum_r e^(a_r - M) over the
  *     prefix ranges and the rest, a_r their log normalisers, M = max a_r.
- * Sequences outside every group get plain decode attention.  A member
+ * Sequences outside every group get plain decode attention; with
+ * num_groups = 0 the call is paged_decode_attention_with on the tables as
+ * given (same launches, no extra work).  A member
  * shorter than its group's prefix, or a prefix longer than the table row,
  * gets NaN rows.  F16 / BF16 pools, head_dim % 32 == 0.  Workspace:
  * paged_decode_cascade_workspace_bytes (256-byte aligned). */
@@ -655,23 +657,39 @@ int pkv_bm_export_tables(const pkv_block_manager* bm, const int* seqs, int n, in
  * entry is the same block form a candidate group, in order of first
  * appearance; its prefix is the longest run of leading entries all its
  * members share, cut to the full blocks of its shortest member (a partial
- * block may still be written).  A candidate with at least min_members rows
- * (at least 2) and a prefix of at least min_prefix_tokens tokens is written
- * out: members_out lists its rows (batch row indices, ascending) from
- * offsets_out[z] to offsets_out[z+1], prefix_blocks_out[z] its prefix
- * blocks.  Room: offsets_out n + 1 entries, members_out n,
- * prefix_blocks_out n.  min_prefix_tokens < 0 takes
- * PKV_CASCADE_MIN_PREFIX_TOKENS.  Rows in no group get plain decode
- * attention from the cascade. */
+ * block may still be written).  A candidate of at least 2 rows whose prefix
+ * holds at least min_prefix_tokens tokens, and whose prefix tokens times
+ * member count reach min_shared_tokens, is written out: members_out lists
+ * its rows (batch row indices, ascending) from offsets_out[z] to
+ * offsets_out[z+1], prefix_blocks_out[z] its prefix blocks.  Room:
+ * offsets_out n + 1 entries, members_out n, prefix_blocks_out n.  A
+ * negative min_prefix_tokens takes PKV_CASCADE_MIN_PREFIX_TOKENS, a
+ * negative min_shared_tokens pkv_cascade_min_shared_tokens(8, 128, 2).
+ * Rows in no group get plain decode attention from the cascade. */
 int pkv_bm_export_cascade_groups(const pkv_block_manager* bm, const int* seqs, int n,
-                                 int min_prefix_tokens, int min_members, int32_t* offsets_out,
-                                 int32_t* members_out, int32_t* prefix_blocks_out,
-                                 int* num_groups_out, int* num_members_out);
+                                 int min_prefix_tokens, long long min_shared_tokens,
+                                 int32_t* offsets_out, int32_t* members_out,
+                                 int32_t* prefix_blocks_out, int* num_groups_out,
+                                 int* num_members_out);
 
-/* Shortest shared prefix, in tokens, for which the cascade decode beat
- * plain decode on MI355X (measured; see pkv_cascade_default_min_prefix_tokens). */
-#define PKV_CASCADE_MIN_PREFIX_TOKENS 2048
-int pkv_cascade_default_min_prefix_tokens(void);
+/* When the cascade pays.  It spends a fixed ~25 us of extra launches plus a
+ * little per member and saves plain decode's re-reads of the shared prefix,
+ * one per member.  Measured on MI355X (32 query / 8 KV heads of 128, fp16,
+ * B 16, private suffixes of U[1, 512] tokens, plain decode with
+ * cache-retaining loads), members x prefix tokens decides it: at 196,608
+ * and above the cascade won everywhere (128 x 1536: 1.13x, 64 x 3072:
+ * 1.29x, 256 x 1024: 1.17x), at 98,304 and below plain decode did or tied
+ * (64 x 1536: 1.00x, 16 x 4096: 0.81x), and at 131,072 it went both ways
+ * (64 x 2048: 1.12x, 128 x 1024: 0.96x).  The threshold sits between, at
+ * 163,840 token rows, and is kept as bytes of K and V re-read (x 4 KiB =
+ * 640 MiB) so that it carries over to other head shapes; no prefix under
+ * 1024 tokens was measured to pay. */
+#define PKV_CASCADE_MIN_PREFIX_TOKENS 1024
+#define PKV_CASCADE_MIN_SHARED_BYTES (640LL << 20)
+/* members x prefix tokens at which the cascade pays for num_kv_heads heads of
+ * head_dim elements of elem_bytes bytes: PKV_CASCADE_MIN_SHARED_BYTES over
+ * the K and V bytes of one token, rounded up; -1 for invalid arguments. */
+long long pkv_cascade_min_shared_tokens(int num_kv_heads, int head_dim, int elem_bytes);
 
 /*
  * pkv_validate_tables - host check of the block-id contract of a batch: every

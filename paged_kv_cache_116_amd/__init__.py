@@ -99,8 +99,8 @@ _sig("paged_decode_attention_cascade_fp8", _i32,
 _sig("pkv_validate_cascade_groups", _i32,
      [_p, _i32, _p, _i32, _i32, _p, _p, _i32, _p, _i32, _intp])
 _sig("pkv_bm_export_cascade_groups", _i32,
-     [_p, _p, _i32, _i32, _i32, _p, _p, _p, _intp, _intp])
-_sig("pkv_cascade_default_min_prefix_tokens", _i32, [])
+     [_p, _p, _i32, _i32, ctypes.c_longlong, _p, _p, _p, _intp, _intp])
+_sig("pkv_cascade_min_shared_tokens", ctypes.c_longlong, [_i32, _i32, _i32])
 _sig("paged_kv_swap_out", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("paged_kv_swap_in", _i32, [_p, _p, _p, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("pkv_bm_seq_swap_out", _i32, [_p, _i32, _p, _i32, _intp])
@@ -502,8 +502,13 @@ def pkv_validate_cascade_groups(block_tables, context_lens, block_size: int, gro
     return bad.value
 
 
-def pkv_cascade_default_min_prefix_tokens() -> int:
-    return _lib.pkv_cascade_default_min_prefix_tokens()
+PKV_CASCADE_MIN_PREFIX_TOKENS = 1024
+
+
+def pkv_cascade_min_shared_tokens(num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
+    """members x prefix tokens from which the cascade beats plain decode (measured
+    crossover, kept in bytes of K and V re-read)."""
+    return int(_lib.pkv_cascade_min_shared_tokens(num_kv_heads, head_dim, elem_bytes))
 
 
 def pkv_validate_tables(block_tables, context_lens, num_blocks: int, block_size: int):
@@ -659,11 +664,12 @@ class BlockManager:
                                          lens.data_ptr()), "pkv_bm_export_tables")
         return out, lens
 
-    def export_cascade_groups(self, seqs, min_prefix_tokens: int = -1, min_members: int = 2):
+    def export_cascade_groups(self, seqs, min_prefix_tokens: int = -1,
+                              min_shared_tokens: int = -1):
         """(offsets [G + 1], members [M], prefix_blocks [G]) int32 CPU tensors: the
         shared-prefix groups of the batch seqs (row i = seqs[i]); members are
-        batch rows.  min_prefix_tokens < 0 takes the library's measured
-        crossover."""
+        batch rows.  Negative thresholds take the library's measured
+        crossover (see the C header)."""
         ids = torch.as_tensor(list(seqs), dtype=torch.int32)
         n = ids.numel()
         offsets = torch.zeros(n + 1, dtype=torch.int32)
@@ -671,7 +677,7 @@ class BlockManager:
         prefix = torch.zeros(max(n, 1), dtype=torch.int32)
         ng, nm = ctypes.c_int(0), ctypes.c_int(0)
         _check(_lib.pkv_bm_export_cascade_groups(
-            self._h, ids.data_ptr(), n, int(min_prefix_tokens), int(min_members),
+            self._h, ids.data_ptr(), n, int(min_prefix_tokens), int(min_shared_tokens),
             offsets.data_ptr(), members.data_ptr(), prefix.data_ptr(), ctypes.byref(ng),
             ctypes.byref(nm)), "pkv_bm_export_cascade_groups")
         return (offsets[: ng.value + 1].clone(), members[: nm.value].clone(),

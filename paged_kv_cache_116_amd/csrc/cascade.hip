@@ -241,6 +241,14 @@ int cascade_impl(int kernel, void* out, const void* q, const void* k_pool, const
                                           kv_fp8, k_scale, v_scale);
     if (st != PKV_OK) return st;
   }
+  // No group (the export policy found none that pays): plain decode over the
+  // tables as given, the same launches as paged_decode_attention_with.
+  if (num_groups == 0)
+    return decode_attention_with_lse(kernel, out, nullptr, q, k_pool, v_pool, block_tables,
+                                     max_blocks_per_seq, context_lens, num_seqs, num_blocks,
+                                     block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                                     ws + w.decode, workspace_bytes - w.decode, dtype, stream,
+                                     kv_fp8, k_scale, v_scale);
   hipStream_t hs = (hipStream_t)stream;
   hipLaunchKernelGGL(cascade_tables, dim3(num_seqs), dim3(kThreads), 0, hs, block_tables,
                      context_lens, max_blocks_per_seq, suf_tables, suf_lens, owners);

@@ -543,10 +543,15 @@ extern "C" int pkv_validate_cascade_groups(const int32_t* block_tables, int max_
   return PKV_OK;
 }
 
-extern "C" int pkv_cascade_default_min_prefix_tokens(void) { return PKV_CASCADE_MIN_PREFIX_TOKENS; }
+extern "C" long long pkv_cascade_min_shared_tokens(int num_kv_heads, int head_dim,
+                                                   int elem_bytes) {
+  if (num_kv_heads < 1 || head_dim < 1 || elem_bytes < 1) return -1;
+  const long long row = 2LL * num_kv_heads * head_dim * elem_bytes;   // K and V of a token
+  return (PKV_CASCADE_MIN_SHARED_BYTES + row - 1) / row;
+}
 
 extern "C" int pkv_bm_export_cascade_groups(const pkv_block_manager* bm, const int* seqs, int n,
-                                            int min_prefix_tokens, int min_members,
+                                            int min_prefix_tokens, long long min_shared_tokens,
                                             int32_t* offsets_out, int32_t* members_out,
                                             int32_t* prefix_blocks_out, int* num_groups_out,
                                             int* num_members_out) {
@@ -559,7 +564,7 @@ extern "C" int pkv_bm_export_cascade_groups(const pkv_block_manager* bm, const i
   *num_members_out = 0;
   if (n == 0) return PKV_OK;
   if (min_prefix_tokens < 0) min_prefix_tokens = PKV_CASCADE_MIN_PREFIX_TOKENS;
-  if (min_members < 2) min_members = 2;
+  if (min_shared_tokens < 0) min_shared_tokens = pkv_cascade_min_shared_tokens(8, 128, 2);
   const int b = bm->block_size;
   // Candidate groups: rows whose first table entry is the same block, in
   // order of first appearance; rows with no full block join none.
@@ -579,7 +584,7 @@ extern "C" int pkv_bm_export_cascade_groups(const pkv_block_manager* bm, const i
   int groups = 0, members = 0;
   offsets_out[0] = 0;
   for (const auto& rows : cand) {
-    if ((int)rows.size() < min_members) continue;
+    if (rows.size() < 2) continue;
     // The prefix: leading entries every member shares, cut to the full
     // blocks of the shortest member (a partial block is still written).
     const auto& first = bm->seqs[seqs[rows[0]]];
@@ -591,7 +596,10 @@ extern "C" int pkv_bm_export_cascade_groups(const pkv_block_manager* bm, const i
       while (j < pb && q.table[j] == first.table[j]) ++j;
       pb = j;
     }
-    if (pb < 1 || (long long)pb * b < min_prefix_tokens) continue;
+    const long long prefix_tokens = (long long)pb * b;
+    if (pb < 1 || prefix_tokens < min_prefix_tokens ||
+        prefix_tokens * (long long)rows.size() < min_shared_tokens)
+      continue;
     for (int r : rows) members_out[members++] = r;
     prefix_blocks_out[groups] = pb;
     offsets_out[++groups] = members;

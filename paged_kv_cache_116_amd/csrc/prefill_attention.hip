@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
   __shared__ __align__(16) uint4 k_lds[2][kTile * LPR];
   __shared__ __align__(16) uint16_t v_lds[2][kTile * VP];
   __shared__ int bad_lds;
-  __shared__ int mism_lds;
+  __shared__ int mism_lds[kPrefix ? kRows : 1];   // prefix mode: per member of a row block
   auto kswz = [](int r) {
     if constexpr (LPR >= 16) return r & 15;
     else if constexpr (LPR == 8) return (r >> 1) & 7;
@@ -237,28 +237,32 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
         const int pb = p.prefix_blocks[z];
         const int i0 = (rb * kRows + g - 1) / g;
         const int i1 = min(n, (rb * kRows + kRows + g - 1) / g);
-        for (int i = i0; i < i1; ++i) {
-          const int s = member_of(i);   // uniform over the workgroup
+        // At most kRows members; their (member, table entry) pairs are
+        // spread over the workgroup: does the entry match the group's prefix
+        // (j < pb), and the suffix table's entry j.
+        const int nm = i1 - i0;
+        const int mbk = p.max_blocks;
+        if (tid < kRows) mism_lds[tid] = 0;
+        lds_barrier();
+        for (int e = tid; e < nm * mbk; e += kThreads) {
+          const int i = e / mbk;
+          const int j = e - i * mbk;
+          const int s = member_of(i0 + i);
           if (s < 0) continue;
-          const size_t row = (size_t)s * p.max_blocks;
-          // Does the member's table start with the group's prefix blocks?
-          if (tid == 0) mism_lds = 0;
-          lds_barrier();
-          bool mism = false;
-          if (!invalid)
-            for (int j = tid; j < pb; j += kThreads) mism |= p.tables[row + j] != trow[j];
-          if (mism) mism_lds = 1;
-          for (int j = tid; j < p.max_blocks; j += kThreads)
-            p.suf_tables[row + j] = (!invalid && j + pb < p.max_blocks) ? p.tables[row + j + pb]
-                                                                        : -1;
-          lds_barrier();
-          if (tid == 0) {
-            // A member shorter than the prefix, a prefix past the table, a
-            // member whose table does not start with the prefix or one listed
-            // in several groups gets an over-long length, which the decode
-            // path turns into NaN rows.
+          const size_t row = (size_t)s * mbk;
+          if (!invalid && j < pb && p.tables[row + j] != trow[j]) mism_lds[i] = 1;
+          p.suf_tables[row + j] = (!invalid && j + pb < mbk) ? p.tables[row + j + pb] : -1;
+        }
+        lds_barrier();
+        if (tid < nm) {
+          // A member shorter than the prefix, a prefix past the table, a
+          // member whose table does not start with the prefix or one listed
+          // in several groups gets an over-long length, which the decode
+          // path turns into NaN rows.
+          const int s = member_of(i0 + tid);
+          if (s >= 0) {
             const int Ls = p.lens[s];
-            const bool bad = invalid || Ls < L || mism_lds != 0 || p.owners[s] != 1;
+            const bool bad = invalid || Ls < L || mism_lds[tid] != 0 || p.owners[s] != 1;
             p.suf_lens[s] = bad ? max_len + 1 : Ls - L;
           }
         }

@@ -327,7 +327,7 @@ def test_admitted_prompts_exported_groups_cascade_matches_oracle():
     v1 = torch.randn(S, Hkv, D, generator=gen).to(dt)
     pkv.paged_kv_append(kd, vd, k1.cuda(), v1.cuda(), i32(t), i32(L - 1))
     ek, ev = o_cache.append_token(ek, ev, f64(k1), f64(v1), t, L - 1, B)
-    off, mem, pre = bm.export_cascade_groups(seqs, min_prefix_tokens=0)
+    off, mem, pre = bm.export_cascade_groups(seqs, min_prefix_tokens=0, min_shared_tokens=0)
     # The four system-prompt rows and the fork share the system prompt's 5 blocks.
     assert off.tolist() == [0, 5] and mem.tolist() == [0, 1, 2, 3, 5] and pre.tolist() == [5]
     assert pkv.pkv_validate_cascade_groups(t, L, B, off, mem, pre) == -1
@@ -338,3 +338,21 @@ def test_admitted_prompts_exported_groups_cascade_matches_oracle():
     torch.cuda.synchronize()
     ref = o_attn.decode_attention(f64(q), ek, ev, t, L, B, D ** -0.5)
     check_close(out, ref, "block manager groups -> cascade")
+
+
+def test_cascade_without_groups_is_plain_decode_bitwise():
+    # What the export policy gives when no group pays: the cascade entry
+    # point with no group runs plain decode on the tables as given.
+    w, pb = shared_prefix_case(batch=6)
+    kp, vp, ek, ev = appended(w)
+    q = w.q.cuda()
+    a, b = torch.empty_like(q), torch.empty_like(q)
+    for k in (pkv.PKV_ATTN_AUTO, pkv.PKV_ATTN_AUTO | pkv.PKV_ATTN_CACHE_KV):
+        pkv.paged_decode_attention_cascade(a, q, kp, vp, i32(w.tables), i32(w.lens), i32([0]),
+                                           i32([]), i32([]), scale=w.scale, kernel=k)
+        pkv.paged_decode_attention_with(k, b, q, kp, vp, i32(w.tables), i32(w.lens),
+                                        scale=w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    ref = o_attn.decode_attention(f64(w.q), ek, ev, w.tables, w.lens, w.block_size, w.scale)
+    check_close(a, ref, "cascade, no groups")

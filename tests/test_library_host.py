@@ -638,22 +638,29 @@ def test_export_cascade_groups_from_admitted_prompts_and_forks():
     bm.seq_admit_prompt(short, [100, 101, 102])        # a partial block only: in no group
     child = bm.seq_fork(ids[2])                        # shares all of row 2's blocks
     batch = [ids[0], other, ids[1], short, ids[2], child]
-    off, mem, pre = export_groups(bm, batch, min_prefix_tokens=0)
+    off, mem, pre = export_groups(bm, batch, min_prefix_tokens=0, min_shared_tokens=0)
     # rows 0, 2, 4, 5 start with the system prompt's first block; they share
     # its 3 blocks; row 1 is alone and row 3 holds no full block.
     assert (off, mem, pre) == ([0, 4], [0, 2, 4, 5], [3])
     tables, lens = bm.export_tables(batch, 8)
     assert pkv.pkv_validate_cascade_groups(tables, lens, B, off, mem, pre) == -1
     # The fork alone with its parent shares every full block (5 of them).
-    off, mem, pre = export_groups(bm, [ids[2], child], min_prefix_tokens=0)
+    off, mem, pre = export_groups(bm, [ids[2], child], min_prefix_tokens=0,
+                                  min_shared_tokens=0)
     assert (off, mem, pre) == ([0, 2], [0, 1], [18 // B])
-    # Thresholds: a 12-token prefix is under 16 tokens; three members needed.
+    # Thresholds: a 12-token prefix is under 16 tokens; 4 members x 12 tokens
+    # = 48 shared tokens; 2 x 12 = 24.
     assert export_groups(bm, batch, min_prefix_tokens=16) == ([0], [], [])
-    assert export_groups(bm, batch, min_prefix_tokens=12, min_members=5) == ([0], [], [])
-    assert export_groups(bm, [ids[0], ids[1]], min_prefix_tokens=12, min_members=3) == \
+    assert export_groups(bm, batch, min_prefix_tokens=0, min_shared_tokens=48) == \
+        ([0, 4], [0, 2, 4, 5], [3])
+    assert export_groups(bm, batch, min_prefix_tokens=0, min_shared_tokens=49) == ([0], [], [])
+    assert export_groups(bm, [ids[0], ids[1]], min_prefix_tokens=12, min_shared_tokens=25) == \
         ([0], [], [])
-    # The library's measured crossover as the default threshold.
-    assert pkv.pkv_cascade_default_min_prefix_tokens() > 0
+    # The measured crossover: 640 MiB of K and V re-reads, 163,840 token-rows
+    # of 8 KV heads x 128 x fp16, half as many at twice the bytes per token.
+    assert pkv.pkv_cascade_min_shared_tokens(8, 128, 2) == 163840
+    assert pkv.pkv_cascade_min_shared_tokens(8, 128, 4) == 81920
+    assert pkv.pkv_cascade_min_shared_tokens(0, 128, 2) == -1
     assert export_groups(bm, batch) == ([0], [], [])     # 12 tokens: below the crossover
     assert export_groups(bm, []) == ([0], [], [])
     with pytest.raises(pkv.PagedKVError):
@@ -686,7 +693,7 @@ def test_export_cascade_groups_keeps_the_contract_under_random_traffic():
         elif len(live) > 2:
             bm.seq_free(live.pop(rng.integers(0, len(live))))
         batch = [int(x) for x in rng.permutation(live)]
-        off, mem, pre = export_groups(bm, batch, min_prefix_tokens=0)
+        off, mem, pre = export_groups(bm, batch, min_prefix_tokens=0, min_shared_tokens=0)
         tables, lens = bm.export_tables(batch, 64)
         assert pkv.pkv_validate_cascade_groups(tables, lens, B, off, mem, pre) == -1
         # Every pair of rows with a full first block in common lands in one group.
