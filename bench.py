@@ -22,7 +22,8 @@ Prints one JSON line.  `value` is KV GB/s over the whole step: valid key and
 value bytes of every sequence, divided by the step time.  The `roofline`
 object prices the partition kernel (the dominant one) against the 8 TB/s HBM
 peak, timed with HIP events on the stream it runs on.  `cpu_baseline` is the
-float64 CPU oracle on a sample of the same batch, single threaded.
+float64 CPU oracle on a sample of the same batch, on a pool of worker
+processes (one per usable core, at most 16), each with one BLAS thread.
 """
 
 from __future__ import annotations
@@ -88,10 +89,46 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
-def kernel_source_digest() -> str:
+CSRC = os.path.join(ROOT, "paged_kv_cache_116_amd", "csrc")
+# The source file that defines each profiled kernel.
+KERNEL_SOURCES = {
+    "attn_partition_mfma": "decode_attention.hip",
+    "attn_partition_valu": "decode_attention.hip",
+    "attn_plan": "decode_attention.hip",
+    "attn_merge": "decode_attention.hip",
+    "attn_prefill_mfma": "prefill_attention.hip",
+    "cascade": "cascade.hip",
+    "swap_kernel": "kv_cache_ops.hip",
+    "append_kernel": "kv_cache_ops.hip",
+}
+
+
+def _source_closure(path: str, seen: set) -> None:
+    """path and every file it includes with #include "...", recursively."""
+    path = os.path.normpath(path)
+    if path in seen or not os.path.exists(path):
+        return
+    seen.add(path)
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("#include \""):
+                _source_closure(os.path.join(os.path.dirname(path), line.split('"')[1]), seen)
+
+
+def kernel_source_digest(kernel: str = "attn_partition_mfma") -> str:
+    """SHA-256 (first 16 hex digits) of the source file that defines `kernel`
+    and of every header it includes, so that a profile taken on other code
+    shows as stale.  The cascade also runs the decode and prefill kernels."""
+    files: set = set()
+    roots = ([KERNEL_SOURCES[kernel]] if kernel != "cascade" else
+             ["cascade.hip", "decode_attention.hip", "prefill_attention.hip"])
+    for name in roots:
+        _source_closure(os.path.join(CSRC, name), files)
     h = hashlib.sha256()
-    for name in ("decode_attention.hip", "pkv_common.h"):
-        with open(os.path.join(ROOT, "paged_kv_cache_116_amd", "csrc", name), "rb") as f:
+    for path in sorted(files):
+        h.update(os.path.relpath(path, ROOT).encode())
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -105,9 +142,69 @@ def measured_traffic(workload: str, kernel: str):
     with open(path) as f:
         rec = json.load(f)
     entry = rec.get(workload, {}).get(kernel)
-    if not entry or entry.get("source_digest") != kernel_source_digest():
+    if not entry or entry.get("source_digest") != kernel_source_digest("attn_partition_" + kernel):
         return None
     return entry.get("traffic_bytes")
+
+
+def _oracle_worker(job):
+    """One CPU-baseline worker: the float64 oracle (append + gather attention)
+    on its share of the sampled sequences, repeated until `seconds` of its
+    own time are spent, BLAS limited to one thread.  Runs in a fresh
+    interpreter (spawn), which never touches the GPU."""
+    import threadpoolctl
+    sys.path.insert(0, ROOT)
+    from oracle import attention as o_attn
+    from oracle import cache_ops as o_cache
+    from oracle import fp8 as o_fp8
+    c, B, scale, fp8, k_scale, v_scale, seconds = job
+    passes, spent = 0, 0.0
+    with threadpoolctl.threadpool_limits(1):
+        while spent < seconds:
+            t = time.perf_counter()
+            if fp8:
+                kc, vc = o_fp8.append_token_fp8(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
+                                                c["tables"], c["lens_pre"], B, k_scale, v_scale)
+                kp, vp = o_fp8.dequantise(kc, k_scale), o_fp8.dequantise(vc, v_scale)
+            else:
+                kp, vp = o_cache.append_token(c["k_pool"], c["v_pool"], c["k_new"], c["v_new"],
+                                              c["tables"], c["lens_pre"], B)
+            o_attn.decode_attention(c["q"], kp, vp, c["tables"], c["lens"], B, scale)
+            spent += time.perf_counter() - t
+            passes += 1
+    return passes, spent
+
+
+def cpu_oracle_baseline(w, workloads, sample, seconds, fp8):
+    """The oracle on a process pool: one worker per usable core (the
+    process's CPU affinity, at most 16, the host share of one GPU), each on
+    its own slice of the sampled sequences for about `seconds`; returns
+    (KV bytes/s, sequences/s, workers)."""
+    import concurrent.futures
+    import multiprocessing
+    n = max(1, min(len(os.sched_getaffinity(0)), 16, len(sample)))
+    chunks = [sample[i::n] for i in range(n)]
+    jobs = [(workloads.extract_sequences(w, ch, dtype=np.float32), w.block_size, w.scale, fp8,
+             w.k_scale, w.v_scale, seconds) for ch in chunks]
+    row = w.num_kv_heads * w.head_dim * 2 * w.k_pool.element_size()
+    kv = [int(j[0]["lens"].astype(np.int64).sum()) * row for j in jobs]
+    saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                            "MKL_NUM_THREADS")}
+    os.environ.update({k: "1" for k in saved})
+    try:
+        ctx = multiprocessing.get_context("spawn")
+        with concurrent.futures.ProcessPoolExecutor(n, mp_context=ctx) as ex:
+            res = list(ex.map(_oracle_worker, jobs))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    gbps = sum(p * b / t for (p, t), b in zip(res, kv)) / 1e9
+    seqs = sum(p * len(ch) / t for (p, t), ch in zip(res, chunks))
+    passes = sum(p for p, _ in res)
+    return gbps, seqs, n, passes
 
 
 def main(argv=None) -> int:
@@ -157,10 +254,8 @@ def main(argv=None) -> int:
     rng = np.random.default_rng(7)
     check_seqs = sorted(set([int(np.argmax(w.lens))] +
                             rng.choice(w.num_seqs, size=min(4, w.num_seqs), replace=False).tolist()))
-    cpu_sample = sorted(rng.choice(w.num_seqs, size=min(32, w.num_seqs), replace=False).tolist())
+    cpu_sample = sorted(rng.choice(w.num_seqs, size=min(64, w.num_seqs), replace=False).tolist())
     check_inputs = None if args.no_check else workloads.extract_sequences(w, check_seqs)
-    cpu_inputs = (workloads.extract_sequences(w, cpu_sample, dtype=np.float32)
-                  if args.cpu_seconds > 0 else None)
 
     esize = w.k_pool.element_size()     # 1 for FP8 pools
     qsize = w.q.element_size()
@@ -250,6 +345,17 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / args.steps
 
+    # Step-time spread: a second pass with an event between consecutive steps
+    # (each interval is one step, launch gap included).
+    step_marks = [ev() for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    step_marks[0].record(stream)
+    for i in range(args.steps):
+        step()
+        step_marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    t_steps = [step_marks[i].elapsed_time(step_marks[i + 1]) for i in range(args.steps)]
+
     # Phase breakdown, a separate pass with an event between launches, the
     # append as its own launch (event records add a few microseconds of gap
     # each, so the phases sum to more than ms_step).  The partition kernel's
@@ -330,26 +436,19 @@ def main(argv=None) -> int:
               flush=True)
 
     cpu = None
-    if cpu_inputs is not None:
-        import threadpoolctl
-        from oracle import attention as o_attn
-        c = cpu_inputs
-        sample_kv = int(c["lens"].astype(np.int64).sum()) * Hkv * D * 2 * esize
-        passes, spent = 0, 0.0
-        with threadpoolctl.threadpool_limits(1):
-            while spent < args.cpu_seconds:
-                t = time.perf_counter()
-                kp, vp = oracle_append(c)
-                o_attn.decode_attention(c["q"], kp, vp, c["tables"], c["lens"], B, w.scale)
-                spent += time.perf_counter() - t
-                passes += 1
-        cpu = {"value": passes * sample_kv / spent / 1e9, "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
-               "seq_layer_steps_per_s": passes * len(cpu_sample) / spent,
+    if args.cpu_seconds > 0:
+        t = time.perf_counter()
+        gbps, seqs, n, passes = cpu_oracle_baseline(w, workloads, cpu_sample, args.cpu_seconds,
+                                                    fp8)
+        wall = time.perf_counter() - t
+        cpu = {"value": gbps, "unit": "GB/s", "cores": n, "kind": "oracle",
+               "seq_layer_steps_per_s": seqs,
                "sample": f"{len(cpu_sample)} of the {S} sequences (seeded), "
-                         f"{int(c['lens'].sum())} tokens, {passes} pass(es) in {spent:.1f}s, "
-                         "append + float64 gather attention, BLAS limited to 1 thread"}
-        print(f"# cpu oracle: {cpu['value']:.4f} GB/s over {spent:.1f}s", file=sys.stderr, flush=True)
+                         f"{int(w.lens[cpu_sample].sum())} tokens, split over {n} worker "
+                         f"processes (one BLAS thread each), each repeating its slice for about "
+                         f"{args.cpu_seconds:.0f}s ({passes} slice passes in all, {wall:.1f}s "
+                         "wall), append + float64 gather attention"}
+        print(f"# cpu oracle: {gbps:.4f} GB/s on {n} workers", file=sys.stderr, flush=True)
 
     kv_gbps_step = kv_bytes / (ms_step * 1e-3) / 1e9
     attn_ms = statistics.mean(t_plan) + statistics.mean(t_part) + statistics.mean(t_merge)
@@ -379,7 +478,11 @@ def main(argv=None) -> int:
         "seq_layer_steps_per_s": round(S / (ms_step * 1e-3), 1),
         "kv_bytes_per_step": kv_bytes,
         "kv_gbps_attention": round(kv_bytes / (attn_ms * 1e-3) / 1e9, 2),
-        "us": {"step": round(ms_step * 1e3, 2), "append": round(statistics.mean(t_app) * 1e3, 2),
+        "us": {"step": round(ms_step * 1e3, 2),
+               "step_median": round(statistics.median(t_steps) * 1e3, 2),
+               "step_p10": round(np.percentile(t_steps, 10) * 1e3, 2),
+               "step_p90": round(np.percentile(t_steps, 90) * 1e3, 2),
+               "append": round(statistics.mean(t_app) * 1e3, 2),
                "plan": round(statistics.mean(t_plan) * 1e3, 2),
                "partitions": round(part_ms * 1e3, 2),
                "partitions_p10": round(np.percentile(t_part, 10) * 1e3, 2),
