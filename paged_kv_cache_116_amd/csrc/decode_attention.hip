@@ -648,12 +648,17 @@ __device__ __forceinline__ uint4 expand8(const uint2& c) {
 template <typename T, int D, int G, bool kStream, bool kF8>
 __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnParams p) {
   using S = typename T::storage;
-  // A lane loads 8 elements of a K or V row at a time: 16 bytes of a 16-bit
-  // pool, 8 bytes of an FP8 pool (decoded to T on use).
-  using KvReg = typename std::conditional<kF8, uint2, uint4>::type;
+  // A lane loads 16 bytes of a K or V row at a time: 8 elements of a 16-bit
+  // pool, 16 codes of an FP8 pool (decoded to T on use), so that every load
+  // instruction moves 1 KiB whatever the pool type.  FP8 rows of 32 channels
+  // (D = 32) take 8 codes per lane, which keeps a whole row group per tile.
+  constexpr bool kWide = kF8 && D >= 64;
+  constexpr int EPL = kWide ? 16 : 8;   // elements per lane load
+  using KvReg = typename std::conditional<kF8 && !kWide, uint2, uint4>::type;
   constexpr int KVB = kF8 ? 1 : T::bytes;   // bytes per pool element
   constexpr int KCH = D / 32;        // MFMA k-chunks of 32 channels
-  constexpr int LPR = D / 8;         // lanes per K/V row (8 elements each)
+  constexpr int CPR = D / 8;         // 8-element chunks per K/V row in LDS
+  constexpr int LPR = D / EPL;       // lanes per K/V row
   constexpr int RPL = 64 / LPR;      // rows per load instruction
   constexpr int TPR = kTile / RPL;   // tokens per row group per tile
   // Tiles in flight per wave: three when the accumulator is large (G >= 4:
@@ -670,18 +675,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
   __shared__ float red_m[kWaves][G];
   __shared__ float red_l[kWaves][G];
   __shared__ __align__(16) float red_acc[kWaves][G][D];
-  // K tile of each wave, 16 rows of LPR 16-byte chunks; chunk c of row r
+  // K tile of each wave, 16 rows of CPR 16-byte chunks; chunk c of row r
   // sits at position c ^ kswz(r), which keeps both the row-wise writes and
   // the operand-wise reads free of bank conflicts.
-  __shared__ __align__(16) uint4 k_lds[kWaves][kTile * LPR];
+  __shared__ __align__(16) uint4 k_lds[kWaves][kTile * CPR];
   // V tile of each wave, token-major, rows padded by 32 bytes: the four rows
   // one 16-lane group reads at a time (a 32-byte piece of each) then land in
   // distinct banks, and so do the two groups of a half-wave.
   constexpr int VP = D + 16;
   __shared__ __align__(16) uint16_t v_lds[kWaves][kTile * VP];
   auto kswz = [](int r) {
-    if constexpr (LPR >= 16) return r & 15;          // rows of >= 256 bytes
-    else if constexpr (LPR == 8) return (r >> 1) & 7; // 128-byte rows: two per 256 bytes
+    if constexpr (CPR >= 16) return r & 15;          // rows of >= 256 bytes
+    else if constexpr (CPR == 8) return (r >> 1) & 7; // 128-byte rows: two per 256 bytes
     else return (r >> 2) & 3;                         // 64-byte rows: four per 256 bytes
   };
 
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;     // A row (token of tile) / B and C column (head)
   const int kgrp = lane >> 4;    // k group of A and B; C rows 4*kgrp .. 4*kgrp+3
-  const int vc = lane % LPR;     // K/V: 8-element chunk within the row
+  const int vc = lane % LPR;     // K/V: EPL-element piece within the row
   const int vr = lane / LPR;     // K/V: row group, tokens TPR*vr .. TPR*vr+TPR-1
   const size_t bytes = KVB;
   // KV-head group kw of the quad; with several waves per group, sub-wave sw
@@ -720,7 +725,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
     // flight.
     KvReg kb[kSlots][TPR], vb[kSlots][TPR];
     auto ld = [&](const char* a) {
-      if constexpr (kF8) return load_kv8<kStream>(a);
+      if constexpr (kF8 && !kWide) return load_kv8<kStream>(a);
       else return load_kv<kStream>(a);
     };
     auto issue = [&](auto slot, int tile) {
@@ -743,7 +748,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
         // every load instruction covers whole rows.
 #pragma unroll
         for (int i = 0; i < TPR; ++i) {
-          const uint32_t o = (uint32_t)min(TPR * vr + i, rlim) * rstride + vc * 8 * bytes;
+          const uint32_t o = (uint32_t)min(TPR * vr + i, rlim) * rstride + vc * EPL * bytes;
           kb[SL][i] = ld(kbase + o);
           vb[SL][i] = ld(vbase + o);
         }
@@ -755,7 +760,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
         };
 #pragma unroll
         for (int i = 0; i < TPR; ++i) {
-          const size_t o = row(tb + TPR * vr + i, vc * 8);
+          const size_t o = row(tb + TPR * vr + i, vc * EPL);
           kb[SL][i] = ld(p.k_pool + o);
           vb[SL][i] = ld(p.v_pool + o);
         }
@@ -781,14 +786,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
 #pragma unroll
       for (int i = 0; i < TPR; ++i) {
         const int r = TPR * vr + i;
-        k_lds[w][r * LPR + (vc ^ kswz(r))] = expand8<T>(kb[SL][i]);
-        *reinterpret_cast<uint4*>(&v_lds[w][r * VP + vc * 8]) = expand8<T>(vb[SL][i]);
+        if constexpr (kWide) {
+          // 16 codes: chunks 2vc and 2vc + 1 of the row.
+          k_lds[w][r * CPR + ((2 * vc) ^ kswz(r))] =
+              expand8<T>(make_uint2(kb[SL][i].x, kb[SL][i].y));
+          k_lds[w][r * CPR + ((2 * vc + 1) ^ kswz(r))] =
+              expand8<T>(make_uint2(kb[SL][i].z, kb[SL][i].w));
+          *reinterpret_cast<uint4*>(&v_lds[w][r * VP + vc * 16]) =
+              expand8<T>(make_uint2(vb[SL][i].x, vb[SL][i].y));
+          *reinterpret_cast<uint4*>(&v_lds[w][r * VP + vc * 16 + 8]) =
+              expand8<T>(make_uint2(vb[SL][i].z, vb[SL][i].w));
+        } else {
+          k_lds[w][r * CPR + (vc ^ kswz(r))] = expand8<T>(kb[SL][i]);
+          *reinterpret_cast<uint4*>(&v_lds[w][r * VP + vc * 8]) = expand8<T>(vb[SL][i]);
+        }
       }
       wave_lds_sync();
       f32x4_t sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KCH; ++j)
-        sc = Mfma<T>::run(k_lds[w][col * LPR + ((4 * j + kgrp) ^ kswz(col))], qop[j], sc);
+        sc = Mfma<T>::run(k_lds[w][col * CPR + ((4 * j + kgrp) ^ kswz(col))], qop[j], sc);
       const int tb = tile * kTile;
       float sv[4];
       float mt = -INFINITY;
