@@ -437,6 +437,7 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     // that are never written).
     const int w_pos0 = w_first >= rows ? -1 : pos_of(w_first / g);
 
+    bool first_tile = true;   // uniform over the wave
     if (tid == 0) bad_lds = 0;
     load_ids(kt_lo);
     load_tile(kt_lo);
@@ -500,7 +501,13 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
         }
         // Every row's first tile holds a visible key, so m_run is finite from
         // then on (rows past the chunk stay at -inf and are never written).
-        if (__any(jump)) {
+        // On the first tile the accumulators are still zero: the maxima are
+        // taken as they are, with nothing to rescale.
+        if (first_tile) {
+#pragma unroll
+          for (int rg = 0; rg < kRG; ++rg) m_run[rg] = mt[rg];
+          first_tile = false;
+        } else if (__any(jump)) {
 #pragma unroll
           for (int rg = 0; rg < kRG; ++rg) {
             const float mn = fmaxf(m_run[rg], mt[rg]);
@@ -564,11 +571,15 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
         if (kgrp == 0)   // ln(l * 2^m), m and l in log2 units
           p.lse[ra.state] = any_bad ? nan : (m_run[rg] + log2f(lsum)) * 0.69314718055994531f;
       } else {
+        // Channels 16j + 4*kgrp .. +3 of the row: one 8-byte store each.
+        const uint32_t nan2 = Pair<T>::pack(nan, nan);
 #pragma unroll
         for (int j = 0; j < D / 16; ++j) {
           S* o = (S*)p.out + ra.qoff + 16 * j + 4 * kgrp;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Cvt<T>::store(o + e, any_bad ? nan : acc[rg][j][e] * inv);
+          *reinterpret_cast<uint2*>(o) =
+              any_bad ? make_uint2(nan2, nan2)
+                      : make_uint2(Pair<T>::pack(acc[rg][j][0] * inv, acc[rg][j][1] * inv),
+                                   Pair<T>::pack(acc[rg][j][2] * inv, acc[rg][j][3] * inv));
         }
       }
     }
