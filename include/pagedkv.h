@@ -18,7 +18,8 @@
  *   not synchronise and they allocate no memory.
  * - Arguments are validated on the host before anything is launched; an invalid
  *   call launches nothing and leaves every buffer untouched.
- * - Layouts are dense row-major.  KV pools are per layer:
+ * - Layouts are dense row-major; q, out, new tokens and pools start on 16-byte
+ *   boundaries (any hipMalloc or torch allocation does).  KV pools are per layer:
  *       k_pool, v_pool : [num_blocks, block_size, num_kv_heads, head_dim]
  *   ([arch] "Production PyTorch Implementation", Step 2 cache tensors; one layer
  *   of the [pofe] "Minimal implementation" pool).  Token t of a sequence lives in

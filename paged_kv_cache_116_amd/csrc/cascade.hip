@@ -149,9 +149,11 @@ __global__ __launch_bounds__(kThreads) void cascade_combine(
         }
       }
       const float inv = den > 0.f ? 1.f / den : 0.f;
+      const float nan = __builtin_nanf("");
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        Cvt<T>::store(o + 8 * c + e, nan_in ? __builtin_nanf("") : v[e] * inv);
+      for (int e = 0; e < 8; e += 4)
+        Cvt<T>::store4(o + 8 * c + e, nan_in ? nan : v[e] * inv, nan_in ? nan : v[e + 1] * inv,
+                       nan_in ? nan : v[e + 2] * inv, nan_in ? nan : v[e + 3] * inv);
     }
   }
 }

@@ -537,10 +537,8 @@ __device__ __forceinline__ void emit_item(const AttnParams& p, const Segment& sg
   if (sg.final) {
     S* o = (S*)p.out + ((size_t)sg.s * p.num_q_heads + kv.h0 + h) * D + d;
     const float inv = 1.f / den;
-    Cvt<T>::store(o + 0, bad ? nan : num.x * inv);
-    Cvt<T>::store(o + 1, bad ? nan : num.y * inv);
-    Cvt<T>::store(o + 2, bad ? nan : num.z * inv);
-    Cvt<T>::store(o + 3, bad ? nan : num.w * inv);
+    Cvt<T>::store4(o, bad ? nan : num.x * inv, bad ? nan : num.y * inv, bad ? nan : num.z * inv,
+                   bad ? nan : num.w * inv);
     if (p.lse && d == 0)
       p.lse[(size_t)sg.s * p.num_q_heads + kv.h0 + h] = bad ? nan : lse_of(big_m, den);
   } else {
@@ -1094,10 +1092,7 @@ template <typename T>
 __device__ __forceinline__ void store4(const AttnParams& p, int s, int head, int d, float4 v) {
   using S = typename T::storage;
   S* o = (S*)p.out + ((size_t)s * p.num_q_heads + head) * p.head_dim + d;
-  Cvt<T>::store(o + 0, v.x);
-  Cvt<T>::store(o + 1, v.y);
-  Cvt<T>::store(o + 2, v.z);
-  Cvt<T>::store(o + 3, v.w);
+  Cvt<T>::store4(o, v.x, v.y, v.z, v.w);
 }
 
 template <typename T>

@@ -77,6 +77,8 @@ __device__ __forceinline__ uint16_t f32_to_f16_rne(float f) {
   return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// store4 writes four consecutive elements with one store (dst aligned to
+// four elements).
 template <typename T> struct Cvt;
 template <> struct Cvt<F32> {
   // Unpack the 4 floats of a 16-byte chunk.
@@ -85,6 +87,9 @@ template <> struct Cvt<F32> {
     out[2] = __uint_as_float(c.z); out[3] = __uint_as_float(c.w);
   }
   __device__ static __forceinline__ void store(float* dst, float v) { *dst = v; }
+  __device__ static __forceinline__ void store4(float* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+  }
 };
 template <> struct Cvt<BF16> {
   __device__ static __forceinline__ void unpack(const uint4& c, float* out) {
@@ -92,6 +97,11 @@ template <> struct Cvt<BF16> {
     out[4] = bf16_lo(c.z); out[5] = bf16_hi(c.z); out[6] = bf16_lo(c.w); out[7] = bf16_hi(c.w);
   }
   __device__ static __forceinline__ void store(uint16_t* dst, float v) { *dst = f32_to_bf16_rne(v); }
+  __device__ static __forceinline__ void store4(uint16_t* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<uint2*>(dst) =
+        make_uint2(f32_to_bf16_rne(a) | ((uint32_t)f32_to_bf16_rne(b) << 16),
+                   f32_to_bf16_rne(c) | ((uint32_t)f32_to_bf16_rne(d) << 16));
+  }
 };
 template <> struct Cvt<F16> {
   __device__ static __forceinline__ void unpack(const uint4& c, float* out) {
@@ -99,6 +109,11 @@ template <> struct Cvt<F16> {
     out[4] = f16_lo(c.z); out[5] = f16_hi(c.z); out[6] = f16_lo(c.w); out[7] = f16_hi(c.w);
   }
   __device__ static __forceinline__ void store(uint16_t* dst, float v) { *dst = f32_to_f16_rne(v); }
+  __device__ static __forceinline__ void store4(uint16_t* dst, float a, float b, float c, float d) {
+    *reinterpret_cast<uint2*>(dst) =
+        make_uint2(f32_to_f16_rne(a) | ((uint32_t)f32_to_f16_rne(b) << 16),
+                   f32_to_f16_rne(c) | ((uint32_t)f32_to_f16_rne(d) << 16));
+  }
 };
 
 __device__ __forceinline__ uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
