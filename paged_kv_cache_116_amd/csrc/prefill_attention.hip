@@ -355,12 +355,11 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
     const uint64_t blk_bytes = tok_bytes << p.log2_b;
     const int bmask = (1 << p.log2_b) - 1;
     const uint32_t lane_off = (uint32_t)(kvh * D + 8 * (lane % LPR)) * KVB;
-    // A wave's lanes cover RPW consecutive rows of each chunk, starting at a
-    // multiple of RPW; with B >= RPW (kWB) they lie in one block, whose id is
-    // then uniform over the wave: a scalar load, and loads addressed as a
-    // scalar base plus a 32-bit lane offset.  Smaller blocks take per-lane
-    // ids.
-    constexpr int RPW = 64 / LPR;
+    // A wave's lanes cover 64 / LPR consecutive rows of each chunk, starting
+    // at a multiple of 64 / LPR; with B >= 64 / LPR (kWB) they lie in one
+    // block, whose id is then uniform over the wave: a scalar load, and loads
+    // addressed as a scalar base plus a 32-bit lane offset.  Smaller blocks
+    // take per-lane ids.
     static_assert(64 % LPR == 0, "lane layout");
     auto wave_row0 = [&](int u) { return (64 * w + kThreads * u) / LPR; };
     // Block ids of the tile loaded next, fetched one tile ahead of its data
