@@ -66,7 +66,9 @@ enum pkv_status {
   PKV_ERR_NO_FREE_BLOCK = -3, /* host block manager: free list empty ([pofe] "Minimal
                                  implementation" raises MemoryError for a preemption)   */
   PKV_ERR_WORKSPACE = -4,     /* workspace missing or smaller than required             */
-  PKV_ERR_HIP = -5            /* a HIP launch or runtime call failed                    */
+  PKV_ERR_HIP = -5,           /* a HIP launch or runtime call failed                    */
+  PKV_ERR_ORDER = -6          /* decode phase entry points called out of order for one
+                                 workspace, or with arguments unlike its plan's         */
 };
 
 /* Name of a status code; never NULL, static storage. */
@@ -228,6 +230,14 @@ int paged_decode_attention_with(int kernel, void* out, const void* q, const void
  *    second launch needs a new plan;
  *  - merge: the range where a split sequence starts combines its partial
  *    states with the rule above and writes the output.
+ * The library holds each workspace (by address) to that order on the host:
+ * partitions needs a plan that no partitions launch has used yet, merge needs
+ * the partitions launch of that plan, and both need the plan's kernel, dtype,
+ * out, block_tables, context_lens, sizes, partition_tokens and
+ * workspace_bytes; otherwise PKV_ERR_ORDER and nothing is launched.  A new
+ * plan replaces an unused one; any whole attention or decode-step call on the
+ * workspace leaves it needing a plan.  The record follows the calls, not the
+ * stream, so the three calls must also reach the stream in this order.
  */
 int paged_decode_attention_plan(int kernel, void* out, const void* q, const void* k_pool,
                                 const void* v_pool, const int32_t* block_tables,

@@ -31,6 +31,7 @@ PKV_ERR_UNSUPPORTED = -2
 PKV_ERR_NO_FREE_BLOCK = -3
 PKV_ERR_WORKSPACE = -4
 PKV_ERR_HIP = -5
+PKV_ERR_ORDER = -6   # decode phases out of order for a workspace
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
 PKV_ATTN_AUTO, PKV_ATTN_VALU, PKV_ATTN_MFMA = 0, 1, 2
@@ -347,7 +348,9 @@ def _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partit
 def paged_decode_attention_plan(kernel, out, q, k_pool, v_pool, block_tables, context_lens, *,
                                 scale=None, partition_tokens=0, workspace, stream=None):
     """First launch of paged_decode_attention_with(kernel, ...) (work plan,
-    empty-row fills).  The three phases must be given the same kernel."""
+    empty-row fills).  The three phases must be given the same kernel and
+    arguments, in the order plan, partitions, merge; the library raises
+    PagedKVError (PKV_ERR_ORDER) otherwise."""
     args = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale,
                       partition_tokens, workspace, stream)
     _check(_lib.paged_decode_attention_plan(int(kernel), *args), "paged_decode_attention_plan")

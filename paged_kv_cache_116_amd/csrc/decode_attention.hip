@@ -1359,6 +1359,61 @@ inline const void* pick_partition(int family, int dtype, int D, int G, bool stre
 
 enum Phase { kPhasePlan = 1, kPhasePartitions = 2, kPhaseMerge = 4, kPhaseAll = 7 };
 
+// What a plan was made for: the arguments that shape its schedule, its
+// empty-row fills and the workspace layout.  The later phases of the same
+// step must agree on all of them.
+struct PlanKey {
+  int kernel, dtype, kv_fp8, num_seqs, num_blocks, block_size, max_blocks_per_seq;
+  int num_q_heads, num_kv_heads, head_dim, partition_tokens;
+  const void* out;
+  const void* context_lens;
+  const void* block_tables;
+  size_t workspace_bytes;
+  bool operator==(const PlanKey& o) const {
+    return kernel == o.kernel && dtype == o.dtype && kv_fp8 == o.kv_fp8 &&
+           num_seqs == o.num_seqs && num_blocks == o.num_blocks &&
+           block_size == o.block_size && max_blocks_per_seq == o.max_blocks_per_seq &&
+           num_q_heads == o.num_q_heads && num_kv_heads == o.num_kv_heads &&
+           head_dim == o.head_dim && partition_tokens == o.partition_tokens && out == o.out &&
+           context_lens == o.context_lens && block_tables == o.block_tables &&
+           workspace_bytes == o.workspace_bytes;
+  }
+};
+
+// The plan resets the claim counter and writes the schedule that exactly one
+// partitions launch consumes, and the merge reads what that launch left, so
+// the phase entry points hold each workspace to plan -> partitions -> merge
+// with one PlanKey.  The host records, per workspace address, the phase the
+// last call left it ready for; a whole call (all three phases) leaves it
+// ready for a plan.  Returns PKV_OK and advances the record, or
+// PKV_ERR_ORDER and leaves it as it was.
+int advance_phase(void* workspace, int phase, const PlanKey& key) {
+  struct Expect {
+    int next;   // kPhasePartitions or kPhaseMerge
+    PlanKey key;
+  };
+  static std::mutex mu;
+  static std::unordered_map<const void*, Expect> state;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = state.find(workspace);
+  switch (phase) {
+    case kPhaseAll:
+      if (it != state.end()) state.erase(it);
+      return PKV_OK;
+    case kPhasePlan:   // a new plan replaces one that was never used
+      state[workspace] = Expect{kPhasePartitions, key};
+      return PKV_OK;
+    default:
+      if (it == state.end() || it->second.next != phase || !(it->second.key == key))
+        return PKV_ERR_ORDER;
+      if (phase == kPhasePartitions)
+        it->second.next = kPhaseMerge;
+      else
+        state.erase(it);
+      return PKV_OK;
+  }
+}
+
 struct Launch {
   AttnParams p;
   const void* part_fn;
@@ -1503,6 +1558,13 @@ int decode_attention_impl(int phase, int kernel, void* out, const void* q, const
                          num_kv_heads, head_dim, scale, partition_tokens, workspace,
                          workspace_bytes, dtype, &L, kv_fp8, k_scale, v_scale);
   if (st != PKV_OK || num_seqs == 0) return st;
+  const PlanKey key{kernel,       dtype,           kv_fp8 ? 1 : 0, num_seqs,
+                    num_blocks,   block_size,      max_blocks_per_seq,
+                    num_q_heads,  num_kv_heads,    head_dim,
+                    partition_tokens, out,         context_lens,
+                    block_tables, workspace_bytes};
+  const int order = advance_phase(workspace, phase, key);
+  if (order != PKV_OK) return order;
   L.p.k_new = (const char*)k_new;
   L.p.lse = lse;
   L.p.v_new = (const char*)v_new;

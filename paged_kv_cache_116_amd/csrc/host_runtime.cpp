@@ -29,6 +29,7 @@ extern "C" const char* pkv_status_string(int status) {
     case PKV_ERR_NO_FREE_BLOCK: return "PKV_ERR_NO_FREE_BLOCK";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_ORDER: return "PKV_ERR_ORDER";
     default: return "PKV_ERR_UNKNOWN";
   }
 }

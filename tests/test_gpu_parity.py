@@ -262,6 +262,58 @@ def test_phased_entry_points_match_oracle(kernel, part):
         check_close(out, ref, w.dtype, f"phased {kernel} P={part}")
 
 
+def test_phased_entry_points_refuse_out_of_order_calls():
+    # One plan serves one partitions launch, and the merge needs that launch:
+    # every call below that breaks the order, or changes an argument the plan
+    # was made for, is refused on the host before anything is launched.
+    w = workloads.make_workload(3, **SMALL[3])
+    dev = to_dev(w)
+    ref = oracle_step(w, w.k_pool, w.v_pool)
+    k = pkv.PKV_ATTN_MFMA
+    pkv.paged_kv_append(dev["k_pool"], dev["v_pool"], dev["k_new"], dev["v_new"], dev["tables"],
+                        dev["lens_pre"])
+    out = torch.empty_like(dev["q"])
+    ws = torch.empty(pkv.paged_decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim,
+                                                      w.max_blocks * w.block_size, 0),
+                     dtype=torch.uint8, device="cuda")
+    args = (out, dev["q"], dev["k_pool"], dev["v_pool"], dev["tables"], dev["lens"])
+    kw = dict(scale=w.scale, workspace=ws)
+
+    def refused(fn, *a, **extra):
+        with pytest.raises(pkv.PagedKVError) as e:
+            fn(*a, **{**kw, **extra})
+        assert e.value.status == pkv.PKV_ERR_ORDER
+
+    plan = pkv.paged_decode_attention_plan
+    parts = pkv.paged_decode_attention_partitions
+    merge = pkv.paged_decode_attention_merge
+    refused(parts, k, *args)                       # no plan yet
+    refused(merge, k, *args)
+    plan(k, *args, **kw)
+    refused(merge, k, *args)                       # merge before partitions
+    refused(parts, pkv.PKV_ATTN_VALU, *args)       # another kernel's grouping
+    refused(parts, k, *args, partition_tokens=48)  # another schedule
+    refused(parts, k, torch.empty_like(out), *args[1:])   # another output
+    out.fill_(7.0)
+    parts(k, *args, **kw)
+    refused(parts, k, *args)                       # the plan is used up
+    merge(k, *args, **kw)
+    refused(merge, k, *args)                       # and so is the merge
+    torch.cuda.synchronize()
+    check_close(out, ref, w.dtype, "phased after refusals")
+    # A whole call on the workspace consumes its own plan.
+    plan(k, *args, **kw)
+    pkv.paged_decode_attention_with(k, *args, **kw)
+    refused(parts, k, *args)
+    out.fill_(7.0)
+    plan(k, *args, **kw)
+    plan(k, *args, **kw)                           # a new plan replaces an unused one
+    parts(k, *args, **kw)
+    merge(k, *args, **kw)
+    torch.cuda.synchronize()
+    check_close(out, ref, w.dtype, "phased after a replaced plan")
+
+
 @pytest.mark.parametrize("B", [1, 2, 4, 8, 16, 32, 64, 128])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_attention_block_sizes(B, dtype):

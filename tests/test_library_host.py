@@ -36,7 +36,8 @@ def test_every_declared_function_is_exported():
 
 def test_status_strings():
     for code, name in [(0, "PKV_OK"), (-1, "PKV_ERR_INVALID_ARG"), (-2, "PKV_ERR_UNSUPPORTED"),
-                       (-3, "PKV_ERR_NO_FREE_BLOCK"), (-4, "PKV_ERR_WORKSPACE"), (-5, "PKV_ERR_HIP")]:
+                       (-3, "PKV_ERR_NO_FREE_BLOCK"), (-4, "PKV_ERR_WORKSPACE"), (-5, "PKV_ERR_HIP"),
+                       (-6, "PKV_ERR_ORDER")]:
         assert pkv.pkv_status_string(code) == name
     assert pkv.pkv_status_string(-99) == "PKV_ERR_UNKNOWN"
 
