@@ -22,6 +22,13 @@ name no FP8 format and no scale convention.  Readings taken here:
   other than 1 every finite code survives dequantise then quantise, the
   code of 1.0 stands for the scale, and a value comes back within half an
   E4M3 step (times the scale) of what was written.
+* Per-head scales (the other option the survey of FP8 caches names; the
+  pages are silent): one float32 per KV head and pool, head h's codes
+  following the rule above with its own scale.  A head whose scale is not
+  finite and positive has no defined codes: its rows store the NaN code
+  0x7F.  Pinned by reduction to the per-pool rule when every head has the
+  same scale, by the code of 1.0 in head h standing for scale h, and by the
+  round trip at distinct scales per head.
 """
 
 from __future__ import annotations
@@ -94,6 +101,49 @@ def dequantise(codes: np.ndarray, scale: float) -> np.ndarray:
     return DECODE_TABLE[np.asarray(codes, dtype=np.uint8)] * np.float64(np.float32(scale))
 
 
+NAN_CODE = 0x7F
+
+
+def scale_is_valid(scale) -> bool:
+    s = float(np.float32(scale))
+    return math.isfinite(s) and s > 0.0
+
+
+def quantise_heads(x: np.ndarray, scales) -> np.ndarray:
+    """Codes of x [..., H_kv, D] with per-head scales [H_kv]: head h is
+    quantise(x[..., h, :], scales[h]), or all NAN_CODE when scales[h] is not
+    finite and positive."""
+    x = np.asarray(x, dtype=np.float32)
+    scales = np.asarray(scales, dtype=np.float32).reshape(-1)
+    if x.shape[-2] != scales.shape[0]:
+        raise ValueError("one scale per KV head")
+    out = np.empty(x.shape, dtype=np.uint8)
+    for h, sc in enumerate(scales):
+        out[..., h, :] = quantise(x[..., h, :], sc) if scale_is_valid(sc) else NAN_CODE
+    return out
+
+
+def dequantise_heads(codes: np.ndarray, scales) -> np.ndarray:
+    """float64 values of codes [..., H_kv, D]: decode(code) * scales[h] in
+    head h (NaN throughout a head whose scale is not finite and positive)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.float32).reshape(-1)
+    if codes.shape[-2] != scales.shape[0]:
+        raise ValueError("one scale per KV head")
+    out = np.empty(codes.shape, dtype=np.float64)
+    for h, sc in enumerate(scales):
+        out[..., h, :] = dequantise(codes[..., h, :], sc) if scale_is_valid(sc) else math.nan
+    return out
+
+
+def _quantise_row(x: np.ndarray, scale) -> np.ndarray:
+    """A [H_kv, D] row: per-pool scale (a number) or per-head scales (a
+    sequence of H_kv numbers)."""
+    if np.ndim(scale) == 0:
+        return quantise(x, scale)
+    return quantise_heads(x, scale)
+
+
 def append_token_fp8(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
                      v_new: np.ndarray, tables: np.ndarray, lens_pre, block_size: int,
                      k_scale: float, v_scale: float):
@@ -103,6 +153,8 @@ def append_token_fp8(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
 
     k_new, v_new: [S, H_kv, D] (float32-representable values); pools uint8
     [N, B, H_kv, D]; lens_pre: [S] (negative: padding row, no write).
+    k_scale, v_scale: one number per pool, or one per KV head ([H_kv],
+    quantise_heads).
     """
     k_out = k_pool.copy()
     v_out = v_pool.copy()
@@ -114,8 +166,8 @@ def append_token_fp8(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray,
         physical, offset = resolve(tables[s], block_size, length)
         if not (0 <= physical < num_blocks):
             raise IndexError(f"sequence {s}: block id {physical} outside the pool")
-        k_out[physical, offset] = quantise(k_new[s], k_scale)
-        v_out[physical, offset] = quantise(v_new[s], v_scale)
+        k_out[physical, offset] = _quantise_row(k_new[s], k_scale)
+        v_out[physical, offset] = _quantise_row(v_new[s], v_scale)
     return k_out, v_out
 
 

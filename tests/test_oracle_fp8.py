@@ -223,3 +223,81 @@ def test_fp8_append_tokens_equals_repeated_single_appends_and_plain_slots():
                                      fp8.quantise(v_new, vs).astype(np.float64),
                                      tables, lens_pre, cu, B)
     assert np.array_equal(kc, pk.astype(np.uint8)) and np.array_equal(vc, pv.astype(np.uint8))
+
+
+# --- per-head scales ---------------------------------------------------------
+
+def test_per_head_scales_reduce_to_the_per_pool_rule():
+    # Every head at the same scale: exactly the per-pool codes and values,
+    # which the round-trip and torch pins above fix.
+    rng = np.random.default_rng(31)
+    x = rng.normal(0, 4, (5, 3, 16)).astype(np.float32)
+    for s in SCALES:
+        q = fp8.quantise_heads(x, [s] * 3)
+        assert np.array_equal(q, fp8.quantise(x, s))
+        assert np.array_equal(fp8.dequantise_heads(q, [s] * 3), fp8.dequantise(q, s))
+
+
+def per_head_convention_holds(quantise_heads, dequantise_heads) -> bool:
+    """Distinct scales per head: (1) the code of 1.0 in head h stands for
+    scale h itself, whatever the other axes; (2) every finite code survives
+    dequantise -> quantise in every head."""
+    scales = np.array([0.05, 3.0, 0.0625, 0.7], np.float32)
+    H = len(scales)
+    ones = np.full((2, 3, H, 4), 0x38, np.uint8)
+    vals = dequantise_heads(ones, scales)
+    for h in range(H):
+        if not np.all(vals[:, :, h, :] == np.float64(scales[h])):
+            return False
+    finite = np.array([c for c in range(256) if not math.isnan(fp8.decode_e4m3(c))], np.uint8)
+    codes = np.stack([np.roll(finite, 37 * h) for h in range(H)], axis=0)[None]   # [1, H, 254]
+    return np.array_equal(quantise_heads(dequantise_heads(codes, scales), scales), codes)
+
+
+def test_per_head_scale_convention():
+    assert per_head_convention_holds(fp8.quantise_heads, fp8.dequantise_heads)
+
+
+def test_planted_per_head_mistakes_fail():
+    # Scales applied along the wrong axis (the channel axis instead of the
+    # head axis, or the heads in reverse order) must fail the pin.
+    def deq_reversed(codes, scales):
+        return fp8.dequantise_heads(codes, np.asarray(scales)[::-1])
+
+    def deq_channel_axis(codes, scales):
+        codes = np.asarray(codes, np.uint8)
+        sc = np.asarray(scales, np.float32)
+        return fp8.DECODE_TABLE[codes] * np.resize(sc, codes.shape[-1]).astype(np.float64)
+
+    assert not per_head_convention_holds(fp8.quantise_heads, deq_reversed)
+    assert not per_head_convention_holds(fp8.quantise_heads, deq_channel_axis)
+
+
+def test_per_head_invalid_scale_gives_nan_codes_in_that_head_only():
+    rng = np.random.default_rng(32)
+    x = rng.normal(0, 1, (4, 3, 8)).astype(np.float32)
+    for bad in (0.0, -1.0, math.nan, math.inf):
+        q = fp8.quantise_heads(x, [0.5, bad, 2.0])
+        assert np.all(q[:, 1, :] == 0x7F)
+        assert np.array_equal(q[:, 0, :], fp8.quantise(x[:, 0, :], 0.5))
+        assert np.array_equal(q[:, 2, :], fp8.quantise(x[:, 2, :], 2.0))
+        v = fp8.dequantise_heads(q, [0.5, bad, 2.0])
+        assert np.all(np.isnan(v[:, 1, :])) and not np.any(np.isnan(v[:, 0, :]))
+
+
+def test_fp8_append_with_per_head_scales_is_the_per_pool_append_head_by_head():
+    # Head h of the per-head append equals head h of the per-pool append at
+    # scale h (pinned above against the plain append's slots).
+    rng = np.random.default_rng(33)
+    N, B, H, D = 10, 4, 3, 8
+    tables = np.array([[4, 1, 9], [2, 6, -1]])
+    lens_pre = np.array([6, 3])
+    k_new = rng.normal(0, 2, (2, H, D)).astype(np.float32)
+    v_new = rng.normal(0, 5, (2, H, D)).astype(np.float32)
+    kp = rng.integers(0, 256, (N, B, H, D)).astype(np.uint8)
+    vp = rng.integers(0, 256, (N, B, H, D)).astype(np.uint8)
+    ks, vs = [0.05, 1.0, 3.0], [0.7, 0.0625, 2.0]
+    k2, v2 = fp8.append_token_fp8(kp, vp, k_new, v_new, tables, lens_pre, B, ks, vs)
+    for h in range(H):
+        kh, vh = fp8.append_token_fp8(kp, vp, k_new, v_new, tables, lens_pre, B, ks[h], vs[h])
+        assert np.array_equal(k2[:, :, h], kh[:, :, h]) and np.array_equal(v2[:, :, h], vh[:, :, h])
