@@ -454,6 +454,52 @@ int paged_decode_step_fp8(int kernel, void* out, const void* q, void* k_pool, vo
                           int partition_tokens, void* workspace, size_t workspace_bytes,
                           int dtype, void* stream);
 
+/*
+ * Per-head FP8 scales: the three calls above with one float32 scale per KV
+ * head and pool instead of one per pool.  The pages fix no scale convention
+ * ([pofe] "Fine-tuned models and adapters" only says FP8 halves the bytes of
+ * a block); per-tensor and per-head scales are the two usual choices, and
+ * these calls take the second:
+ *   k_scales, v_scales : device float32 [num_kv_heads], owned by the caller,
+ *                        read by the kernels (not copied); head h's codes
+ *                        follow the per-pool rule above with k_scales[h] /
+ *                        v_scales[h].  NULL with num_seqs > 0 gives
+ *                        PKV_ERR_INVALID_ARG.
+ * The host cannot see device values, so an entry that is not finite and > 0
+ * is handled on the device: the append stores the NaN code 0x7F in every
+ * element of that head of that pool, and attention writes NaN to the rows of
+ * that head's query heads (either of the head's two scales being unusable is
+ * enough).  Everything
+ * else as paged_kv_append_fp8, paged_decode_attention_fp8 and
+ * paged_decode_step_fp8; with all entries equal to s the results are bit
+ * for bit those of the per-pool calls at scale s.  Chunked prefill and the
+ * cascade take per-pool scales only.
+ */
+int paged_kv_append_fp8_per_head(void* k_pool, void* v_pool, const void* k_new,
+                                 const void* v_new, const int32_t* block_tables,
+                                 int max_blocks_per_seq, const int32_t* context_lens_pre,
+                                 int num_seqs, int num_blocks, int block_size, int num_kv_heads,
+                                 int head_dim, int new_dtype, const float* k_scales,
+                                 const float* v_scales, void* stream);
+int paged_decode_attention_fp8_per_head(int kernel, void* out, const void* q,
+                                        const void* k_pool, const void* v_pool,
+                                        const int32_t* block_tables, int max_blocks_per_seq,
+                                        const int32_t* context_lens, int num_seqs,
+                                        int num_blocks, int block_size, int num_q_heads,
+                                        int num_kv_heads, int head_dim, float scale,
+                                        const float* k_scales, const float* v_scales,
+                                        int partition_tokens, void* workspace,
+                                        size_t workspace_bytes, int dtype, void* stream);
+int paged_decode_step_fp8_per_head(int kernel, void* out, const void* q, void* k_pool,
+                                   void* v_pool, const void* k_new, const void* v_new,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int num_seqs, int num_blocks,
+                                   int block_size, int num_q_heads, int num_kv_heads,
+                                   int head_dim, float scale, const float* k_scales,
+                                   const float* v_scales, int partition_tokens,
+                                   void* workspace, size_t workspace_bytes, int dtype,
+                                   void* stream);
+
 /* ------------------------------------------------------------------------- */
 /* Swap: preemption to host memory                                           */
 /* ------------------------------------------------------------------------- */

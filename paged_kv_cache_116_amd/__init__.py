@@ -80,6 +80,13 @@ _sig("paged_kv_append_fp8", _i32,
 _ATTN_ARGS_FP8 = _ATTN_ARGS[:14] + [_f32, _f32] + _ATTN_ARGS[14:]
 _sig("paged_decode_attention_fp8", _i32, [_i32] + _ATTN_ARGS_FP8)
 _sig("paged_decode_step_fp8", _i32, [_i32, _p, _p, _p, _p, _p, _p] + _ATTN_ARGS_FP8[4:])
+# Per-head scales: device float32 arrays in place of the two scale floats.
+_sig("paged_kv_append_fp8_per_head", _i32,
+     [_p, _p, _p, _p, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p])
+_ATTN_ARGS_FP8_HEADS = _ATTN_ARGS[:14] + [_p, _p] + _ATTN_ARGS[14:]
+_sig("paged_decode_attention_fp8_per_head", _i32, [_i32] + _ATTN_ARGS_FP8_HEADS)
+_sig("paged_decode_step_fp8_per_head", _i32,
+     [_i32, _p, _p, _p, _p, _p, _p] + _ATTN_ARGS_FP8_HEADS[4:])
 _sig("paged_kv_append_tokens", _i32,
      [_p, _p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _i32, _i32, _i32, _p])
 _sig("paged_prefill_attention", _i32,
@@ -743,6 +750,74 @@ def paged_decode_step_fp8(out, q, k_pool, v_pool, k_new, v_new, block_tables, co
                                       _dev(k_new, "k_new", q.dtype), _dev(v_new, "v_new", q.dtype),
                                       *a[4:14], float(k_scale), float(v_scale), *a[14:]),
            "paged_decode_step_fp8")
+
+
+def _head_scales(scales, name, num_kv_heads, device):
+    if not (torch.is_tensor(scales) and scales.dtype == torch.float32 and
+            scales.shape == (num_kv_heads,) and scales.device == device):
+        raise ValueError(f"{name} must be a float32 tensor [num_kv_heads] on the pools' device")
+    return _dev(scales, name, torch.float32)
+
+
+def paged_kv_append_fp8_per_head(k_pool, v_pool, k_new, v_new, block_tables, context_lens_pre,
+                                 k_scales, v_scales, *, stream=None):
+    """paged_kv_append_fp8 with one scale per KV head: k_scales / v_scales are
+    float32 device tensors [num_kv_heads]; head h's codes are e4m3(x /
+    scales[h]), and a head whose scale is not finite and positive stores NaN
+    codes."""
+    _fp8_pools(k_pool, v_pool)
+    n, b, h, d, _ = _pool_dims(k_pool, v_pool)
+    s = k_new.shape[0]
+    if k_new.shape != (s, h, d) or v_new.shape != (s, h, d) or v_new.dtype != k_new.dtype:
+        raise ValueError("k_new / v_new must be [num_seqs, kv_heads, head_dim] of one dtype")
+    if k_new.dtype not in _DTYPE_CODE or _DTYPE_CODE[k_new.dtype] == PKV_FP8_E4M3:
+        raise TypeError(f"new-token dtype {k_new.dtype} is not supported")
+    if block_tables.dim() != 2 or block_tables.shape[0] != s or context_lens_pre.shape != (s,):
+        raise ValueError("block_tables [num_seqs, max_blocks] and context_lens_pre [num_seqs]")
+    ks = _head_scales(k_scales, "k_scales", h, k_pool.device)
+    vs = _head_scales(v_scales, "v_scales", h, k_pool.device)
+    _check(_lib.paged_kv_append_fp8_per_head(
+        _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"), _dev(k_new, "k_new"),
+        _dev(v_new, "v_new"), _dev(block_tables, "block_tables", torch.int32),
+        block_tables.shape[1], _dev(context_lens_pre, "context_lens_pre", torch.int32), s, n, b,
+        h, d, _DTYPE_CODE[k_new.dtype], ks, vs, _stream(stream)),
+        "paged_kv_append_fp8_per_head")
+
+
+def paged_decode_attention_fp8_per_head(out, q, k_pool, v_pool, block_tables, context_lens,
+                                        k_scales, v_scales, *, kernel=0, scale=None,
+                                        partition_tokens=0, workspace=None, stream=None):
+    """paged_decode_attention_fp8 with one scale per KV head (float32 device
+    tensors [num_kv_heads]); the rows of a head whose scale is not finite and
+    positive are NaN."""
+    _fp8_pools(k_pool, v_pool)
+    a = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partition_tokens,
+                   workspace, stream, io_dtype=q.dtype)
+    h = k_pool.shape[2]
+    ks = _head_scales(k_scales, "k_scales", h, k_pool.device)
+    vs = _head_scales(v_scales, "v_scales", h, k_pool.device)
+    _check(_lib.paged_decode_attention_fp8_per_head(int(kernel), *a[:14], ks, vs, *a[14:]),
+           "paged_decode_attention_fp8_per_head")
+
+
+def paged_decode_step_fp8_per_head(out, q, k_pool, v_pool, k_new, v_new, block_tables,
+                                   context_lens, k_scales, v_scales, *, kernel=0, scale=None,
+                                   partition_tokens=0, workspace=None, stream=None):
+    """paged_decode_step_fp8 with one scale per KV head, as
+    paged_kv_append_fp8_per_head then paged_decode_attention_fp8_per_head."""
+    _fp8_pools(k_pool, v_pool)
+    a = _attn_args(out, q, k_pool, v_pool, block_tables, context_lens, scale, partition_tokens,
+                   workspace, stream, io_dtype=q.dtype)
+    s, h, d = q.shape[0], k_pool.shape[2], k_pool.shape[3]
+    if k_new.shape != (s, h, d) or v_new.shape != (s, h, d):
+        raise ValueError("k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    ks = _head_scales(k_scales, "k_scales", h, k_pool.device)
+    vs = _head_scales(v_scales, "v_scales", h, k_pool.device)
+    _check(_lib.paged_decode_step_fp8_per_head(int(kernel), a[0], a[1], a[2], a[3],
+                                               _dev(k_new, "k_new", q.dtype),
+                                               _dev(v_new, "v_new", q.dtype), *a[4:14], ks, vs,
+                                               *a[14:]),
+           "paged_decode_step_fp8_per_head")
 
 
 def paged_kv_append_tokens_fp8(k_pool, v_pool, k_new, v_new, cu_seqlens, block_tables,

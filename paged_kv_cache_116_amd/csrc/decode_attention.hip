@@ -157,6 +157,10 @@ struct AttnParams {
   int kv_fp8;        // pools hold E4M3FN codes
   float k_scale;     // FP8 pools: value = code * scale (the decode-step append divides)
   float v_scale;     // multiplies the weighted V sum (1 unless FP8)
+  // FP8 pools with one scale per KV head: [num_kv_heads] each (device), in
+  // place of k_scale / v_scale (both 1 then); nullptr for per-pool scales.
+  const float* k_scales;
+  const float* v_scales;
   float* lse;        // optional [S, Hq]: natural log of each head's softmax normaliser
 };
 
@@ -219,10 +223,17 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
           float kf[8], vf[8];
           Cvt<T>::unpack(load16(p.k_new + src), kf);
           Cvt<T>::unpack(load16(p.v_new + src), vf);
+          float ks = p.k_scale, vs = p.v_scale;
+          if (p.k_scales) {   // the chunk's KV head (chunks never straddle heads)
+            const int hh = E * ch / p.head_dim;
+            ks = p.k_scales[hh];
+            vs = p.v_scales[hh];
+          }
+          const bool k_ok = scale_ok(ks), v_ok = scale_ok(vs);
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            kf[e] = kf[e] / p.k_scale;
-            vf[e] = vf[e] / p.v_scale;
+            kf[e] = k_ok ? kf[e] / ks : __builtin_nanf("");
+            vf[e] = v_ok ? vf[e] / vs : __builtin_nanf("");
           }
           *reinterpret_cast<uint2*>((char*)p.k_pool + elem) =
               make_uint2(e4m3_encode4(kf[0], kf[1], kf[2], kf[3]),
@@ -541,10 +552,15 @@ __device__ __forceinline__ void emit_item(const AttnParams& p, const Segment& sg
   }
   const float nan = __builtin_nanf("");
   if constexpr (kScaleV) {   // FP8 pools: the V codes' scale
-    num.x *= p.v_scale;
-    num.y *= p.v_scale;
-    num.z *= p.v_scale;
-    num.w *= p.v_scale;
+    float vs = p.v_scale;
+    if (p.v_scales) {
+      vs = p.v_scales[kv.kvh];
+      if (!scale_ok(vs) || !scale_ok(p.k_scales[kv.kvh])) bad = 1;
+    }
+    num.x *= vs;
+    num.y *= vs;
+    num.z *= vs;
+    num.w *= vs;
   }
   if (sg.final) {
     S* o = (S*)p.out + ((size_t)sg.s * p.num_q_heads + kv.h0 + h) * D + d;
@@ -719,6 +735,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
     const int L = sg.L;
     const int last = L - 1;
     const WaveKv kv = wave_kv(p, sg.qd, kw);
+    // Score scale in log2 units.  FP8 pools with per-head scales fold in the
+    // KV head's key scale here (an unusable one leaves the factor 1, and the
+    // head's rows come out NaN at the end of the segment).
+    float sl2 = p.scale_log2;
+    if constexpr (kF8) {
+      if (p.k_scales && kv.live) {
+        const float ks = p.k_scales[kv.kvh];
+        if (scale_ok(ks)) sl2 *= ks;
+      }
+    }
 
     // B operand: query head `col` of this group, channels 32j + 8*kgrp .. +7.
     uint4 qop[KCH];
@@ -821,7 +847,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_partition_mfma(const AttnPar
       float mt = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[i] = (tb + 4 * kgrp + i < L) ? sc[i] * p.scale_log2 : -INFINITY;
+        sv[i] = (tb + 4 * kgrp + i < L) ? sc[i] * sl2 : -INFINITY;
         mt = fmaxf(mt, sv[i]);
       }
       mt = max_xor32(max_xor16(mt));
@@ -1425,7 +1451,8 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
             int num_seqs, int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
             int head_dim, float scale, int partition_tokens, void* workspace,
             size_t workspace_bytes, int dtype, Launch* L, bool kv_fp8 = false,
-            float k_scale = 1.f, float v_scale = 1.f) {
+            float k_scale = 1.f, float v_scale = 1.f, const float* k_scales = nullptr,
+            const float* v_scales = nullptr) {
   int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, dtype);
   if (st != PKV_OK) return st;
   if (!supported_dtype(dtype)) return PKV_ERR_UNSUPPORTED;   // q / out element type
@@ -1464,6 +1491,8 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
   const long long kvg = (long long)num_kv_heads * head_groups;
   // Tile counts are 32-bit on the device.
   if ((long long)num_seqs * ((max_len + kTile - 1) / kTile) * kvg >= (1LL << 31))
+    return PKV_ERR_INVALID_ARG;
+  if ((k_scales == nullptr) != (v_scales == nullptr) || (k_scales && !kv_fp8))
     return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
@@ -1525,6 +1554,9 @@ int prepare(int kernel, void* out, const void* q, const void* k_pool, const void
   p.kv_fp8 = kv_fp8 ? 1 : 0;
   p.k_scale = kv_fp8 ? k_scale : 1.f;
   p.v_scale = kv_fp8 ? v_scale : 1.f;
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
+  p.lse = nullptr;
   L->part_fn = fn;
   return PKV_OK;
 }
@@ -1551,12 +1583,14 @@ int decode_attention_impl(int phase, int kernel, void* out, const void* q, const
                           size_t workspace_bytes, int dtype, void* stream,
                           const void* k_new = nullptr, const void* v_new = nullptr,
                           bool kv_fp8 = false, float k_scale = 1.f, float v_scale = 1.f,
-                          float* lse = nullptr) {
+                          float* lse = nullptr, const float* k_scales = nullptr,
+                          const float* v_scales = nullptr) {
   Launch L;
   const int st = prepare(kernel, out, q, k_pool, v_pool, block_tables, max_blocks_per_seq,
                          context_lens, num_seqs, num_blocks, block_size, num_q_heads,
                          num_kv_heads, head_dim, scale, partition_tokens, workspace,
-                         workspace_bytes, dtype, &L, kv_fp8, k_scale, v_scale);
+                         workspace_bytes, dtype, &L, kv_fp8, k_scale, v_scale, k_scales,
+                         v_scales);
   if (st != PKV_OK || num_seqs == 0) return st;
   const PlanKey key{kernel,       dtype,           kv_fp8 ? 1 : 0, num_seqs,
                     num_blocks,   block_size,      max_blocks_per_seq,
@@ -1749,6 +1783,35 @@ extern "C" int paged_decode_step_fp8(int kernel, void* out, const void* q, void*
                                     block_size, num_q_heads, num_kv_heads, head_dim, scale,
                                     partition_tokens, workspace, workspace_bytes, dtype, stream,
                                     k_new, v_new, true, k_scale, v_scale);
+}
+
+extern "C" int paged_decode_attention_fp8_per_head(
+    int kernel, void* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+    int num_seqs, int num_blocks, int block_size, int num_q_heads, int num_kv_heads,
+    int head_dim, float scale, const float* k_scales, const float* v_scales,
+    int partition_tokens, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (num_seqs > 0 && (!k_scales || !v_scales)) return PKV_ERR_INVALID_ARG;
+  return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, out, q, k_pool, v_pool, block_tables,
+                                    max_blocks_per_seq, context_lens, num_seqs, num_blocks,
+                                    block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                                    partition_tokens, workspace, workspace_bytes, dtype, stream,
+                                    nullptr, nullptr, true, 1.f, 1.f, nullptr, k_scales,
+                                    v_scales);
+}
+
+extern "C" int paged_decode_step_fp8_per_head(
+    int kernel, void* out, const void* q, void* k_pool, void* v_pool, const void* k_new,
+    const void* v_new, const int32_t* block_tables, int max_blocks_per_seq,
+    const int32_t* context_lens, int num_seqs, int num_blocks, int block_size, int num_q_heads,
+    int num_kv_heads, int head_dim, float scale, const float* k_scales, const float* v_scales,
+    int partition_tokens, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new || !k_scales || !v_scales)) return PKV_ERR_INVALID_ARG;
+  return pkv::decode_attention_impl(pkv::kPhaseAll, kernel, out, q, k_pool, v_pool, block_tables,
+                                    max_blocks_per_seq, context_lens, num_seqs, num_blocks,
+                                    block_size, num_q_heads, num_kv_heads, head_dim, scale,
+                                    partition_tokens, workspace, workspace_bytes, dtype, stream,
+                                    k_new, v_new, true, 1.f, 1.f, nullptr, k_scales, v_scales);
 }
 
 extern "C" int paged_decode_attention_lse(int kernel, float* lse, PKV_ATTN_ARGS) {

@@ -43,13 +43,15 @@ __global__ __launch_bounds__(kThreads) void append_kernel(
 
 // FP8 pools: one workgroup per sequence; each thread quantises 8 elements of
 // the new token's row, code = e4m3(fp32(x) / fp32(scale)), and stores them
-// as 8 bytes.  T is the element type of k_new / v_new.
+// as 8 bytes.  T is the element type of k_new / v_new.  k_scales / v_scales
+// (per-head scales, [num_kv_heads]) replace k_scale / v_scale when not null.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void append_fp8_kernel(
     uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool, const char* __restrict__ k_new,
     const char* __restrict__ v_new, const int32_t* __restrict__ tables, int max_blocks,
     const int32_t* __restrict__ lens_pre, int num_blocks, int log2_b, int num_kv_heads,
-    int head_dim, float k_scale, float v_scale) {
+    int head_dim, float k_scale, float v_scale, const float* __restrict__ k_scales,
+    const float* __restrict__ v_scales) {
   const int s = blockIdx.x;
   const int len = lens_pre[s];
   if (len < 0) return;
@@ -71,10 +73,16 @@ __global__ __launch_bounds__(kThreads) void append_fp8_kernel(
       Cvt<T>::unpack(load16(k_new + src), kf);
       Cvt<T>::unpack(load16(v_new + src), vf);
     }
+    float ks = k_scale, vs = v_scale;
+    if (k_scales) {   // the chunk's KV head (head_dim is a multiple of 16)
+      ks = k_scales[8 * c / head_dim];
+      vs = v_scales[8 * c / head_dim];
+    }
+    const bool k_ok = scale_ok(ks), v_ok = scale_ok(vs);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      kf[e] = kf[e] / k_scale;
-      vf[e] = vf[e] / v_scale;
+      kf[e] = k_ok ? kf[e] / ks : __builtin_nanf("");
+      vf[e] = v_ok ? vf[e] / vs : __builtin_nanf("");
     }
     const uint2 kc = make_uint2(e4m3_encode4(kf[0], kf[1], kf[2], kf[3]),
                                 e4m3_encode4(kf[4], kf[5], kf[6], kf[7]));
@@ -296,12 +304,15 @@ extern "C" int paged_kv_append_tokens(void* k_pool, void* v_pool, const void* k_
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-extern "C" int paged_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new,
-                                   const void* v_new, const int32_t* block_tables,
-                                   int max_blocks_per_seq, const int32_t* context_lens_pre,
-                                   int num_seqs, int num_blocks, int block_size, int num_kv_heads,
-                                   int head_dim, int new_dtype, float k_scale, float v_scale,
-                                   void* stream) {
+namespace {
+
+// paged_kv_append_fp8 with per-pool scales (k_scales == v_scales == null) or
+// per-head ones.
+int append_fp8_impl(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens_pre, int num_seqs, int num_blocks, int block_size,
+                    int num_kv_heads, int head_dim, int new_dtype, float k_scale, float v_scale,
+                    const float* k_scales, const float* v_scales, void* stream) {
   int st = check_pool_shape(num_blocks, block_size, num_kv_heads, head_dim, PKV_FP8_E4M3);
   if (st != PKV_OK) return st;
   if (!supported_dtype(new_dtype)) return PKV_ERR_UNSUPPORTED;
@@ -318,12 +329,38 @@ extern "C" int paged_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new
                        (hipStream_t)stream, (uint8_t*)k_pool, (uint8_t*)v_pool,
                        (const char*)k_new, (const char*)v_new, block_tables, max_blocks_per_seq,
                        context_lens_pre, num_blocks, log2_b, num_kv_heads, head_dim, k_scale,
-                       v_scale);
+                       v_scale, k_scales, v_scales);
   };
   if (new_dtype == PKV_F32) launch(F32{});
   else if (new_dtype == PKV_F16) launch(F16{});
   else launch(BF16{});
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int paged_kv_append_fp8(void* k_pool, void* v_pool, const void* k_new,
+                                   const void* v_new, const int32_t* block_tables,
+                                   int max_blocks_per_seq, const int32_t* context_lens_pre,
+                                   int num_seqs, int num_blocks, int block_size, int num_kv_heads,
+                                   int head_dim, int new_dtype, float k_scale, float v_scale,
+                                   void* stream) {
+  return append_fp8_impl(k_pool, v_pool, k_new, v_new, block_tables, max_blocks_per_seq,
+                         context_lens_pre, num_seqs, num_blocks, block_size, num_kv_heads,
+                         head_dim, new_dtype, k_scale, v_scale, nullptr, nullptr, stream);
+}
+
+extern "C" int paged_kv_append_fp8_per_head(void* k_pool, void* v_pool, const void* k_new,
+                                            const void* v_new, const int32_t* block_tables,
+                                            int max_blocks_per_seq,
+                                            const int32_t* context_lens_pre, int num_seqs,
+                                            int num_blocks, int block_size, int num_kv_heads,
+                                            int head_dim, int new_dtype, const float* k_scales,
+                                            const float* v_scales, void* stream) {
+  if (num_seqs > 0 && (!k_scales || !v_scales)) return PKV_ERR_INVALID_ARG;
+  return append_fp8_impl(k_pool, v_pool, k_new, v_new, block_tables, max_blocks_per_seq,
+                         context_lens_pre, num_seqs, num_blocks, block_size, num_kv_heads,
+                         head_dim, new_dtype, 1.f, 1.f, k_scales, v_scales, stream);
 }
 
 extern "C" int paged_kv_append_tokens_fp8(void* k_pool, void* v_pool, const void* k_new,

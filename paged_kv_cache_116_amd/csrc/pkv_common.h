@@ -51,6 +51,11 @@ __device__ __forceinline__ bool valid_block(int id, int num_blocks) {
   return id >= 0 && id < num_blocks;
 }
 
+// A per-head FP8 scale is usable when it is finite and positive; with any
+// other scale the appends store NaN codes in that head of that pool, and
+// attention gives the head's rows NaN.
+__device__ __forceinline__ bool scale_ok(float s) { return s > 0.f && s < INFINITY; }
+
 // ---------------------------------------------------------------------------
 // Conversions.
 // ---------------------------------------------------------------------------
