@@ -304,12 +304,16 @@ __global__ __launch_bounds__(kThreads, D <= 128 ? 2 : 1) void attn_prefill_mfma(
       for (int rg = 0; rg < kRG; ++rg) {
         if (!row_ok[rg]) continue;
         const RowAddr ra = row_addr(rg);
+        // (Rolled loops: unrolled, their per-lane offsets would be hoisted
+        // out of the row-block loop and held in registers throughout.)
         if constexpr (kPrefix) {   // NaN, or an empty key range: sum 0, log 0
           const float v = invalid ? __builtin_nanf("") : 0.f;
+#pragma unroll 1
           for (int d = kgrp; d < D; d += 4) p.o_states[ra.state * D + d] = v;
           if (kgrp == 0) p.lse[ra.state] = invalid ? __builtin_nanf("") : -INFINITY;
         } else {
           S* orow = (S*)p.out + ra.qoff;
+#pragma unroll 1
           for (int d = kgrp; d < D; d += 4) Cvt<T>::store(orow + d, __builtin_nanf(""));
         }
       }
