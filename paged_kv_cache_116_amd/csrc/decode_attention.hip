@@ -13,19 +13,22 @@
 // normaliser l and unnormalised accumulator o updated tile by tile.
 //
 // Work decomposition: three launches.
-//   attn_plan (1 workgroup): counts each live sequence's 16-token tiles,
+//   attn_plan (16 workgroups): counts each live sequence's 16-token tiles,
 //     prefix-sums them, and cuts the flattened space
 //         (quad of kw KV-head groups, sequence, tile)
 //     into claims: stage 0 gives each resident workgroup one claim of half
 //     its share, each later stage halves the claim size down to a few tiles
-//     per wave.  It writes a start descriptor per claim, the lists of split
-//     sequences for the merge, and fills the rows of empty sequences.
+//     per wave.  It writes a descriptor per claim (where it starts, its
+//     size, the first sequence's tile count and length, its successor and
+//     the claim count), the lists of split sequences for the merge, and
+//     fills the rows of empty sequences.
 //   attn_partition_* (persistent workgroups, 4 waves each): workgroup b takes
 //     claim b of stage 0 and claim b of stage 1, then the next unclaimed one
 //     from an atomic counter, so compute units that stream faster take more
-//     of the small late claims and all of them finish together.  Each stretch of one sequence inside a claim is a
-//     segment.  With kw = 1 the four waves take the segment's tiles in turn
-//     and combine their online-softmax states in LDS at its end; with kw = 4
+//     of the small late claims and all of them finish together.  Each
+//     stretch of one sequence inside a claim is a segment.  With kw = 1 the
+//     four waves take the segment's tiles in turn and combine their
+//     online-softmax states in LDS at its end; with kw = 4
 //     each wave serves its own KV-head group over the same tiles.  A segment
 //     that is the whole sequence writes the final output; otherwise it writes
 //     a partial state (m, l, o) in a slot named by (claim + sequence slot).
@@ -93,29 +96,26 @@ constexpr int kMergeWaves = 8;      // waves per merge workgroup
 constexpr int kMergeThreads = 64 * kMergeWaves;
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanLdsCum = 8192;   // prefix sums kept in LDS up to this many sequences
+constexpr int kDescWords = 8;       // words per claim descriptor
+// The claim walk reads descriptor blockIdx.x before it knows the claim count:
+// the partition grid (at most kMaxWgPerCu per CU) never exceeds the
+// descriptor slots (at least kClaimsPerCu per CU).
+static_assert(kMaxWgPerCu <= kClaimsPerCu, "first descriptor inside the descriptor area");
 
-// Plan area (int32 words): header | cum[S + 1] | desc[range_cap][4] |
+// Plan area (int32 words): header | cum[S + 1] | desc[range_cap][8] |
 // short tasks[kvq * S][4] | long tasks[kvq * S][4]; plan workgroup b writes
 // its tasks from entry b * task_seg of each list.
-// Header: totals, the claim counter and the stage table; stage k covers
-// claims [C_k, C_k+1) and tiles [X_k, X_k+1), every claim z_k tiles long but
-// the last of the final stage.  Entry ns (= number of stages) is a sentinel.
+// Header: the claim counter and each plan workgroup's task counts; the claim
+// schedule itself lives in the descriptors.
 constexpr int kPlanGroups = 16;     // workgroups of the plan launch that plan
 constexpr int kAppendGroups = 16;   // further workgroups that do the decode-step append
 constexpr int kHdrWords = 128;
 enum Hdr {
-  kHdrTot = 0,      // tiles of one KV-head quad (sum over sequences)
-  kHdrClaims = 1,   // number of claims
-  kHdrStages = 2,   // number of stages
-  kHdrTotal = 3,    // tiles of the whole space
   kHdrNext = 4,     // claim counter
-  kHdrX = 8,        // X_k, kMaxStages + 1 entries
-  kHdrC = 8 + kMaxStages + 1,
-  kHdrZ = 8 + 2 * (kMaxStages + 1),
   kHdrShort = 64,   // per plan workgroup: split pairs of at most kMergeBlock partials
   kHdrLong = 64 + kPlanGroups,   // per plan workgroup: split pairs of more partials
 };
-static_assert(kHdrZ + kMaxStages + 1 <= kHdrShort && kHdrLong + kPlanGroups <= kHdrWords, "header");
+static_assert(kHdrLong + kPlanGroups <= kHdrWords, "header");
 
 typedef const __attribute__((address_space(4))) int32_t cint;   // read with scalar loads
 
@@ -372,7 +372,16 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
     return st_c[k] + (x - st_x[k]) / st_z[k];
   };
 
-  // Claim descriptors (qd, sequence, first tile, tiles), this workgroup's share.
+  // Claim descriptors, this workgroup's share: qd, sequence, first tile,
+  // tiles; the first sequence's tile count and length; the successor; the
+  // claim count.  With all a claim needs in one 32-byte load, a workgroup
+  // reaches its first tiles after the descriptor and the block ids alone.
+  // Stages 0 and 1 have one claim per workgroup, handed out by index
+  // (successor c + grid); the counter serves stage 2 on, or the final stage
+  // when there are fewer stages (successor -1 - c_dyn: ask the counter,
+  // which numbers claims from c_dyn).
+  const int c_dyn = max(ns > 2 ? st_c[2] : ns > 0 ? st_c[ns - 1] : 0, p.grid);
+  auto successor = [&](int c) { return c + p.grid < c_dyn ? c + p.grid : -1 - c_dyn; };
   int32_t* desc = p.plan + p.off_desc;
   for (int c = b * kPlanThreads + tid; c < C; c += kPlanGroups * kPlanThreads) {
     const int k = stage_of_claim(c);
@@ -386,7 +395,15 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
       const int mid = (lo + hi) >> 1;
       if (cum_at(mid) <= rem) lo = mid; else hi = mid;
     }
-    *reinterpret_cast<int4*>(desc + 4 * c) = make_int4(qd, lo, rem - cum_at(lo), size);
+    *reinterpret_cast<int4*>(desc + kDescWords * c) = make_int4(qd, lo, rem - cum_at(lo), size);
+    *reinterpret_cast<int4*>(desc + kDescWords * c + 4) =
+        make_int4(cum_at(lo + 1) - cum_at(lo), p.lens[lo], successor(c), C);
+  }
+  // Workgroups past the last claim read an empty descriptor (no tiles, the
+  // claim count as successor) and stop.
+  for (int c = C + b * kPlanThreads + tid; c < p.grid; c += kPlanGroups * kPlanThreads) {
+    *reinterpret_cast<int4*>(desc + kDescWords * c) = make_int4(0, 0, 0, 0);
+    *reinterpret_cast<int4*>(desc + kDescWords * c + 4) = make_int4(0, 0, C, C);
   }
 
   // Merge tasks.  A (quad, sequence) pair whose tiles span claims c0 .. c1
@@ -420,20 +437,7 @@ __global__ __launch_bounds__(kPlanThreads) void attn_plan(const AttnParams p) {
     p.plan[kHdrShort + b] = n_short;
     p.plan[kHdrLong + b] = n_long;
   }
-  if (b == 0) {
-    if (tid <= ns) {
-      p.plan[kHdrX + tid] = st_x[tid];
-      p.plan[kHdrC + tid] = st_c[tid];
-      p.plan[kHdrZ + tid] = st_z[tid];
-    }
-    if (tid == 0) {
-      p.plan[kHdrTot] = tot;
-      p.plan[kHdrClaims] = C;
-      p.plan[kHdrStages] = ns;
-      p.plan[kHdrTotal] = total;
-      p.plan[kHdrNext] = 0;
-    }
-  }
+  if (b == 0 && tid == 0) p.plan[kHdrNext] = 0;
 }
 
 // Natural log of a softmax normaliser kept as (m, l) in log2 units:
@@ -463,35 +467,49 @@ struct Segment {
 // the second are better balanced by the counter.)
 template <typename Fn>
 __device__ __forceinline__ void walk_claims(const AttnParams& p, Fn&& process) {
-  cint* hdr = (cint*)p.plan;
   cint* cum = (cint*)(p.plan + kHdrWords);
   cint* desc = (cint*)(p.plan + p.off_desc);
-  const int C = hdr[kHdrClaims];
-  const int G = (int)gridDim.x;
-  // First claim served by the counter: stage 2's first, or the final
-  // stage's when there are fewer stages (never one of stage 0's G).
-  const int ns = hdr[kHdrStages];
-  const int c_dyn = max(ns > 2 ? hdr[kHdrC + 2] : ns > 0 ? hdr[kHdrC + ns - 1] : 0, G);
+  // Every load before a claim's first tiles is a dependent round trip, and
+  // at the start of the launch all workgroups wait on them together, so a
+  // claim's descriptor carries all the walk needs.  Descriptor blockIdx.x
+  // exists whatever the claim count (gridDim.x <= range_cap; the plan
+  // writes empty ones past the last claim).
+  auto load_desc = [&](int c, int (&d)[kDescWords]) {
+#pragma unroll
+    for (int i = 0; i < kDescWords; ++i) d[i] = desc[kDescWords * c + i];
+  };
+  int d[kDescWords];
+  load_desc(blockIdx.x, d);
   __shared__ int next_lds[2];
   int parity = 0;
-  for (int c = blockIdx.x; c < C;) {
+  for (int c = blockIdx.x;;) {
+    const int succ = d[6];
+    const int C = d[7];
     int next = 0;
     if (threadIdx.x == 0)
-      next = c + G < c_dyn ? c + G : c_dyn + atomicAdd(p.plan + kHdrNext, 1);
-    int qd = desc[4 * c + 0];
-    int s = desc[4 * c + 1];
-    int t0 = desc[4 * c + 2];
-    int remaining = desc[4 * c + 3];
+      next = succ >= 0 ? succ : (-1 - succ) + atomicAdd(p.plan + kHdrNext, 1);
+    int qd = d[0];
+    int s = d[1];
+    int t0 = d[2];
+    int remaining = d[3];
+    // The first sequence's tile count and length come with the descriptor.
+    int nt = d[4];
+    int L = d[5];
     // The claim holds `remaining` tiles of the flattened space; the walk can
     // never pass the last quad, which bounds the loop for any input.
+    bool first = true;
     while (remaining > 0 && qd < p.kvq_count) {
-      const int nt = cum[s + 1] - cum[s];
+      if (!first) {
+        nt = cum[s + 1] - cum[s];
+        L = ((cint*)p.lens)[s];
+      }
+      first = false;
       const int take = min(nt - t0, remaining);
       if (take > 0) {
         Segment sg;
         sg.qd = qd;
         sg.s = s;
-        sg.L = ((cint*)p.lens)[s];
+        sg.L = L;
         sg.t0 = t0;
         sg.take = take;
         sg.final = (t0 == 0 && take == nt);
@@ -513,6 +531,8 @@ __device__ __forceinline__ void walk_claims(const AttnParams& p, Fn&& process) {
     lds_barrier();
     c = __builtin_amdgcn_readfirstlane(next_lds[parity]);
     parity ^= 1;
+    if (c >= C) break;
+    load_desc(c, d);
   }
 }
 
@@ -1277,7 +1297,7 @@ inline WsLayout ws_layout(int num_seqs, int kvq_count, int pair_heads, int head_
   const size_t pairs_q = (size_t)kvq_count * num_seqs;
   w.task_seg = (pairs_q + kPlanGroups - 1) / kPlanGroups;
   w.off_desc = (kHdrWords + (size_t)num_seqs + 1 + 3) & ~(size_t)3;
-  w.off_short = w.off_desc + 4 * (size_t)range_cap;
+  w.off_short = w.off_desc + kDescWords * (size_t)range_cap;
   w.off_long = w.off_short + 4 * w.task_seg * kPlanGroups;
   const size_t plan_words = w.off_long + 4 * w.task_seg * kPlanGroups;
   w.plan_words = plan_words;
@@ -1704,7 +1724,8 @@ extern "C" size_t paged_decode_workspace_bytes(int num_seqs, int num_q_heads, in
   // Plan words: header, cum, descriptors, then the two merge task lists of
   // at most kvq_count * S <= Hq * S entries each (rounded up per plan
   // workgroup).
-  const size_t plan_words = pkv::kHdrWords + (size_t)num_seqs + 4 + 4 * (size_t)range_cap +
+  const size_t plan_words = pkv::kHdrWords + (size_t)num_seqs + 4 +
+                            pkv::kDescWords * (size_t)range_cap +
                             8 * ((size_t)num_q_heads * num_seqs + pkv::kPlanGroups);
   const size_t heads = (size_t)pkv::device_cu_count() * pkv::kClaimsPerCu * pkv::kWaves *
                            pkv::kMaxGroup +
