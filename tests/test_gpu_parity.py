@@ -391,6 +391,42 @@ def _with_lengths(w, lens):
                        v_new=torch.randn(S, Hkv, D, generator=gen).to(dt), k_pool=kp, v_pool=vp)
 
 
+@pytest.mark.parametrize("kernel", ["mfma", "valu"])
+def test_workspace_reused_with_fewer_claims_than_workgroups(kernel):
+    # One workspace serves a batch of many claims, then batches with far
+    # fewer claims than the partition launch has workgroups (the others read
+    # the empty descriptors the plan writes for them, not the previous
+    # call's), then one with no live sequence at all.
+    k = pkv.PKV_ATTN_MFMA if kernel == "mfma" else pkv.PKV_ATTN_VALU
+    big = workloads.make_workload(3, **SMALL[3])
+    ws = torch.empty(pkv.paged_decode_workspace_bytes(big.num_seqs, big.num_q_heads, big.head_dim,
+                                                      big.max_blocks * big.block_size, 0),
+                     dtype=torch.uint8, device="cuda")
+
+    def run(w):
+        dev = to_dev(w)
+        pkv.paged_kv_append(dev["k_pool"], dev["v_pool"], dev["k_new"], dev["v_new"],
+                            dev["tables"], dev["lens_pre"])
+        out = torch.full_like(dev["q"], 7.0)
+        pkv.paged_decode_attention(out, dev["q"], dev["k_pool"], dev["v_pool"], dev["tables"],
+                                   dev["lens"], scale=w.scale, workspace=ws, kernel=k)
+        torch.cuda.synchronize()
+        return out, dev
+
+    for lens in (None, [1], [3, 17]):
+        w = big if lens is None else _with_lengths(big, lens)
+        ref = oracle_step(w, w.k_pool, w.v_pool)
+        out, dev = run(w)
+        check_close(out, ref, w.dtype, f"reused workspace, lengths {lens or 'config 3'}")
+    # No live sequence: every row zeros, nothing else touched.
+    out = torch.full_like(dev["q"], 7.0)
+    pkv.paged_decode_attention(out, dev["q"], dev["k_pool"], dev["v_pool"], dev["tables"],
+                               torch.zeros_like(dev["lens"]), scale=w.scale, workspace=ws,
+                               kernel=k)
+    torch.cuda.synchronize()
+    assert (out.float() == 0).all()
+
+
 @pytest.mark.parametrize("part", [0, 64])
 def test_many_sequences_and_long_ones(part):
     # More sequences than the plan keeps in LDS (global binary search), mixed
